@@ -1,0 +1,186 @@
+"""CPU fp64 oracle of the selective-SSM (S6) scan and decode step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The GPU library (``selective_scan_02_amd``) never imports,
+links or calls anything here, and this package never imports the GPU library: the
+two share no code.  The arithmetic lives in ``ssm_oracle.c`` (plain sequential
+fp64 recurrence, see its header for the definition and the page passages it
+follows); this module only builds it with gcc and marshals arguments.
+
+Pins: ``tests/test_oracle.py`` checks this oracle against brute force (mpmath),
+closed forms (LTI convolution, step response, memoryless limit), exact special
+cases (Delta = 0) and invariants.  Every function here is pinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ssm_oracle.c -> liboracle.so (gcc -O2 -fopenmp, IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_scan.argtypes = [P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I64, I, P, I64, P, P, I]
+        lib.oracle_scan.restype = I
+        lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P, I64, P, P, I]
+        lib.oracle_step.restype = I
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _raw(x, keep):
+    """Pointer to the exact bytes of a CPU tensor / array (fp32 or bf16), or None."""
+    if x is None:
+        return None, None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            a = x.view(torch.int16).numpy()
+            dt = 1
+        elif x.dtype == torch.float32:
+            a = x.numpy()
+            dt = 0
+        else:
+            raise TypeError(f"oracle takes fp32 or bf16 tensors, got {x.dtype}")
+    else:
+        a = np.ascontiguousarray(x)
+        if a.dtype == np.float32:
+            dt = 0
+        else:
+            raise TypeError(f"oracle takes fp32 arrays, got {a.dtype}")
+    keep.append(a)
+    return a.ctypes.data, dt
+
+
+def _f32(x, keep):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().to(torch.float32).contiguous().numpy()
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    keep.append(a)
+    return a.ctypes.data
+
+
+def _chans(chans, total, keep):
+    if chans is None:
+        return None, total
+    c = np.ascontiguousarray(np.asarray(chans, dtype=np.int64))
+    if c.size and (c.min() < 0 or c.max() >= total):
+        raise IndexError("channel index out of range")
+    keep.append(c)
+    return c.ctypes.data, int(c.size)
+
+
+def scan(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None, chans=None,
+         threads: int = 0):
+    """Sequential fp64 scan.  Shapes: u, delta, z [B,D,L]; B, C [B,N,L]; A [D,N].
+
+    Returns (y, last_state) as float64 numpy arrays of shape [B,D,L] and [B,D,N]
+    (or [k,L], [k,N] for a channel subset ``chans`` of flat indices b*D + d).
+    ``h0``: optional initial state, [B,D,N] (or [k,N] with ``chans``).
+    """
+    keep = []
+    batch, dim, seqlen = (int(s) for s in u.shape)
+    dstate = int(A.shape[1])
+    pu, dtype = _raw(u, keep)
+    pdl, dt2 = _raw(delta, keep)
+    pB, dt3 = _raw(B, keep)
+    pC, dt4 = _raw(C, keep)
+    pz, dt5 = _raw(z, keep)
+    if len({dtype, dt2, dt3, dt4} | ({dt5} if z is not None else set())) != 1:
+        raise TypeError("u, delta, B, C, z must share one dtype")
+    pchans, rows = _chans(chans, batch * dim, keep)
+    ph0 = None
+    if h0 is not None:
+        h = h0.detach().cpu().double().numpy() if isinstance(h0, torch.Tensor) else np.asarray(h0, np.float64)
+        h = np.ascontiguousarray(h.reshape(rows, dstate), dtype=np.float64)
+        keep.append(h)
+        ph0 = h.ctypes.data
+    y = np.empty((rows, seqlen), dtype=np.float64)
+    last = np.empty((rows, dstate), dtype=np.float64)
+    rc = _load().oracle_scan(pu, pdl, _f32(A, keep), pB, pC, _f32(D, keep), pz, _f32(dt_bias, keep),
+                             1 if softplus else 0, ph0, batch, dim, dstate, seqlen, dtype, pchans, rows,
+                             y.ctypes.data, last.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan failed ({rc})")
+    if chans is None:
+        return y.reshape(batch, dim, seqlen), last.reshape(batch, dim, dstate)
+    return y, last
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, chans=None, threads: int = 0):
+    """One fp64 decode step.  state [B,D,N] (any float dtype; or [k,N] with ``chans``),
+    u, delta, z [B,D], B, C [B,N].  Returns (y, new_state) float64: [B,D], [B,D,N]
+    (or [k], [k,N]).  Softplus is always applied."""
+    keep = []
+    batch, dim = (int(s) for s in u.shape)
+    dstate = int(A.shape[1])
+    pu, dtype = _raw(u, keep)
+    pdl, dt2 = _raw(delta, keep)
+    pB, dt3 = _raw(B, keep)
+    pC, dt4 = _raw(C, keep)
+    pz, dt5 = _raw(z, keep)
+    if len({dtype, dt2, dt3, dt4} | ({dt5} if z is not None else set())) != 1:
+        raise TypeError("u, delta, B, C, z must share one dtype")
+    pchans, rows = _chans(chans, batch * dim, keep)
+    s = state.detach().cpu().double().numpy() if isinstance(state, torch.Tensor) else np.asarray(state)
+    s = np.ascontiguousarray(s.reshape(rows, dstate), dtype=np.float64)
+    keep.append(s)
+    y = np.empty((rows,), dtype=np.float64)
+    out = np.empty((rows, dstate), dtype=np.float64)
+    rc = _load().oracle_step(s.ctypes.data, pu, pdl, _f32(A, keep), pB, pC, _f32(D, keep), pz,
+                             _f32(dt_bias, keep), batch, dim, dstate, dtype, pchans, rows, y.ctypes.data,
+                             out.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_step failed ({rc})")
+    if chans is None:
+        return y.reshape(batch, dim), out.reshape(batch, dim, dstate)
+    return y, out
+
+
+def rel_err(got, ref) -> float:
+    """Max error relative to max(|ref_i|, rms(ref)) -- the parity metric.
+
+    Pure elementwise relative error is meaningless where a reference entry is
+    near zero, so each entry's error is scaled by the larger of its own
+    magnitude and the RMS of the whole reference tensor."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    rms = float(np.sqrt(np.mean(r * r)))
+    floor = max(rms, np.finfo(np.float64).tiny)
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), floor)))
