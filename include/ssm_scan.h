@@ -1,0 +1,118 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * Two operations of the Mamba selective SSM ("S6"), as described on the pages
+ * this library follows:
+ *
+ *   selective_scan_fwd      the whole-sequence forward scan (training / prefill):
+ *                           "Selective Scan 如何兼顾训练与 Decode" in "AI inference
+ *                           series (14)" (wiblog.cn) -- prefill runs the parallel
+ *                           selective scan and writes the final state; the
+ *                           hardware-aware chunked scan of the Mamba summary
+ *                           (junchaoiu.github.io, 方法 step 2) and of the mlqm.cn
+ *                           tutorial §6.
+ *   selective_state_update  one autoregressive decode step: a single-step
+ *                           recurrent update of a fixed-size per-request state,
+ *                           updated in place (same wiblog.cn page, table of the
+ *                           two execution forms and "推理框架需要管理完全不同的请求状态";
+ *                           mlqm.cn tutorial §9.2, the single-step update).
+ *
+ * Per channel d, state n and step t (h_{-1} = 0 for the scan):
+ *   Delta_t   = softplus(delta_t + dt_bias[d])   (softplus flag off: delta_t + dt_bias[d])
+ *   Abar_t[n] = exp(Delta_t * A[d,n])            ZOH transition (mlqm.cn §3.2;
+ *                                                "Mamba close reading" (jsqmd.com) §1.2)
+ *   h_t[n]    = Abar_t[n] * h_{t-1}[n] + Delta_t * B_t[n] * u_t
+ *                                                first-order input term Delta*B (mlqm.cn §3.2, §9.2)
+ *   y_t       = (sum_n C_t[n] h_t[n] + D[d] u_t) * silu(z_t),  silu(z) = z * sigmoid(z)
+ *                                                readout and D skip (tech.kj168168.com essay §二.1,
+ *                                                mlqm.cn §9.2); SiLU gate (Mamba summary 方法 step 3)
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory on the
+ *    current device), row-major and contiguous (last dimension fastest).
+ *  - `dtype` (ssm_dtype_t) is the element type of u, delta, z, B, C and y.  A, D,
+ *    dt_bias and the state are always fp32.  Arithmetic is fp32 throughout.
+ *  - Ownership: the caller owns every buffer.  The library keeps no pointer after
+ *    a call returns.  Scratch memory (scan segment carries) is taken from HIP's
+ *    stream-ordered allocator on `stream` and released on `stream`.
+ *  - Calls are asynchronous on `stream` (hipStream_t; NULL = the null stream) and
+ *    never synchronise the device.
+ *  - Errors: the return value is an ssm_status_t.  Arguments are validated before
+ *    any HIP call; a validation error leaves every output untouched.  Launch errors
+ *    return SSM_ERR_HIP; faults inside a kernel surface at the caller's next
+ *    synchronisation.  Non-finite inputs propagate; they are not checked.
+ *    ssm_last_error() gives a text for the calling thread's last non-OK status.
+ *  - Thread safety: calls on different streams may run concurrently.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL_ARG = -1,     /* a required pointer is NULL                         */
+  SSM_ERR_BAD_SHAPE = -2,    /* a size is negative / zero where not allowed / too big */
+  SSM_ERR_BAD_DTYPE = -3,    /* dtype is not SSM_F32 or SSM_BF16                   */
+  SSM_ERR_MISALIGNED = -4,   /* a pointer is not aligned to its element size       */
+  SSM_ERR_ALIAS = -5,        /* an output overlaps an input or another output      */
+  SSM_ERR_UNSUPPORTED = -6,  /* dstate not in the compiled set {1,2,4,8,16,32,64}  */
+  SSM_ERR_HIP = -7           /* a HIP runtime call or kernel launch failed         */
+} ssm_status_t;
+
+/*
+ * Forward selective scan over a whole sequence.
+ *
+ *   u, delta, z : [batch, dim, seqlen]  (dtype)   u = input x_t, delta = raw step before bias/softplus
+ *   A           : [dim, dstate] fp32             (= -exp(A_log); sign is not checked)
+ *   B, C        : [batch, dstate, seqlen] (dtype)  input-dependent, shared by all channels of a batch row
+ *   D, dt_bias  : [dim] fp32                     NULL = no skip term / zero bias
+ *   z           : NULL = no gate
+ *   softplus    : 0 or 1
+ *   y           : [batch, dim, seqlen] (dtype) output; must not overlap any input
+ *   last_state  : [batch, dim, dstate] fp32 output h_{L-1}; NULL = not written;
+ *                 seqlen == 0 writes zeros
+ * Required: u, delta, A, B, C, y (all but A may be NULL when seqlen == 0, as
+ * the sequence tensors are then empty).  batch, dim, dstate >= 1 and seqlen >= 0;
+ * batch * dim * max(seqlen, dstate) < 2^40 elements.
+ */
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus, void* y,
+                       float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                       int dtype, void* stream);
+
+/*
+ * One decode step for `batch` independent requests, state updated IN PLACE.
+ *
+ *   state       : [batch, dim, dstate] fp32, read as h_{t-1} and overwritten with h_t
+ *   u, delta, z : [batch, dim] (dtype); z NULL = no gate
+ *   A           : [dim, dstate] fp32
+ *   B, C        : [batch, dstate] (dtype)
+ *   D, dt_bias  : [dim] fp32, NULL = absent / zero
+ *   y           : [batch, dim] (dtype) output
+ * Softplus is always applied to delta + dt_bias.  Required: state, u, delta, A,
+ * B, C, y; state and y must not overlap an input or each other.
+ */
+int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* dt_bias, void* y,
+                           int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream);
+
+/* Text describing the calling thread's most recent non-OK status ("" if none). */
+const char* ssm_last_error(void);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int ssm_abi_version(void);
+
+#define SSM_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

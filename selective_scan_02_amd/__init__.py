@@ -1,0 +1,171 @@
+"""MI355X-native selective state-space (Mamba S6) scan -- Python binding.
+
+A thin ctypes layer over the C ABI in ``include/ssm_scan.h`` (library
+``libssm_scan.so``, built in-tree by ``selective_scan_02_amd.build``).  Every step
+of the computation runs in the library's HIP kernels; this module only checks
+tensor shapes, allocates outputs with torch and passes device pointers and the
+current HIP stream.  There is no CPU fallback: without the built library or a
+GPU these functions raise.
+
+    y, last_state = scan_fwd(u, delta, A, B, C, D, z, dt_bias, softplus=True)
+    y = state_update(state, u, delta, A, B, C, D, z, dt_bias)   # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "lib_path", "scan_fwd", "state_update", "SsmError", "STATUS", "selective_scan_fwd",
+           "selective_state_update", "last_error"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_PKG, "libssm_scan.so")
+_lib = None
+
+STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
+          -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
+F32, BF16 = 0, 1
+EXPORTS = ("selective_scan_fwd", "selective_state_update", "ssm_last_error", "ssm_abi_version")
+
+
+class SsmError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load():
+    """Load libssm_scan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is not built; run `python -m selective_scan_02_amd.build`")
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.selective_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
+        lib.selective_scan_fwd.restype = I
+        lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
+        lib.selective_state_update.restype = I
+        lib.ssm_last_error.argtypes = []
+        lib.ssm_last_error.restype = ctypes.c_char_p
+        lib.ssm_abi_version.argtypes = []
+        lib.ssm_abi_version.restype = I
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().ssm_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SsmError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"u must be float32 or bfloat16, got {t.dtype}")
+
+
+def _require(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device} (a GPU tensor)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# Raw C-ABI calls (device pointers as ints), used by the tests of the boundary.
+def selective_scan_fwd(*args) -> int:
+    return int(load().selective_scan_fwd(*args))
+
+
+def selective_state_update(*args) -> int:
+    return int(load().selective_state_update(*args))
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True,
+             return_last_state: bool = True, y=None, last_state=None):
+    """Forward selective scan.  u, delta, z: [batch, dim, L]; B, C: [batch, N, L]
+    (dtype of u); A: [dim, N] fp32; D, dt_bias: [dim] fp32.  Returns (y, last_state)."""
+    lib = load()
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    dev = u.device
+    dt = u.dtype
+    _require(u, "u", (batch, dim, L), dt, dev)
+    _require(delta, "delta", (batch, dim, L), dt, dev)
+    _require(z, "z", (batch, dim, L), dt, dev)
+    _require(B, "B", (batch, N, L), dt, dev)
+    _require(C, "C", (batch, N, L), dt, dev)
+    _require(A, "A", (dim, N), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (dim,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _require(y, "y", (batch, dim, L), dt, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    if last_state is not None:
+        _require(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    rc = lib.selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                1 if softplus else 0, _ptr(y), _ptr(last_state), batch, dim, N, L,
+                                _dtype_code(u), _stream(dev))
+    _check(rc)
+    return y, last_state
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, y=None):
+    """One decode step; ``state`` [batch, dim, N] fp32 is updated in place.
+    u, delta, z: [batch, dim]; B, C: [batch, N] (dtype of u).  Returns y [batch, dim]."""
+    lib = load()
+    if u.dim() != 2 or state.dim() != 3:
+        raise ValueError("u must be [batch, dim] and state [batch, dim, dstate]")
+    batch, dim = u.shape
+    N = state.shape[2]
+    dev = u.device
+    dt = u.dtype
+    _require(state, "state", (batch, dim, N), torch.float32, dev)
+    _require(u, "u", (batch, dim), dt, dev)
+    _require(delta, "delta", (batch, dim), dt, dev)
+    _require(z, "z", (batch, dim), dt, dev)
+    _require(B, "B", (batch, N), dt, dev)
+    _require(C, "C", (batch, N), dt, dev)
+    _require(A, "A", (dim, N), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (dim,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _require(y, "y", (batch, dim), dt, dev)
+    rc = lib.selective_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(dt_bias), _ptr(y), batch, dim, N, _dtype_code(u),
+                                    _stream(dev))
+    _check(rc)
+    return y

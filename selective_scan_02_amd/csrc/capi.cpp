@@ -1,0 +1,161 @@
+// capi.cpp -- the extern "C" boundary: argument validation, error reporting and
+// dispatch to the gfx950 kernels.  Validation happens entirely on the host and
+// before any HIP call, so a rejected call touches no output.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ssm_scan.h"
+#include "ssm_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+struct Range {
+  const char* name;
+  const void* p;
+  uint64_t bytes;
+  uint64_t align;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int check_aligned(const Range& r) {
+  if (r.p && ((uintptr_t)r.p % r.align) != 0)
+    return fail(SSM_ERR_MISALIGNED, "%s is not %llu-byte aligned", r.name, (unsigned long long)r.align);
+  return SSM_OK;
+}
+
+// Product of sizes with an overflow guard: every tensor must stay below 2^40 elements.
+bool too_big(int64_t a, int64_t b, int64_t c) {
+  const double e = (double)a * (double)b * (double)c;
+  return e >= 1099511627776.0;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SSM_OK;
+  return fail(SSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus, void* y,
+                       float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                       void* stream) {
+  g_last_error.clear();
+  // With seqlen == 0 the sequence tensors are empty and may be NULL.
+  if (seqlen != 0) {
+    if (!u) return fail(SSM_ERR_NULL_ARG, "u is NULL");
+    if (!delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
+    if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
+    if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
+    if (!y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
+  }
+  if (!A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld dstate=%lld seqlen=%lld", (long long)batch,
+                (long long)dim, (long long)dstate, (long long)seqlen);
+  if (too_big(batch, dim, seqlen) || too_big(batch, dstate, seqlen) || too_big(batch, dim, dstate) ||
+      batch * ((dim + 63) / 64) > 0x7fffffffLL)
+    return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (!ssm::dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim * seqlen, nbc = (uint64_t)batch * dstate * seqlen;
+  const Range ins[] = {{"u", u, nx * es, es},
+                       {"delta", delta, nx * es, es},
+                       {"z", z, nx * es, es},
+                       {"B", B, nbc * es, es},
+                       {"C", C, nbc * es, es},
+                       {"A", A, (uint64_t)dim * dstate * 4, 4},
+                       {"D", D, (uint64_t)dim * 4, 4},
+                       {"dt_bias", dt_bias, (uint64_t)dim * 4, 4}};
+  const Range ry{"y", y, nx * es, es}, rl{"last_state", last_state, (uint64_t)batch * dim * dstate * 4, 4};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(ry)) return rc;
+  if (int rc = check_aligned(rl)) return rc;
+  for (const Range& r : ins) {
+    if (overlap(ry, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+    if (overlap(rl, r)) return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
+  }
+  if (overlap(ry, rl)) return fail(SSM_ERR_ALIAS, "y overlaps last_state");
+
+  ssm::ScanParams p{};
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
+  p.softplus = softplus; p.y = y; p.last_state = last_state; p.h0 = nullptr;
+  p.batch = batch; p.dim = dim; p.dstate = dstate; p.seqlen = seqlen; p.dtype = dtype;
+  return hip_status(ssm::launch_scan_fwd(p, (hipStream_t)stream), "selective_scan_fwd launch");
+}
+
+int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* dt_bias, void* y,
+                           int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!state) return fail(SSM_ERR_NULL_ARG, "state is NULL");
+  if (!u) return fail(SSM_ERR_NULL_ARG, "u is NULL");
+  if (!delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
+  if (!A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+  if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
+  if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
+  if (!y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || dstate < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld dstate=%lld", (long long)batch, (long long)dim,
+                (long long)dstate);
+  if (too_big(batch, dim, dstate)) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (!ssm::dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim, nbc = (uint64_t)batch * dstate;
+  const Range ins[] = {{"u", u, nx * es, es},
+                       {"delta", delta, nx * es, es},
+                       {"z", z, nx * es, es},
+                       {"B", B, nbc * es, es},
+                       {"C", C, nbc * es, es},
+                       {"A", A, (uint64_t)dim * dstate * 4, 4},
+                       {"D", D, (uint64_t)dim * 4, 4},
+                       {"dt_bias", dt_bias, (uint64_t)dim * 4, 4}};
+  const Range rs{"state", state, nx * dstate * 4, dstate >= 4 ? 16u : 4u}, ry{"y", y, nx * es, es};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(rs)) return rc;
+  if (int rc = check_aligned(ry)) return rc;
+  for (const Range& r : ins) {
+    if (overlap(rs, r)) return fail(SSM_ERR_ALIAS, "state overlaps %s", r.name);
+    if (overlap(ry, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+  }
+  if (overlap(ry, rs)) return fail(SSM_ERR_ALIAS, "y overlaps state");
+
+  ssm::StepParams p{state, u, delta, A, B, C, D, z, dt_bias, y, batch, dim, dstate, dtype};
+  return hip_status(ssm::launch_state_update(p, (hipStream_t)stream), "selective_state_update launch");
+}
+
+}  // extern "C"

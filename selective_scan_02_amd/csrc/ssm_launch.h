@@ -1,0 +1,47 @@
+// ssm_launch.h -- internal interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+enum IoType { kF32 = 0, kBF16 = 1 };
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* dt_bias;  // nullable
+  int softplus;
+  void* y;
+  float* last_state;  // nullable
+  const float* h0;    // nullable initial state [batch, dim, dstate]
+  int64_t batch, dim, dstate, seqlen;
+  int dtype;
+};
+
+struct StepParams {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* dt_bias;  // nullable
+  void* y;
+  int64_t batch, dim, dstate;
+  int dtype;
+};
+
+bool dstate_supported(int64_t n);
+hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);
+hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
+
+}  // namespace ssm

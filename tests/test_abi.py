@@ -1,0 +1,140 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load without a device, export every function the public
+header declares, and reject bad arguments on the host -- before any HIP call --
+with the documented status codes.  Fake (never dereferenced) device addresses
+are used: a rejected call touches nothing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_scan_02_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+NULL_ARG, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, UNSUPPORTED = -1, -2, -3, -4, -5, -6
+
+# Fake 256-byte-aligned device addresses, far apart (1 TiB) so nothing overlaps by accident.
+BASE = 1 << 44
+def addr(i):
+    return BASE + (i << 40)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.lib_path()):
+        import selective_scan_02_amd.build as b
+        b.build()
+    return ssm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("selective_scan_fwd", "selective_state_update", "ssm_last_error", "ssm_abi_version"):
+        assert name in fns
+    assert set(fns) == set(ssm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version(lib):
+    assert lib.ssm_abi_version() == 1
+
+
+def scan_args(**over):
+    a = dict(u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), dt_bias=addr(8),
+             softplus=1, y=addr(9), last=addr(10), batch=2, dim=64, dstate=16, seqlen=128, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "dt_bias", "softplus", "y", "last", "batch", "dim",
+                           "dstate", "seqlen", "dtype", "stream")]
+
+
+def step_args(**over):
+    a = dict(state=addr(1), u=addr(2), delta=addr(3), A=addr(4), B=addr(5), C=addr(6), D=addr(7), z=addr(8),
+             dt_bias=addr(9), y=addr(10), batch=4, dim=64, dstate=16, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("state", "u", "delta", "A", "B", "C", "D", "z", "dt_bias", "y", "batch", "dim", "dstate",
+                           "dtype", "stream")]
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "y"])
+def test_scan_null_required(lib, field):
+    assert lib.selective_scan_fwd(*scan_args(**{field: None})) == NULL_ARG
+    assert field in ssm.last_error()
+
+
+@pytest.mark.parametrize("field", ["state", "u", "delta", "A", "B", "C", "y"])
+def test_step_null_required(lib, field):
+    assert lib.selective_state_update(*step_args(**{field: None})) == NULL_ARG
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(dim=0), dict(dstate=0), dict(seqlen=-1), dict(batch=-3),
+                                  dict(batch=1 << 20, dim=1 << 20, seqlen=1 << 20), dict(softplus=2)])
+def test_scan_bad_shape(lib, over):
+    assert lib.selective_scan_fwd(*scan_args(**over)) == BAD_SHAPE
+
+
+def test_bad_dtype(lib):
+    assert lib.selective_scan_fwd(*scan_args(dtype=7)) == BAD_DTYPE
+    assert lib.selective_state_update(*step_args(dtype=-1)) == BAD_DTYPE
+
+
+@pytest.mark.parametrize("n", [3, 5, 12, 128, 1000])
+def test_unsupported_dstate(lib, n):
+    assert lib.selective_scan_fwd(*scan_args(dstate=n)) == UNSUPPORTED
+    assert lib.selective_state_update(*step_args(dstate=n)) == UNSUPPORTED
+    assert str(n) in ssm.last_error()
+
+
+def test_misaligned(lib):
+    assert lib.selective_scan_fwd(*scan_args(u=addr(1) + 1)) == MISALIGNED          # bf16 needs 2 bytes
+    assert lib.selective_scan_fwd(*scan_args(dtype=0, delta=addr(2) + 2)) == MISALIGNED  # fp32 needs 4
+    assert lib.selective_scan_fwd(*scan_args(A=addr(3) + 2)) == MISALIGNED
+    assert lib.selective_state_update(*step_args(state=addr(1) + 4)) == MISALIGNED   # float4 state rows
+
+
+def test_alias(lib):
+    # y placed inside u
+    assert lib.selective_scan_fwd(*scan_args(y=addr(1) + 64)) == ALIAS
+    # last_state overlapping B
+    assert lib.selective_scan_fwd(*scan_args(last=addr(4) + 16)) == ALIAS
+    # y overlapping last_state
+    assert lib.selective_scan_fwd(*scan_args(last=addr(9) + 32)) == ALIAS
+    # decode: state overlapping u, y overlapping state
+    assert lib.selective_state_update(*step_args(state=addr(2))) == ALIAS
+    assert lib.selective_state_update(*step_args(y=addr(1) + 16)) == ALIAS
+    assert "overlaps" in ssm.last_error()
+
+
+def test_error_text_is_per_call(lib):
+    lib.selective_scan_fwd(*scan_args(u=None))
+    assert ssm.last_error()
+    lib.selective_scan_fwd(*scan_args(dtype=9))
+    assert "dtype" in ssm.last_error()
+
+
+def test_python_wrapper_refuses_cpu_tensors(lib):
+    import torch
+    u = torch.zeros(1, 4, 8)
+    with pytest.raises((ValueError, TypeError)):
+        ssm.scan_fwd(u, u, torch.zeros(4, 4), torch.zeros(1, 4, 8), torch.zeros(1, 4, 8))
+
+
+def test_empty_sequence_allows_null_sequence_tensors(lib):
+    # seqlen == 0: u, delta, B, C, y are empty and may be NULL; A is still required
+    assert lib.selective_scan_fwd(*scan_args(seqlen=0, A=None, u=None)) == NULL_ARG
+    assert "A" in ssm.last_error()

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerances (on max |got - ref| / max(|ref_i|, rms(ref)), see oracle.rel_err):
+1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32 state.  Small cases are
+compared element by element; full-size workloads are compared on sampled
+channels, each of which the oracle computes over the whole sequence.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import selective_scan_02_amd as ssm
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    ssm.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def gpu_scan(x, **kw):
+    g = dev(x)
+    y, last = ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g.get("D"), g.get("z"), g.get("dt_bias"),
+                           softplus=x.get("softplus", True), **kw)
+    torch.cuda.synchronize()
+    return y, last
+
+
+def ref_scan(x, **kw):
+    return oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x.get("D"), x.get("z"), x.get("dt_bias"),
+                       x.get("softplus", True), **kw)
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_scan(x, tol=None, chans=None):
+    tol = tol or TOL[x["dtype"]]
+    y, last = gpu_scan(x)
+    yr, lr = ref_scan(x, chans=chans)
+    if chans is not None:   # select on the device, copy back only the sampled rows
+        idx = torch.as_tensor(chans, device=y.device)
+        y = y.reshape(-1, y.shape[-1])[idx]
+        last = last.reshape(-1, last.shape[-1])[idx]
+    yg, lg = f64(y), f64(last)
+    ey, el = oracle.rel_err(yg, yr), oracle.rel_err(lg, lr)
+    note(f"  y err {ey:.3e}  last_state err {el:.3e}  (tol {tol:g})")
+    assert ey <= tol, ey
+    assert el <= tol, el
+    return ey, el
+
+
+def test_workload0_tiny():
+    note("workload 0 tiny fp32 (full compare)")
+    check_scan(gen.scan_inputs(0))
+
+
+# Several tiles (64-channel groups, multi-segment splits) and ragged tails.
+SHAPES = [
+    (1, 64, 16, 256, "f32"),
+    (2, 100, 16, 777, "f32"),
+    (3, 130, 4, 1000, "bf16"),
+    (1, 1, 1, 1, "f32"),
+    (1, 7, 2, 5, "bf16"),
+    (2, 65, 8, 2048, "bf16"),
+    (1, 40, 32, 300, "f32"),
+    (1, 33, 64, 129, "f32"),
+    (4, 256, 16, 4096, "bf16"),
+    (1, 64, 16, 20000, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes(shape):
+    b, d, n, L, dt = shape
+    note(f"random shape B={b} D={d} N={n} L={L} {dt}")
+    check_scan(gen.random_scan_inputs(b, d, n, L, dt, seed=b * 7 + n))
+
+
+@pytest.mark.parametrize("opts", [dict(with_D=False), dict(with_z=False), dict(with_bias=False),
+                                  dict(softplus=False, delta_scale=0.05, with_bias=False), dict(a_mode="random"),
+                                  dict(with_D=False, with_z=False, with_bias=False)],
+                         ids=["noD", "noz", "nobias", "nosoftplus", "randomA", "bare"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_optional_terms(opts, dt):
+    o = dict(opts)
+    sp = o.pop("softplus", True)
+    x = gen.random_scan_inputs(2, 96, 16, 600, dt, seed=21, softplus=sp, **o)
+    if not sp:
+        x["delta"] = (x["delta"].float().abs() + 0.01).to(x["delta"].dtype)
+    note(f"optional terms {opts} {dt}")
+    check_scan(x)
+
+
+def test_empty_sequence_writes_zero_state():
+    x = gen.random_scan_inputs(2, 10, 16, 0, "f32", seed=0)
+    note("L = 0")
+    g = dev(x)
+    last = torch.full((2, 10, 16), 7.0, device="cuda")
+    y, last = ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"], last_state=last)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 10, 0) and torch.all(last == 0)
+
+
+def test_zero_step_keeps_zero_state():
+    # Delta = 0 (softplus off, delta = 0, no bias): h stays 0 and y = D*u*silu(z).
+    x = gen.random_scan_inputs(2, 70, 16, 500, "f32", seed=3, softplus=False, with_bias=False)
+    x["delta"] = torch.zeros_like(x["delta"])
+    note("Delta = 0 scan")
+    y, last = gpu_scan(x)
+    assert torch.all(last == 0)
+    yr, _ = ref_scan(x)
+    assert oracle.rel_err(f64(y), yr) < 1e-6
+
+
+def test_causality_bit_exact():
+    x = gen.random_scan_inputs(1, 64, 16, 3000, "f32", seed=4)
+    note("causality")
+    y1, _ = gpu_scan(x)
+    x2 = dict(x)
+    t0 = 2000
+    for k in ("u", "delta", "z", "B", "C"):
+        x2[k] = x[k].clone()
+        x2[k][..., t0:] += 1.0
+    y2, _ = gpu_scan(x2)
+    assert torch.equal(y1[..., :t0], y2[..., :t0])
+
+
+def test_deterministic():
+    x = gen.random_scan_inputs(2, 128, 16, 4000, "bf16", seed=5)
+    note("determinism")
+    g = dev(x)
+    outs = [ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y, last in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(last, outs[0][1])
+
+
+def test_noncurrent_stream():
+    x = gen.random_scan_inputs(1, 64, 16, 1000, "f32", seed=6)
+    note("side stream")
+    g = dev(x)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y, last = ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"])
+    s.synchronize()
+    yr, lr = ref_scan(x)
+    assert oracle.rel_err(f64(y), yr) < 1e-4 and oracle.rel_err(f64(last), lr) < 1e-4
+
+
+# ----------------------------- full-size workloads (sampled channels) -------
+def sampled(x, k, seed):
+    g = np.random.default_rng(seed)
+    total = x["batch"] * x["dim"]
+    c = np.sort(g.choice(total, size=min(k, total), replace=False))
+    # always include the first and last channel and a group edge
+    return np.unique(np.concatenate([c, [0, 63, 64, total - 1]]))
+
+
+@pytest.mark.parametrize("w", [1, 2])
+def test_workload_full_size_sampled(w):
+    x = gen.scan_inputs(w)
+    note(f"workload {w} full size, sampled channels")
+    check_scan(x, chans=sampled(x, 384, w))
+
+
+def test_workload3_long_sequence_sampled():
+    x = gen.scan_inputs(3)
+    note("workload 3 L=2^20, sampled channels")
+    check_scan(x, chans=sampled(x, 12, 3))
+
+
+# ----------------------------- decode ---------------------------------------
+def gpu_step(state, p, st):
+    y = ssm.state_update(state, st["u"], st["delta"], p["A"], st["B"], st["C"], p["D"], st["z"], p["dt_bias"])
+    return y
+
+
+def test_decode_small_shapes():
+    for (b, d, n, dt) in [(3, 100, 16, "bf16"), (2, 64, 4, "f32"), (1, 5, 1, "f32"), (2, 33, 64, "bf16"),
+                          (5, 17, 8, "f32"), (4, 80, 32, "bf16"), (1, 3, 2, "bf16")]:
+        note(f"decode B={b} D={d} N={n} {dt}")
+        x = gen.random_scan_inputs(b, d, n, 3, dt, seed=b + d + n)
+        state0 = torch.randn(b, d, n, generator=torch.Generator().manual_seed(n))
+        ref_state = state0.double().numpy()
+        state = state0.cuda()
+        g = dev(x)
+        for t in range(3):
+            st = {k: g[k][..., t].contiguous() for k in ("u", "delta", "z", "B", "C")}
+            y = gpu_step(state, g, st)
+            torch.cuda.synchronize()
+            yr, ref_state = oracle.step(ref_state, *(x[k][..., t].contiguous() for k in ("u", "delta")), x["A"],
+                                        x["B"][..., t].contiguous(), x["C"][..., t].contiguous(), x["D"],
+                                        x["z"][..., t].contiguous(), x["dt_bias"])
+            assert oracle.rel_err(f64(y), yr) <= TOL[dt]
+            assert oracle.rel_err(f64(state), ref_state) <= 1e-5
+
+
+def test_decode_zero_step_bit_identical_state():
+    b, d, n = 4, 96, 16
+    x = gen.random_scan_inputs(b, d, n, 1, "bf16", seed=2, with_bias=False)
+    note("decode Delta = 0: state bit-identical")
+    g = dev(x)
+    state = torch.randn(b, d, n, device="cuda")
+    before = state.clone()
+    delta = torch.full((b, d), -200.0).to(torch.bfloat16).cuda()   # softplus(-200) underflows to exactly 0
+    ssm.state_update(state, g["u"][..., 0].contiguous(), delta, g["A"], g["B"][..., 0].contiguous(),
+                     g["C"][..., 0].contiguous(), g["D"], g["z"][..., 0].contiguous(), None)
+    torch.cuda.synchronize()
+    assert torch.equal(state, before)
+
+
+def test_workload4_decode_128_steps():
+    w = gen.WORKLOADS[4]
+    p = gen.decode_params(4)
+    state0 = gen.decode_state(4)
+    g = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([g.choice(w.batch * w.dim, 4096, replace=False), [0, w.batch * w.dim - 1]]))
+    ref = state0.reshape(-1, w.dstate)[rows].double().numpy()
+    state = state0.cuda()
+    pg = dev(p)
+    worst_y = worst_s = 0.0
+    for s in range(w.seqlen):
+        st = gen.decode_step_inputs(4, s)
+        if s % 32 == 0:
+            note(f"workload 4 decode step {s}")
+        before = state.cpu() if s < 2 else None
+        y = gpu_step(state, pg, dev(st))
+        torch.cuda.synchronize()
+        if before is not None:   # every row on the first two steps, from the GPU's own prior state
+            yr_full, sr_full = oracle.step(before, st["u"], st["delta"], p["A"], st["B"], st["C"], p["D"], st["z"],
+                                           p["dt_bias"])
+            assert oracle.rel_err(f64(y), yr_full) <= TOL["bf16"]
+            assert oracle.rel_err(f64(state), sr_full) <= 1e-5
+        yr, ref = oracle.step(ref, st["u"], st["delta"], p["A"], st["B"], st["C"], p["D"], st["z"], p["dt_bias"],
+                              chans=rows)
+        ey = oracle.rel_err(f64(y).reshape(-1)[rows], yr)
+        es = oracle.rel_err(f64(state).reshape(-1, w.dstate)[rows], ref)
+        worst_y, worst_s = max(worst_y, ey), max(worst_s, es)
+        assert ey <= TOL["bf16"], (s, ey)
+        assert es <= TOL["bf16"], (s, es)
+    note(f"  worst y err {worst_y:.3e}  worst state err {worst_s:.3e}")
+
+
+def test_prefill_then_decode_handoff():
+    L, k = 1000, 5
+    x = gen.random_scan_inputs(2, 80, 16, L + k, "bf16", seed=8)
+    note("prefill -> decode hand-off")
+    g = dev(x)
+    pre = {key: g[key][..., :L].contiguous() for key in ("u", "delta", "z", "B", "C")}
+    _, state = ssm.scan_fwd(pre["u"], pre["delta"], g["A"], pre["B"], pre["C"], g["D"], pre["z"], g["dt_bias"])
+    ys = []
+    for t in range(L, L + k):
+        st = {key: g[key][..., t].contiguous() for key in ("u", "delta", "z", "B", "C")}
+        ys.append(gpu_step(state, g, st))
+    torch.cuda.synchronize()
+    yr, lr = ref_scan(x)
+    for i, t in enumerate(range(L, L + k)):
+        assert oracle.rel_err(f64(ys[i]), yr[..., t]) <= TOL["bf16"]
+    assert oracle.rel_err(f64(state), lr) <= 1e-4
