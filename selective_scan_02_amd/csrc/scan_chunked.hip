@@ -1,0 +1,537 @@
+// scan_chunked.hip -- the main forward selective-scan kernel for gfx950.
+//
+// Why this shape.  At dstate = 16 the scan costs ~110 VALU issue slots per
+// element (16 exps at half rate plus 4 FMA-class ops per state, softplus and
+// SiLU) against ~8 bytes of HBM traffic, so on MI355X it is bound by the
+// vector ALUs, not by HBM.  The design therefore spends no VALU work that the
+// plain recurrence does not need, and finds parallelism without recomputation:
+//
+//  * Workgroup = 64 consecutive channels (b, d0..d0+63) x G waves.  Wave g owns
+//    states n in [g*N/G, (g+1)*N/G) of all 64 channels, one channel per lane.
+//    B_t[n] and C_t[n] are then uniform across the wave and live in SGPRs
+//    (scalar loads straight from global memory), so they cost no VALU or LDS
+//    bandwidth.  The readout sum over n is split across waves and combined
+//    through LDS.
+//  * Per element work that does not depend on n (softplus of the step, Delta*u,
+//    D*u, SiLU(z), the partial-sum reduction, the bf16 conversions) is done once,
+//    spread over all G waves by time step ("prep" and "finalize").
+//  * The sequence is processed in chunks of kT steps through a three-stage
+//    pipeline -- prep(j+1) | scan(j) | finalize(j-1) -- with one workgroup
+//    barrier per chunk.  Waves 0..G/2-1 run the scan stage first and waves
+//    G/2..G-1 last, so the two waves sharing a SIMD overlap VALU-heavy and
+//    LDS-heavy stages.  u, delta, z are fetched with 16-byte coalesced loads two
+//    chunks ahead and staged through LDS; y leaves through an LDS tile as
+//    16-byte coalesced stores.  Only y and the final state are written to HBM
+//    (fusion with on-chip intermediates: Mamba summary (junchaoiu.github.io),
+//    方法 step 2; tech.kj168168.com essay §二.3).
+//
+// Sequence parallelism (chunked two-level scan: "Mamba close reading"
+// (jsqmd.com) §2.2 and the sketch of §7; mlqm.cn tutorial §6).  The sequence is
+// cut into K segments; work unit (k, group) scans segment k of a channel group.
+//  MODE 0 (chained): persistent workgroups take units in order from an atomic
+//    ticket; unit (k, grp) starts from the end state of unit (k-1, grp), handed
+//    over through global memory with a release/acquire flag.  Units are ordered
+//    k-major, so a unit's predecessor was taken at least `groups` tickets
+//    earlier and has normally finished: no recomputation, full sequential
+//    exactness of the carry.  Used when there are enough channel groups to
+//    occupy the GPU.
+//  MODE 1 (output) with K = 1: one segment per group, no carry at all.
+//  MODE 2 (aggregate) + carry kernel + MODE 1 (output): for few channel groups
+//    (very long sequences).  Every segment but the last first computes its end
+//    state from h = 0 and its sum of Delta (the segment's transition is
+//    exp(A * sum Delta)); a carry kernel turns these into incoming states; the
+//    output pass reruns each segment from its incoming state.
+//
+// Deadlock freedom of MODE 0: a unit waits only on a unit with a smaller
+// ticket, which was taken by a workgroup that is already running; the oldest
+// unfinished unit never waits.  The wait is additionally bounded (it gives up
+// after ~2^26 polls), so every wave always reaches the exit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+namespace chunked {
+
+constexpr int kT = 16;  // time steps per chunk
+constexpr int kW = 64;  // channels per group = lanes per wave
+
+
+struct Args {
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* h0;
+  void* y;
+  float* last_state;
+  float* seg_h;   // MODE 1/2: [K, batch*dim, N]
+  float* seg_dt;  // MODE 2:   [K, batch*dim]
+  float* carry;   // MODE 0:   [groups, N, 64]
+  int* flags;     // MODE 0:   [units]
+  int* ticket;    // MODE 0:   1 counter
+  int64_t batch, dim, L, seg_len;
+  int gpr;     // channel groups per batch row
+  int groups;  // batch * gpr
+  int nseg;    // K
+  int units;   // K * groups
+  int softplus;
+};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// element e (0..kT-1) of a chunk row held as packed words
+template <typename TI>
+__device__ __forceinline__ float unpack(const uint32_t* w, int e) {
+  if constexpr (sizeof(TI) == 2) return (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
+  else return __builtin_bit_cast(float, w[e]);
+}
+
+template <typename TI>
+__device__ __forceinline__ float lds_elem(const unsigned char* row, int e) {
+  if constexpr (sizeof(TI) == 2) {
+    const uint16_t v = *reinterpret_cast<const uint16_t*>(row + 2 * e);
+    return __builtin_bit_cast(float, (uint32_t)v << 16);
+  } else {
+    return *reinterpret_cast<const float*>(row + 4 * e);
+  }
+}
+
+template <typename TI>
+__device__ __forceinline__ void lds_store_elem(unsigned char* row, int e, float v) {
+  if constexpr (sizeof(TI) == 2) {
+    *reinterpret_cast<__bf16*>(row + 2 * e) = (__bf16)v;
+  } else {
+    *reinterpret_cast<float*>(row + 4 * e) = v;
+  }
+}
+
+// LDS of one workgroup.
+template <int N, int G, typename TI, bool OUT>
+struct Smem {
+  static constexpr int ROWB = kT * sizeof(TI) + 4;  // padded row stride (bytes): conflict-free column access
+  unsigned char tile[2][3][kW * ROWB];               // u, delta, z of one chunk, [channel][t]
+  float2 dtdu[2][kT][kW];                            // (Delta, Delta*u), [t][channel]
+  float part[OUT ? 2 : 1][OUT ? G : 1][kT][kW];      // per-wave partial readouts
+  unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
+  float red[G][kW];
+  int unit;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) u32x4* kptr4;  // scalar 16-byte loads
+
+// Every 16-byte piece of u, delta, z, y, B and C is either entirely before
+// t_end or entirely after it: the fast path requires seqlen to be a multiple of
+// the piece length, and segments are multiples of kT.  So tails need only
+// whole-piece predicates.
+template <int N, int G, typename TI, int MODE>
+__global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
+  constexpr int NPW = N / G;         // states per wave
+  constexpr int ES = sizeof(TI);     // I/O element bytes
+  constexpr int EPP = 16 / ES;       // elements per 16-byte piece
+  constexpr int PPR = kT / EPP;      // pieces per tile row
+  constexpr int NTHR = kW * G;
+  constexpr int PIECES = 3 * kW * PPR;  // u, delta, z tiles of one chunk
+  constexpr int LPT = (PIECES + NTHR - 1) / NTHR;
+  constexpr int TPG = kT / G;  // prep / finalize steps per thread
+  constexpr bool OUT = MODE != 2;
+  constexpr int ROWB = Smem<N, G, TI, OUT>::ROWB;
+  static_assert(kT % G == 0 && N % G == 0, "bad split");
+  static_assert(kW * PPR <= NTHR, "one y piece per thread");
+
+  __shared__ Smem<N, G, TI, OUT> sm;
+
+  const int tid = threadIdx.x;
+  const int g = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index: uniform, keeps B/C loads scalar
+  const int lane = tid % kW;
+  const bool scan_first = g < G / 2 || G == 1;
+
+  for (int iter = 0;; ++iter) {
+    int unit;
+    if (MODE == 0) {
+      if (tid == 0) sm.unit = atomicAdd(a.ticket, 1);
+      __syncthreads();
+      unit = __builtin_amdgcn_readfirstlane(sm.unit);
+    } else {
+      unit = iter == 0 ? (int)blockIdx.x : a.units;
+    }
+    if (unit >= a.units) break;
+    const int k = unit / a.groups;
+    const int grp = unit - k * a.groups;
+    const int b = grp / a.gpr;
+    const int d0 = (grp - b * a.gpr) * kW;
+    const int64_t L = a.L;
+    const int64_t t_begin = (int64_t)k * a.seg_len;
+    const int len = (int)((t_begin + a.seg_len < L ? a.seg_len : L - t_begin));  // steps in this unit
+    const int nch = (len + kT - 1) / kT;
+
+    // this lane's channel (scan, prep and finalize all use channel d0 + lane)
+    const int c = d0 + lane;
+    const bool active = c < a.dim;
+    const int cc = active ? c : (int)a.dim - 1;
+    const int64_t ch = (int64_t)b * a.dim + cc;
+    const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
+    const float Dd = a.D ? a.D[cc] : 0.0f;
+    const bool gated = a.z != nullptr;
+    const bool sp = a.softplus != 0;
+    float A2[NPW], h[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + g * NPW + j] * kLog2e;
+
+    // per-thread global pointers of this unit (VGPRs): loader pieces and the y piece
+    const TI* lsrc[LPT];
+    int lstep[LPT];  // first step (relative to t_begin) of each loader piece within a chunk
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int p = tid + i * NTHR;
+      const int tensor = p / (kW * PPR);
+      const int row = (p / PPR) % kW;
+      const int q = p % PPR;
+      const TI* base = tensor == 0 ? (const TI*)a.u : tensor == 1 ? (const TI*)a.delta : (const TI*)a.z;
+      lsrc[i] = (p < PIECES && base && d0 + row < a.dim) ? base + ((int64_t)b * a.dim + d0 + row) * L + t_begin + q * EPP
+                                                        : nullptr;
+      lstep[i] = q * EPP;
+    }
+    const int yrow = tid / PPR, yq = tid % PPR;
+    TI* ydst = (OUT && tid < kW * PPR && d0 + yrow < a.dim)
+                   ? (TI*)a.y + ((int64_t)b * a.dim + d0 + yrow) * L + t_begin + yq * EPP
+                   : nullptr;
+    // B / C rows of this wave's states (uniform; 16-byte aligned rows)
+    kptr4 brow[NPW], crow[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int64_t e0 = ((int64_t)b * N + g * NPW + j) * L + t_begin;
+      brow[j] = (kptr4)(uintptr_t)((const unsigned char*)a.B + e0 * ES);
+      crow[j] = (kptr4)(uintptr_t)((const unsigned char*)a.C + e0 * ES);
+    }
+
+    // ---- incoming state -------------------------------------------------
+    if (MODE == 0 && k > 0) {
+      if (tid == 0) {
+        const int* f = a.flags + (unit - a.groups);
+        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
+          if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const float* cp = a.carry + (int64_t)grp * N * kW;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j)
+        h[j] = __hip_atomic_load(cp + (g * NPW + j) * kW + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (MODE == 1 && a.seg_h) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + g * NPW + j];
+    } else if (MODE != 2 && k == 0 && a.h0) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = a.h0[ch * N + g * NPW + j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = 0.0f;
+    }
+
+    float sdt = 0.0f;
+    float dsk[3][TPG], gat[3][TPG];  // D*u and silu(z) of chunks j-2, j-1, j (this thread's steps)
+    uint4 rcur[LPT], rnext[LPT];
+
+    // global -> registers: 16-byte pieces of chunk cj (zero past the end)
+#define SSM_LOAD_CHUNK(R, CJ)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
+    const int st0 = (CJ) * kT + lstep[i];                                                           \
+    R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
+                                  : make_uint4(0, 0, 0, 0);                                         \
+  }
+    // registers -> LDS tile
+#define SSM_STORE_TILE(BUF, R)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                              \
+    const int p = tid + i * NTHR;                                                                \
+    if (p < PIECES) {                                                                            \
+      const int tensor = p / (kW * PPR), row = (p / PPR) % kW, q = p % PPR;                      \
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[BUF][tensor][row * ROWB + q * 16]);  \
+      dst[0] = R[i].x; dst[1] = R[i].y; dst[2] = R[i].z; dst[3] = R[i].w;                        \
+    }                                                                                            \
+  }
+    // prep chunk J: Delta, Delta*u to LDS; D*u and silu(z) kept in registers for finalize
+#define SSM_PREP(J)                                                                               \
+  if ((J) < nch) {                                                                                \
+    const int buf = (J) & 1;                                                                      \
+    const unsigned char* ru = &sm.tile[buf][0][lane * ROWB];                                      \
+    const unsigned char* rd = &sm.tile[buf][1][lane * ROWB];                                      \
+    const unsigned char* rz = &sm.tile[buf][2][lane * ROWB];                                      \
+    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
+      const int tl = g * TPG + i;                                                                 \
+      const float x = lds_elem<TI>(rd, tl) + bias;                                                \
+      float dt = sp ? softplus(x) : x;                                                            \
+      if ((J) * kT + tl >= len) dt = 0.0f; /* past the end: identity step */                      \
+      const float ut = lds_elem<TI>(ru, tl);                                                      \
+      sm.dtdu[buf][tl][lane] = make_float2(dt, dt * ut);                                          \
+      if (MODE == 2) sdt += dt;                                                                   \
+      if (OUT) {                                                                                  \
+        dsk[2][i] = Dd * ut;                                                                      \
+        gat[2][i] = gated ? silu(lds_elem<TI>(rz, tl)) : 1.0f;                                    \
+      }                                                                                           \
+    }                                                                                             \
+  }
+    // finalize chunk J: sum the G partial readouts, add D*u, gate, round into the y tile
+#define SSM_FINALIZE(J)                                                                           \
+  if (OUT && (J) >= 0 && (J) < nch) {                                                             \
+    const int buf = (J) & 1;                                                                      \
+    unsigned char* ry = &sm.ytile[buf][lane * ROWB];                                              \
+    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
+      const int tl = g * TPG + i;                                                                 \
+      float acc = sm.part[buf][0][tl][lane];                                                      \
+      _Pragma("unroll") for (int w = 1; w < G; ++w) acc += sm.part[buf][w][tl][lane];             \
+      lds_store_elem<TI>(ry, tl, (acc + dsk[0][i]) * gat[0][i]);                                  \
+    }                                                                                             \
+  }
+
+    // prologue: chunk 0 into LDS, chunk 1 into registers
+    {
+      uint4 r0[LPT];
+      SSM_LOAD_CHUNK(r0, 0)
+      SSM_LOAD_CHUNK(rcur, 1)
+      SSM_STORE_TILE(0, r0)
+      __syncthreads();
+    }
+
+    const int last_j = nch + (OUT ? 3 : 1);
+    for (int j = 0; j < last_j; ++j) {
+      // 1. prefetch chunk j+2
+      SSM_LOAD_CHUNK(rnext, j + 2)
+
+      // 2. store y of chunk j-3 (16-byte pieces from the LDS tile)
+      if (OUT && j >= 3 && ydst && (j - 3) * kT + yq * EPP < len) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[(j - 3) & 1][yrow * ROWB + yq * 16]);
+        *reinterpret_cast<uint4*>(ydst + (j - 3) * kT) = make_uint4(src[0], src[1], src[2], src[3]);
+      }
+
+      if (!scan_first) {
+        SSM_PREP(j)
+        SSM_FINALIZE(j - 2)
+      }
+      // 3. scan chunk j-1 over this wave's states
+      if (j >= 1 && j <= nch) {
+        const int cj = j - 1, buf = cj & 1;
+#pragma unroll
+        for (int half = 0; half < kT / EPP; ++half) {
+          // B_t, C_t of 8 (bf16) or 4 (fp32) steps: one 16-byte scalar load per state and tensor
+          const bool ok = cj * kT + half * EPP < len;
+          uint32_t bw[NPW][4], cw[NPW][4];
+#pragma unroll
+          for (int jj = 0; jj < NPW; ++jj) {
+            const int off = ok ? cj * PPR + half : 0;
+            const u32x4 vb = brow[jj][off], vc = crow[jj][off];
+            bw[jj][0] = ok ? vb.x : 0u; bw[jj][1] = ok ? vb.y : 0u; bw[jj][2] = ok ? vb.z : 0u; bw[jj][3] = ok ? vb.w : 0u;
+            cw[jj][0] = ok ? vc.x : 0u; cw[jj][1] = ok ? vc.y : 0u; cw[jj][2] = ok ? vc.z : 0u; cw[jj][3] = ok ? vc.w : 0u;
+          }
+#pragma unroll
+          for (int e = 0; e < EPP; ++e) {
+            const int tl = half * EPP + e;
+            const float2 dd = sm.dtdu[buf][tl][lane];
+            float p = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < NPW; ++jj) {
+              const float ab = ex2(dd.x * A2[jj]);
+              h[jj] = __builtin_fmaf(ab, h[jj], dd.y * unpack<TI>(bw[jj], e));
+              if (OUT) p = jj == 0 ? unpack<TI>(cw[jj], e) * h[jj] : __builtin_fmaf(unpack<TI>(cw[jj], e), h[jj], p);
+            }
+            if (OUT) sm.part[buf][g][tl][lane] = p;
+          }
+        }
+      }
+      if (scan_first) {
+        SSM_PREP(j)
+        SSM_FINALIZE(j - 2)
+      }
+
+      // 4. registers -> LDS: chunk j+1
+      if (j + 1 < nch) SSM_STORE_TILE((j + 1) & 1, rcur)
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) rcur[i] = rnext[i];
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];
+        gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];
+      }
+    }
+#undef SSM_LOAD_CHUNK
+#undef SSM_STORE_TILE
+#undef SSM_PREP
+#undef SSM_FINALIZE
+
+    // ---- unit end: hand the state on ----
+    if (MODE == 2) {
+      if (active) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + g * NPW + j] = h[j];
+      }
+      sm.red[g][lane] = sdt;
+      __syncthreads();
+      if (g == 0 && active) {
+        float s2 = sm.red[0][lane];
+        for (int w = 1; w < G; ++w) s2 += sm.red[w][lane];
+        a.seg_dt[(int64_t)k * a.batch * a.dim + ch] = s2;
+      }
+    } else {
+      if (k == a.nseg - 1) {
+        if (a.last_state && active) {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) a.last_state[ch * N + g * NPW + j] = h[j];
+        }
+      } else if (MODE == 0) {
+        float* cp = a.carry + (int64_t)grp * N * kW;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)
+          __hip_atomic_store(cp + (g * NPW + j) * kW + lane, h[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(a.flags + unit, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (MODE != 0) break;
+  }
+}
+
+__global__ void zero_ints(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// One thread per (channel, n): turn per-segment end states (from h = 0) into
+// incoming states, in place: seg_h[s] <- state entering segment s.
+__global__ __launch_bounds__(256) void carry_kernel(float* seg_h, const float* seg_dt, const float* A,
+                                                    const float* h0, int64_t chans, int64_t dim, int N, int nseg) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= chans * N) return;
+  const int64_t chn = i / N;
+  const int n = (int)(i % N);
+  const float A2 = A[(chn % dim) * N + n] * kLog2e;
+  float h = h0 ? h0[i] : 0.0f;
+  for (int s = 0; s < nseg; ++s) {
+    const int64_t kk = (int64_t)s * chans * N + i;
+    const float agg = seg_h[kk];
+    seg_h[kk] = h;
+    h = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + chn]), h, agg);
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int N, typename TI>
+hipError_t run(const ScanParams& p, hipStream_t stream) {
+  constexpr int G = N >= 8 ? 8 : N;
+  Args a{};
+  a.u = p.u; a.delta = p.delta; a.z = p.z; a.B = p.B; a.C = p.C; a.A = p.A; a.D = p.D; a.dt_bias = p.dt_bias;
+  a.h0 = p.h0; a.y = p.y; a.last_state = p.last_state;
+  a.batch = p.batch; a.dim = p.dim; a.L = p.seqlen; a.softplus = p.softplus;
+  a.gpr = (int)((p.dim + kW - 1) / kW);
+  a.groups = (int)(p.batch * a.gpr);
+  const int64_t nch_total = (p.seqlen + kT - 1) / kT;
+  const int cus = cu_count();
+  const bool chained = a.groups >= cus / 2;
+  // units: ~8 per CU when chained (balance), ~4 per CU worth of parallel segments otherwise
+  const int64_t target_units = chained ? 8LL * cus : 4LL * cus;
+  int64_t K = std::max<int64_t>(1, std::min<int64_t>(nch_total, (target_units + a.groups - 1) / a.groups));
+  int64_t seg_chunks = (nch_total + K - 1) / K;
+  a.seg_len = seg_chunks * kT;
+  K = (p.seqlen + a.seg_len - 1) / a.seg_len;
+  a.nseg = (int)K;
+  a.units = (int)(K * a.groups);
+  const int64_t chans = p.batch * p.dim;
+  hipError_t err = hipSuccess;
+  void* scratch = nullptr;
+  if (chained && K > 1) {
+    const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
+    const size_t bytes = carry_bytes + (size_t)(a.units + 64) * sizeof(int);
+    if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
+    a.carry = (float*)scratch;
+    a.ticket = (int*)((char*)scratch + carry_bytes);
+    a.flags = a.ticket + 64;
+    const int nints = a.units + 64;
+    hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+      const int grid = std::min(a.units, cus);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 0>), dim3(grid), dim3(kW * G), 0, stream, a);
+      err = hipGetLastError();
+    }
+  } else if (K > 1) {
+    const size_t bytes = (size_t)K * chans * (N + 1) * sizeof(float);
+    if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
+    a.seg_h = (float*)scratch;
+    a.seg_dt = a.seg_h + (size_t)K * chans * N;
+    Args agg = a;
+    agg.units = (int)((K - 1) * a.groups);  // the last segment's aggregate is never needed
+    hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 2>), dim3(agg.units), dim3(kW * G), 0, stream, agg);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+      const int64_t threads = chans * N;
+      hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.seg_h,
+                         a.seg_dt, p.A, p.h0, chans, p.dim, N, (int)K);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 1>), dim3(a.units), dim3(kW * G), 0, stream, a);
+      err = hipGetLastError();
+    }
+  } else {
+    // one segment: a plain output pass from h0 / zeros
+    a.nseg = 1;
+    hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 1>), dim3(a.units), dim3(kW * G), 0, stream, a);
+    err = hipGetLastError();
+  }
+  if (scratch) {
+    hipError_t ferr = hipFreeAsync(scratch, stream);
+    if (err == hipSuccess) err = ferr;
+  }
+  return err;
+}
+
+template <typename TI>
+hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
+  switch (p.dstate) {
+    case 4: return run<4, TI>(p, s);
+    case 8: return run<8, TI>(p, s);
+    case 16: return run<16, TI>(p, s);
+    case 32: return run<32, TI>(p, s);
+    case 64: return run<64, TI>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace chunked
+
+bool chunked_supported(const ScanParams& p) {
+  const int es = p.dtype == kBF16 ? 2 : 4;
+  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
+  return p.dstate >= 4 && (p.seqlen * es) % 16 == 0 && p.seqlen < (1LL << 31) && p.dim < (1LL << 30) && p.batch < (1LL << 30) &&
+         al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C);
+}
+
+hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream) {
+  return p.dtype == kBF16 ? chunked::dispatch_n<__bf16>(p, stream) : chunked::dispatch_n<float>(p, stream);
+}
+
+}  // namespace ssm

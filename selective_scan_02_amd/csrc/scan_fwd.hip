@@ -1,4 +1,8 @@
-// scan_fwd.hip -- forward selective scan on gfx950.
+// scan_fwd.hip -- generic forward selective scan on gfx950, and the dispatcher.
+//
+// The fast path is scan_chunked.hip; it needs 16-byte aligned rows
+// (seqlen * element size a multiple of 16) and 16-byte aligned u, delta, z, y.
+// Every other shape runs through the generic kernels below.
 //
 // Work decomposition.  Each (batch row b, channel d) is an independent
 // recurrence over t with dstate diagonal states.  A wavefront holds 64
@@ -209,7 +213,7 @@ hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
 
 bool dstate_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
 
-hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream) {
+hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream) {
   if (p.seqlen == 0) {
     if (p.last_state) {
       const size_t bytes = (size_t)p.batch * p.dim * p.dstate * sizeof(float);
@@ -219,6 +223,11 @@ hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream) {
     return hipSuccess;
   }
   return p.dtype == kBF16 ? dispatch_n<__bf16>(p, stream) : dispatch_n<float>(p, stream);
+}
+
+hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream) {
+  if (p.seqlen > 0 && chunked_supported(p)) return launch_scan_chunked(p, stream);
+  return launch_scan_generic(p, stream);
 }
 
 }  // namespace ssm

@@ -41,7 +41,10 @@ struct StepParams {
 };
 
 bool dstate_supported(int64_t n);
-hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
+hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment
+bool chunked_supported(const ScanParams& p);
+hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 
 }  // namespace ssm

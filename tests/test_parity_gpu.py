@@ -87,7 +87,32 @@ SHAPES = [
     (1, 33, 64, 129, "f32"),
     (4, 256, 16, 4096, "bf16"),
     (1, 64, 16, 20000, "f32"),
+    # fast (chunked) path: seqlen a multiple of the 16-byte piece, half-chunk tails
+    (1, 64, 16, 8, "bf16"),
+    (2, 100, 4, 1000, "bf16"),
+    (1, 130, 8, 2024, "f32"),
+    (3, 96, 32, 520, "bf16"),
+    (1, 70, 64, 264, "f32"),
 ]
+
+
+# Launch-shape coverage of the fast path: chained segments (many channel groups),
+# the two-pass aggregate/carry/output split (few groups, long sequences), one segment.
+LAUNCH_CASES = [
+    ("chained", 2, 8192, 16, 1000, "bf16", 512),
+    ("chained-f32", 1, 16384, 16, 512, "f32", 512),
+    ("two-pass", 1, 256, 16, 100_000, "f32", 24),
+    ("two-pass-bf16", 2, 64, 16, 65_536, "bf16", 24),
+    ("single-segment", 1, 128, 16, 16, "bf16", None),
+]
+
+
+@pytest.mark.parametrize("case", LAUNCH_CASES, ids=lambda c: c[0])
+def test_launch_shapes(case):
+    name, b, d, n, L, dt, k = case
+    note(f"launch shape {name}: B={b} D={d} N={n} L={L} {dt}")
+    x = gen.random_scan_inputs(b, d, n, L, dt, seed=len(name))
+    check_scan(x, chans=None if k is None else sampled(x, k, 7))
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
