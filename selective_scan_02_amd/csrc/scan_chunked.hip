@@ -34,7 +34,9 @@
 //    k-major, so a unit's predecessor was taken at least `groups` tickets
 //    earlier and has normally finished: no recomputation, full sequential
 //    exactness of the carry.  Used when there are enough channel groups to
-//    occupy the GPU.
+//    occupy the GPU.  The hand-over uses device-scope atomic loads and stores
+//    only (no agent-scope fences: on this multi-XCD part those write back or
+//    invalidate whole L2 caches).
 //  MODE 1 (output) with K = 1: one segment per group, no carry at all.
 //  MODE 2 (aggregate) + carry kernel + MODE 1 (output): for few channel groups
 //    (very long sequences).  Every segment but the last first computes its end
@@ -85,16 +87,6 @@ struct Args {
   int softplus;
 };
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-// element e (0..kT-1) of a chunk row held as packed words
-template <typename TI>
-__device__ __forceinline__ float unpack(const uint32_t* w, int e) {
-  if constexpr (sizeof(TI) == 2) return (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
-  else return __builtin_bit_cast(float, w[e]);
-}
-
 template <typename TI>
 __device__ __forceinline__ float lds_elem(const unsigned char* row, int e) {
   if constexpr (sizeof(TI) == 2) {
@@ -122,17 +114,30 @@ struct Smem {
   float2 dtdu[2][kT][kW];                            // (Delta, Delta*u), [t][channel]
   float part[OUT ? 2 : 1][OUT ? G : 1][kT][kW];      // per-wave partial readouts
   unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
+  float bc[3][2][N][kT];                             // B, C of a chunk in fp32 (3-deep ring)
   float red[G][kW];
   int unit;
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(4))) u32x4* kptr4;  // scalar 16-byte loads
+// B_t[n] and C_t[n] are uniform across a wave.  For each chunk of kT = 16 steps
+// a wave holds them in VGPRs, lane l carrying step (l mod 16) -- every 16-lane
+// row holds the same 16 values -- and the consuming VALU instruction reads
+// "lane t of my row" through the DPP row_newbcast source modifier.  The
+// broadcast is free (part of the multiply / FMA) and needs no scalar registers.
+// The loader threads stage each chunk's B and C rows into LDS as fp32 and every
+// wave reads its vectors with one LDS load each, so a DPP source register is
+// only ever written by an LDS load, never by a VALU instruction (a VALU write
+// followed within two instructions by a DPP read of the same register is a
+// hazard the compiler does not see through inline assembly).
+#define SSM_DPP_MUL(dst, bc, other, T) \
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #T " row_mask:0xf bank_mask:0xf" : "=v"(dst) : "v"(bc), "v"(other))
+#define SSM_DPP_FMAC(acc, bc, other, T) \
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #T " row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(bc), "v"(other))
 
-// Every 16-byte piece of u, delta, z, y, B and C is either entirely before
-// t_end or entirely after it: the fast path requires seqlen to be a multiple of
-// the piece length, and segments are multiples of kT.  So tails need only
-// whole-piece predicates.
+// Every 16-byte piece of u, delta, z, y and every 16-step group of B and C is
+// either entirely before the end of the unit or entirely after it: the fast
+// path requires seqlen to be a multiple of the piece length, and segments are
+// multiples of kT.  So tails need only whole-piece predicates.
 template <int N, int G, typename TI, int MODE>
 __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
   constexpr int NPW = N / G;         // states per wave
@@ -140,19 +145,22 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
   constexpr int PPR = kT / EPP;      // pieces per tile row
   constexpr int NTHR = kW * G;
-  constexpr int PIECES = 3 * kW * PPR;  // u, delta, z tiles of one chunk
+  constexpr int XPIECES = 3 * kW * PPR;          // u, delta, z tiles of one chunk
+  constexpr int PIECES = XPIECES + 2 * N * PPR;  // ... and the B, C rows of the chunk
   constexpr int LPT = (PIECES + NTHR - 1) / NTHR;
   constexpr int TPG = kT / G;  // prep / finalize steps per thread
   constexpr bool OUT = MODE != 2;
   constexpr int ROWB = Smem<N, G, TI, OUT>::ROWB;
+  static_assert(kT == 16, "the DPP broadcast addresses the 16 lanes of a row");
   static_assert(kT % G == 0 && N % G == 0, "bad split");
   static_assert(kW * PPR <= NTHR, "one y piece per thread");
 
   __shared__ Smem<N, G, TI, OUT> sm;
 
   const int tid = threadIdx.x;
-  const int g = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index: uniform, keeps B/C loads scalar
+  const int g = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index (uniform)
   const int lane = tid % kW;
+  const int lt = lane & (kT - 1);  // the step this lane carries in the B/C vectors
   const bool scan_first = g < G / 2 || G == 1;
 
   for (int iter = 0;; ++iter) {
@@ -187,44 +195,44 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + g * NPW + j] * kLog2e;
 
-    // per-thread global pointers of this unit (VGPRs): loader pieces and the y piece
+    // per-thread global pointers of this unit: loader pieces, the y piece, B/C elements
     const TI* lsrc[LPT];
     int lstep[LPT];  // first step (relative to t_begin) of each loader piece within a chunk
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int p = tid + i * NTHR;
-      const int tensor = p / (kW * PPR);
-      const int row = (p / PPR) % kW;
       const int q = p % PPR;
-      const TI* base = tensor == 0 ? (const TI*)a.u : tensor == 1 ? (const TI*)a.delta : (const TI*)a.z;
-      lsrc[i] = (p < PIECES && base && d0 + row < a.dim) ? base + ((int64_t)b * a.dim + d0 + row) * L + t_begin + q * EPP
-                                                        : nullptr;
+      const TI* src = nullptr;
+      if (p < XPIECES) {
+        const int tensor = p / (kW * PPR), row = (p / PPR) % kW;
+        const TI* base = tensor == 0 ? (const TI*)a.u : tensor == 1 ? (const TI*)a.delta : (const TI*)a.z;
+        if (base && d0 + row < a.dim) src = base + ((int64_t)b * a.dim + d0 + row) * L + t_begin + q * EPP;
+      } else if (p < PIECES) {
+        const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;
+        src = (tensor == 0 ? (const TI*)a.B : (const TI*)a.C) + ((int64_t)b * N + n) * L + t_begin + q * EPP;
+      }
+      lsrc[i] = src;
       lstep[i] = q * EPP;
     }
     const int yrow = tid / PPR, yq = tid % PPR;
     TI* ydst = (OUT && tid < kW * PPR && d0 + yrow < a.dim)
                    ? (TI*)a.y + ((int64_t)b * a.dim + d0 + yrow) * L + t_begin + yq * EPP
                    : nullptr;
-    // B / C rows of this wave's states (uniform; 16-byte aligned rows)
-    kptr4 brow[NPW], crow[NPW];
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) {
-      const int64_t e0 = ((int64_t)b * N + g * NPW + j) * L + t_begin;
-      brow[j] = (kptr4)(uintptr_t)((const unsigned char*)a.B + e0 * ES);
-      crow[j] = (kptr4)(uintptr_t)((const unsigned char*)a.C + e0 * ES);
-    }
 
     // ---- incoming state -------------------------------------------------
     if (MODE == 0 && k > 0) {
+      // Hand-over protocol (see the writer at the unit end): flag and state are
+      // device-scope atomics, coherent across the XCDs' L2 caches without any
+      // cache-wide write-back or invalidation; the state loads are issued only
+      // after the flag has been observed (thread 0) and a workgroup barrier.
       if (tid == 0) {
         const int* f = a.flags + (unit - a.groups);
-        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
+        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
           if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
           __builtin_amdgcn_s_sleep(1);
         }
       }
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
       for (int j = 0; j < NPW; ++j)
@@ -242,24 +250,34 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
 
     float sdt = 0.0f;
     float dsk[3][TPG], gat[3][TPG];  // D*u and silu(z) of chunks j-2, j-1, j (this thread's steps)
-    uint4 rcur[LPT], rnext[LPT];
+    uint4 rs[2][LPT];  // u/delta/z/B/C pieces of chunks in flight (chunk c in rs[c & 1])
 
-    // global -> registers: 16-byte pieces of chunk cj (zero past the end)
+    // global -> registers: 16-byte pieces of chunk CJ (zero past the end)
 #define SSM_LOAD_CHUNK(R, CJ)                                                                       \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
     const int st0 = (CJ) * kT + lstep[i];                                                           \
     R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
                                   : make_uint4(0, 0, 0, 0);                                         \
   }
-    // registers -> LDS tile
-#define SSM_STORE_TILE(BUF, R)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                              \
-    const int p = tid + i * NTHR;                                                                \
-    if (p < PIECES) {                                                                            \
-      const int tensor = p / (kW * PPR), row = (p / PPR) % kW, q = p % PPR;                      \
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[BUF][tensor][row * ROWB + q * 16]);  \
-      dst[0] = R[i].x; dst[1] = R[i].y; dst[2] = R[i].z; dst[3] = R[i].w;                        \
-    }                                                                                            \
+    // registers -> LDS: the u/delta/z tile of chunk CJ, and its B/C rows as fp32
+#define SSM_STORE_TILE(CJ, R)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                  \
+    const int p = tid + i * NTHR;                                                                    \
+    const int q = p % PPR;                                                                           \
+    if (p < XPIECES) {                                                                               \
+      const int tensor = p / (kW * PPR), row = (p / PPR) % kW;                                       \
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[(CJ) & 1][tensor][row * ROWB + q * 16]); \
+      dst[0] = R[i].x; dst[1] = R[i].y; dst[2] = R[i].z; dst[3] = R[i].w;                            \
+    } else if (p < PIECES) {                                                                         \
+      const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;                       \
+      float* dst = &sm.bc[(CJ) % 3][tensor][n][q * EPP];                                             \
+      const uint32_t w[4] = {R[i].x, R[i].y, R[i].z, R[i].w};                                        \
+      _Pragma("unroll") for (int e = 0; e < EPP; ++e) {                                              \
+        if constexpr (ES == 2) dst[e] = (e & 1) ? __builtin_bit_cast(float, w[e >> 1] & 0xffff0000u)  \
+                                                : __builtin_bit_cast(float, w[e >> 1] << 16);        \
+        else dst[e] = __builtin_bit_cast(float, w[e]);                                               \
+      }                                                                                              \
+    }                                                                                                \
   }
     // prep chunk J: Delta, Delta*u to LDS; D*u and silu(z) kept in registers for finalize
 #define SSM_PREP(J)                                                                               \
@@ -294,81 +312,79 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
       lds_store_elem<TI>(ry, tl, (acc + dsk[0][i]) * gat[0][i]);                                  \
     }                                                                                             \
   }
+    // one step T (a literal 0..15) of the recurrence for this wave's states
+#define SSM_STEP(T)                                                                               \
+  {                                                                                               \
+    const float2 dd = sm.dtdu[buf][T][lane];                                                      \
+    float p = 0.0f;                                                                               \
+    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
+      const float ab = ex2(dd.x * A2[jj]);                                                        \
+      float bu;                                                                                   \
+      SSM_DPP_MUL(bu, bB[jj], dd.y, T); /* Delta*u * B_t[n] */                                    \
+      h[jj] = __builtin_fmaf(ab, h[jj], bu);                                                      \
+      if (OUT) {                                                                                  \
+        if (jj == 0) SSM_DPP_MUL(p, bC[jj], h[jj], T); /* C_t[n] * h */                           \
+        else SSM_DPP_FMAC(p, bC[jj], h[jj], T);                                                   \
+      }                                                                                           \
+    }                                                                                             \
+    if (OUT) sm.part[buf][g][T][lane] = p;                                                        \
+  }
+    // scan chunk CJ: this wave's B/C vectors from LDS (lane carries step lt), then 16 steps
+#define SSM_SCAN(CJ)                                                                              \
+  if ((CJ) >= 0 && (CJ) < nch) {                                                                  \
+    const int buf = (CJ) & 1;                                                                     \
+    float bB[NPW], bC[NPW];                                                                       \
+    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
+      bB[jj] = sm.bc[(CJ) % 3][0][g * NPW + jj][lt];                                              \
+      bC[jj] = sm.bc[(CJ) % 3][1][g * NPW + jj][lt];                                              \
+    }                                                                                             \
+    SSM_STEP(0) SSM_STEP(1) SSM_STEP(2) SSM_STEP(3) SSM_STEP(4) SSM_STEP(5) SSM_STEP(6)           \
+    SSM_STEP(7) SSM_STEP(8) SSM_STEP(9) SSM_STEP(10) SSM_STEP(11) SSM_STEP(12) SSM_STEP(13)       \
+    SSM_STEP(14) SSM_STEP(15)                                                                     \
+  }
+    // iteration J (parity PP = J & 1): prefetch, store y(J-3), prep(J), scan(J-1), finalize(J-2)
+#define SSM_ITER(J, PP)                                                                           \
+  {                                                                                               \
+    SSM_LOAD_CHUNK(rs[PP], (J) + 2)                                                               \
+    if (OUT && (J) >= 3 && ydst && ((J) - 3) * kT + yq * EPP < len) {                             \
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[((J) - 3) & 1][yrow * ROWB + yq * 16]); \
+      *reinterpret_cast<uint4*>(ydst + ((J) - 3) * kT) = make_uint4(src[0], src[1], src[2], src[3]); \
+    }                                                                                             \
+    if (!scan_first) {                                                                            \
+      SSM_PREP(J)                                                                                 \
+      SSM_FINALIZE((J) - 2)                                                                       \
+    }                                                                                             \
+    SSM_SCAN((J) - 1)                                                                             \
+    if (scan_first) {                                                                             \
+      SSM_PREP(J)                                                                                 \
+      SSM_FINALIZE((J) - 2)                                                                       \
+    }                                                                                             \
+    if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, rs[1 - (PP)])                                      \
+    __syncthreads();                                                                              \
+    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
+      dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];                                               \
+      gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];                                               \
+    }                                                                                             \
+  }
 
     // prologue: chunk 0 into LDS, chunk 1 into registers
-    {
-      uint4 r0[LPT];
-      SSM_LOAD_CHUNK(r0, 0)
-      SSM_LOAD_CHUNK(rcur, 1)
-      SSM_STORE_TILE(0, r0)
-      __syncthreads();
-    }
+    SSM_LOAD_CHUNK(rs[0], 0)
+    SSM_LOAD_CHUNK(rs[1], 1)
+    SSM_STORE_TILE(0, rs[0])
+    __syncthreads();
 
     const int last_j = nch + (OUT ? 3 : 1);
-    for (int j = 0; j < last_j; ++j) {
-      // 1. prefetch chunk j+2
-      SSM_LOAD_CHUNK(rnext, j + 2)
-
-      // 2. store y of chunk j-3 (16-byte pieces from the LDS tile)
-      if (OUT && j >= 3 && ydst && (j - 3) * kT + yq * EPP < len) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[(j - 3) & 1][yrow * ROWB + yq * 16]);
-        *reinterpret_cast<uint4*>(ydst + (j - 3) * kT) = make_uint4(src[0], src[1], src[2], src[3]);
-      }
-
-      if (!scan_first) {
-        SSM_PREP(j)
-        SSM_FINALIZE(j - 2)
-      }
-      // 3. scan chunk j-1 over this wave's states
-      if (j >= 1 && j <= nch) {
-        const int cj = j - 1, buf = cj & 1;
-#pragma unroll
-        for (int half = 0; half < kT / EPP; ++half) {
-          // B_t, C_t of 8 (bf16) or 4 (fp32) steps: one 16-byte scalar load per state and tensor
-          const bool ok = cj * kT + half * EPP < len;
-          uint32_t bw[NPW][4], cw[NPW][4];
-#pragma unroll
-          for (int jj = 0; jj < NPW; ++jj) {
-            const int off = ok ? cj * PPR + half : 0;
-            const u32x4 vb = brow[jj][off], vc = crow[jj][off];
-            bw[jj][0] = ok ? vb.x : 0u; bw[jj][1] = ok ? vb.y : 0u; bw[jj][2] = ok ? vb.z : 0u; bw[jj][3] = ok ? vb.w : 0u;
-            cw[jj][0] = ok ? vc.x : 0u; cw[jj][1] = ok ? vc.y : 0u; cw[jj][2] = ok ? vc.z : 0u; cw[jj][3] = ok ? vc.w : 0u;
-          }
-#pragma unroll
-          for (int e = 0; e < EPP; ++e) {
-            const int tl = half * EPP + e;
-            const float2 dd = sm.dtdu[buf][tl][lane];
-            float p = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < NPW; ++jj) {
-              const float ab = ex2(dd.x * A2[jj]);
-              h[jj] = __builtin_fmaf(ab, h[jj], dd.y * unpack<TI>(bw[jj], e));
-              if (OUT) p = jj == 0 ? unpack<TI>(cw[jj], e) * h[jj] : __builtin_fmaf(unpack<TI>(cw[jj], e), h[jj], p);
-            }
-            if (OUT) sm.part[buf][g][tl][lane] = p;
-          }
-        }
-      }
-      if (scan_first) {
-        SSM_PREP(j)
-        SSM_FINALIZE(j - 2)
-      }
-
-      // 4. registers -> LDS: chunk j+1
-      if (j + 1 < nch) SSM_STORE_TILE((j + 1) & 1, rcur)
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) rcur[i] = rnext[i];
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];
-        gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];
-      }
+    for (int j = 0; j < last_j; j += 2) {
+      SSM_ITER(j, 0)
+      if (j + 1 < last_j) SSM_ITER(j + 1, 1)
     }
 #undef SSM_LOAD_CHUNK
 #undef SSM_STORE_TILE
 #undef SSM_PREP
 #undef SSM_FINALIZE
+#undef SSM_STEP
+#undef SSM_SCAN
+#undef SSM_ITER
 
     // ---- unit end: hand the state on ----
     if (MODE == 2) {
@@ -390,13 +406,20 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
           for (int j = 0; j < NPW; ++j) a.last_state[ch * N + g * NPW + j] = h[j];
         }
       } else if (MODE == 0) {
+        // Publish the end state: device-scope stores, then wait until every one of
+        // them is acknowledged (s_waitcnt 0: all counters drained) before the
+        // barrier, so the flag -- stored after the barrier -- can only become
+        // visible after the state.  The signal fences keep the compiler from
+        // moving the stores across the wait.
         float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
         for (int j = 0; j < NPW; ++j)
           __hip_atomic_store(cp + (g * NPW + j) * kW + lane, h[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
-        if (tid == 0) __hip_atomic_store(a.flags + unit, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(a.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (MODE != 0) break;
