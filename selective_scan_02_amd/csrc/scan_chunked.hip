@@ -58,6 +58,13 @@
 namespace ssm {
 namespace chunked {
 
+#ifndef SSM_CHAINED_UNITS_PER_CU
+#define SSM_CHAINED_UNITS_PER_CU 8
+#endif
+#ifndef SSM_SPLIT_UNITS_PER_CU
+#define SSM_SPLIT_UNITS_PER_CU 4
+#endif
+
 constexpr int kT = 16;  // time steps per chunk
 constexpr int kW = 64;  // channels per group = lanes per wave
 
@@ -161,7 +168,6 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
   const int g = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index (uniform)
   const int lane = tid % kW;
   const int lt = lane & (kT - 1);  // the step this lane carries in the B/C vectors
-  const bool scan_first = g < G / 2 || G == 1;
 
   for (int iter = 0;; ++iter) {
     int unit;
@@ -250,8 +256,13 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
 
     float sdt = 0.0f;
     float dsk[3][TPG], gat[3][TPG];  // D*u and silu(z) of chunks j-2, j-1, j (this thread's steps)
-    uint4 rs[2][LPT];  // u/delta/z/B/C pieces of chunks in flight (chunk c in rs[c & 1])
+    uint4 rs[2][LPT];                // u/delta/z/B/C pieces of chunks in flight (chunk c in rs[c & 1])
+    // unconditional-load pointers for full chunks: an unused piece reads a harmless valid address
+    const TI* lsrc_f[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) lsrc_f[i] = lsrc[i] ? lsrc[i] : (const TI*)a.u + t_begin + lstep[i];
 
+    // ---------------- pipeline stages (TB: LDS double-buffer index of the chunk) --------------
     // global -> registers: 16-byte pieces of chunk CJ (zero past the end)
 #define SSM_LOAD_CHUNK(R, CJ)                                                                       \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
@@ -259,14 +270,17 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
     R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
                                   : make_uint4(0, 0, 0, 0);                                         \
   }
+    // same for a chunk known to be full: no predicates
+#define SSM_LOAD_CHUNK_FULL(R, CJ)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
     // registers -> LDS: the u/delta/z tile of chunk CJ, and its B/C rows as fp32
-#define SSM_STORE_TILE(CJ, R)                                                                        \
+#define SSM_STORE_TILE(CJ, TB, R)                                                                    \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                  \
     const int p = tid + i * NTHR;                                                                    \
     const int q = p % PPR;                                                                           \
     if (p < XPIECES) {                                                                               \
       const int tensor = p / (kW * PPR), row = (p / PPR) % kW;                                       \
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[(CJ) & 1][tensor][row * ROWB + q * 16]); \
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[TB][tensor][row * ROWB + q * 16]);       \
       dst[0] = R[i].x; dst[1] = R[i].y; dst[2] = R[i].z; dst[3] = R[i].w;                            \
     } else if (p < PIECES) {                                                                         \
       const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;                       \
@@ -279,112 +293,171 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
       }                                                                                              \
     }                                                                                                \
   }
-    // prep chunk J: Delta, Delta*u to LDS; D*u and silu(z) kept in registers for finalize
-#define SSM_PREP(J)                                                                               \
-  if ((J) < nch) {                                                                                \
-    const int buf = (J) & 1;                                                                      \
-    const unsigned char* ru = &sm.tile[buf][0][lane * ROWB];                                      \
-    const unsigned char* rd = &sm.tile[buf][1][lane * ROWB];                                      \
-    const unsigned char* rz = &sm.tile[buf][2][lane * ROWB];                                      \
+    // prep chunk J: Delta, Delta*u to LDS; D*u and silu(z) kept in registers for finalize.
+    // TAIL: steps past the end of the unit become identity steps (Delta = 0).
+#define SSM_PREP(J, TB, TAIL)                                                                     \
+  {                                                                                               \
+    const unsigned char* ru = &sm.tile[TB][0][lane * ROWB];                                       \
+    const unsigned char* rd = &sm.tile[TB][1][lane * ROWB];                                       \
+    const unsigned char* rz = &sm.tile[TB][2][lane * ROWB];                                       \
+    float xv[TPG], uv[TPG], zv[TPG];                                                              \
+    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
+      xv[i] = lds_elem<TI>(rd, g * TPG + i);                                                      \
+      uv[i] = lds_elem<TI>(ru, g * TPG + i);                                                      \
+      zv[i] = lds_elem<TI>(rz, g * TPG + i);                                                      \
+    }                                                                                             \
     _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
       const int tl = g * TPG + i;                                                                 \
-      const float x = lds_elem<TI>(rd, tl) + bias;                                                \
+      const float x = xv[i] + bias;                                                               \
       float dt = sp ? softplus(x) : x;                                                            \
-      if ((J) * kT + tl >= len) dt = 0.0f; /* past the end: identity step */                      \
-      const float ut = lds_elem<TI>(ru, tl);                                                      \
-      sm.dtdu[buf][tl][lane] = make_float2(dt, dt * ut);                                          \
+      if (TAIL && (J) * kT + tl >= len) dt = 0.0f;                                                \
+      sm.dtdu[TB][tl][lane] = make_float2(dt, dt * uv[i]);                                        \
       if (MODE == 2) sdt += dt;                                                                   \
       if (OUT) {                                                                                  \
-        dsk[2][i] = Dd * ut;                                                                      \
-        gat[2][i] = gated ? silu(lds_elem<TI>(rz, tl)) : 1.0f;                                    \
+        dsk[2][i] = Dd * uv[i];                                                                   \
+        gat[2][i] = gated ? silu(zv[i]) : 1.0f;                                                   \
       }                                                                                           \
     }                                                                                             \
   }
     // finalize chunk J: sum the G partial readouts, add D*u, gate, round into the y tile
-#define SSM_FINALIZE(J)                                                                           \
-  if (OUT && (J) >= 0 && (J) < nch) {                                                             \
-    const int buf = (J) & 1;                                                                      \
-    unsigned char* ry = &sm.ytile[buf][lane * ROWB];                                              \
+#define SSM_FINALIZE(TB)                                                                          \
+  if (OUT) {                                                                                      \
+    unsigned char* ry = &sm.ytile[OUT ? (TB) : 0][lane * ROWB];                                   \
+    float pp[TPG][G];                                                                             \
+    _Pragma("unroll") for (int i = 0; i < TPG; ++i)                                               \
+      _Pragma("unroll") for (int w = 0; w < G; ++w) pp[i][w] = sm.part[OUT ? (TB) : 0][w][g * TPG + i][lane]; \
     _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
-      const int tl = g * TPG + i;                                                                 \
-      float acc = sm.part[buf][0][tl][lane];                                                      \
-      _Pragma("unroll") for (int w = 1; w < G; ++w) acc += sm.part[buf][w][tl][lane];             \
-      lds_store_elem<TI>(ry, tl, (acc + dsk[0][i]) * gat[0][i]);                                  \
+      float acc = pp[i][0];                                                                       \
+      _Pragma("unroll") for (int w = 1; w < G; ++w) acc += pp[i][w];                              \
+      lds_store_elem<TI>(ry, g * TPG + i, (acc + dsk[0][i]) * gat[0][i]);                         \
     }                                                                                             \
   }
-    // one step T (a literal 0..15) of the recurrence for this wave's states
-#define SSM_STEP(T)                                                                               \
+    // scan, first part: for step T, Abar = exp(Delta*A) and Delta*u*B_t[n] (independent of h)
+#define SSM_PRE(T)                                                                                \
+  _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                            \
+    abv[T][jj] = ex2(ddv[T].x * A2[jj]);                                                          \
+    SSM_DPP_MUL(buv[T][jj], bB[jj], ddv[T].y, T);                                                 \
+  }
+    // scan, second part: the recurrence and the readout C_t . h_t of step T
+#define SSM_CHAIN(T)                                                                              \
   {                                                                                               \
-    const float2 dd = sm.dtdu[buf][T][lane];                                                      \
     float p = 0.0f;                                                                               \
     _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
-      const float ab = ex2(dd.x * A2[jj]);                                                        \
-      float bu;                                                                                   \
-      SSM_DPP_MUL(bu, bB[jj], dd.y, T); /* Delta*u * B_t[n] */                                    \
-      h[jj] = __builtin_fmaf(ab, h[jj], bu);                                                      \
+      h[jj] = __builtin_fmaf(abv[T][jj], h[jj], buv[T][jj]);                                      \
       if (OUT) {                                                                                  \
-        if (jj == 0) SSM_DPP_MUL(p, bC[jj], h[jj], T); /* C_t[n] * h */                           \
+        if (jj == 0) SSM_DPP_MUL(p, bC[jj], h[jj], T);                                            \
         else SSM_DPP_FMAC(p, bC[jj], h[jj], T);                                                   \
       }                                                                                           \
     }                                                                                             \
-    if (OUT) sm.part[buf][g][T][lane] = p;                                                        \
+    if (OUT) pv[T] = p;                                                                           \
   }
-    // scan chunk CJ: this wave's B/C vectors from LDS (lane carries step lt), then 16 steps
-#define SSM_SCAN(CJ)                                                                              \
-  if ((CJ) >= 0 && (CJ) < nch) {                                                                  \
-    const int buf = (CJ) & 1;                                                                     \
+    // scan chunk CJ (LDS buffer TB) over this wave's states
+#define SSM_SCAN(CJ, TB)                                                                          \
+  {                                                                                               \
     float bB[NPW], bC[NPW];                                                                       \
     _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
       bB[jj] = sm.bc[(CJ) % 3][0][g * NPW + jj][lt];                                              \
       bC[jj] = sm.bc[(CJ) % 3][1][g * NPW + jj][lt];                                              \
     }                                                                                             \
-    SSM_STEP(0) SSM_STEP(1) SSM_STEP(2) SSM_STEP(3) SSM_STEP(4) SSM_STEP(5) SSM_STEP(6)           \
-    SSM_STEP(7) SSM_STEP(8) SSM_STEP(9) SSM_STEP(10) SSM_STEP(11) SSM_STEP(12) SSM_STEP(13)       \
-    SSM_STEP(14) SSM_STEP(15)                                                                     \
+    float2 ddv[kT];                                                                               \
+    _Pragma("unroll") for (int t = 0; t < kT; ++t) ddv[t] = sm.dtdu[TB][t][lane];                 \
+    float abv[kT][NPW], buv[kT][NPW], pv[OUT ? kT : 1];                                           \
+    /* exps and products of a group of steps first, then that group's recurrence; the group */    \
+    /* shrinks with the states per wave so that the registers stay bounded                   */    \
+    if constexpr (NPW <= 2) {                                                                     \
+      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7)      \
+      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) \
+      SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6)   \
+      SSM_CHAIN(7) SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10) SSM_CHAIN(11) SSM_CHAIN(12)            \
+      SSM_CHAIN(13) SSM_CHAIN(14) SSM_CHAIN(15)                                                   \
+    } else if constexpr (NPW <= 4) {                                                              \
+      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7)      \
+      SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6)   \
+      SSM_CHAIN(7)                                                                                \
+      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) \
+      SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10) SSM_CHAIN(11) SSM_CHAIN(12) SSM_CHAIN(13)           \
+      SSM_CHAIN(14) SSM_CHAIN(15)                                                                 \
+    } else {                                                                                      \
+      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) \
+      SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6) SSM_CHAIN(7) \
+      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10)       \
+      SSM_CHAIN(11)                                                                               \
+      SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) SSM_CHAIN(12) SSM_CHAIN(13) SSM_CHAIN(14)   \
+      SSM_CHAIN(15)                                                                               \
+    }                                                                                             \
+    if (OUT) {                                                                                    \
+      _Pragma("unroll") for (int t = 0; t < kT; ++t) sm.part[OUT ? (TB) : 0][g][t][lane] = pv[t]; \
+    }                                                                                             \
   }
-    // iteration J (parity PP = J & 1): prefetch, store y(J-3), prep(J), scan(J-1), finalize(J-2)
+    // y tile of chunk CJ (LDS buffer TB) -> global, 16-byte pieces
+#define SSM_STORE_Y(CJ, TB, TAIL)                                                                  \
+  if (OUT && ydst && (!(TAIL) || (CJ) * kT + yq * EPP < len)) {                                    \
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[OUT ? (TB) : 0][yrow * ROWB + yq * 16]); \
+    *reinterpret_cast<uint4*>(ydst + (CJ) * kT) = make_uint4(src[0], src[1], src[2], src[3]);       \
+  }
+#define SSM_ROTATE                                                                                \
+  _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                               \
+    dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];                                                 \
+    gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];                                                 \
+  }
+    // general iteration J (register parity PP = J & 1): every stage checks its range
 #define SSM_ITER(J, PP)                                                                           \
   {                                                                                               \
     SSM_LOAD_CHUNK(rs[PP], (J) + 2)                                                               \
-    if (OUT && (J) >= 3 && ydst && ((J) - 3) * kT + yq * EPP < len) {                             \
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[((J) - 3) & 1][yrow * ROWB + yq * 16]); \
-      *reinterpret_cast<uint4*>(ydst + ((J) - 3) * kT) = make_uint4(src[0], src[1], src[2], src[3]); \
-    }                                                                                             \
-    if (!scan_first) {                                                                            \
-      SSM_PREP(J)                                                                                 \
-      SSM_FINALIZE((J) - 2)                                                                       \
-    }                                                                                             \
-    SSM_SCAN((J) - 1)                                                                             \
-    if (scan_first) {                                                                             \
-      SSM_PREP(J)                                                                                 \
-      SSM_FINALIZE((J) - 2)                                                                       \
-    }                                                                                             \
-    if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, rs[1 - (PP)])                                      \
+    if ((J) >= 3) SSM_STORE_Y((J) - 3, ((J) - 3) & 1, true)                                       \
+    if ((J) < nch) SSM_PREP(J, (J) & 1, true)                                                     \
+    if ((J) >= 1 && (J) <= nch) SSM_SCAN((J) - 1, ((J) - 1) & 1)                                  \
+    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE(((J) - 2) & 1)                                   \
+    if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, ((J) + 1) & 1, rs[1 - (PP)])                       \
     __syncthreads();                                                                              \
-    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
-      dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];                                               \
-      gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];                                               \
-    }                                                                                             \
+    SSM_ROTATE                                                                                    \
+  }
+    // steady-state iteration: all stages active, all chunks full, compile-time buffers; prep,
+    // scan and finalize form one straight-line block the compiler can interleave
+#define SSM_ITER_STEADY(J, PP)                                                                    \
+  {                                                                                               \
+    SSM_LOAD_CHUNK_FULL(rs[PP], (J) + 2)                                                          \
+    SSM_STORE_Y((J) - 3, 1 - (PP), false)                                                         \
+    SSM_PREP(J, PP, false)                                                                        \
+    SSM_SCAN((J) - 1, 1 - (PP))                                                                   \
+    SSM_FINALIZE(PP)                                                                              \
+    SSM_STORE_TILE((J) + 1, 1 - (PP), rs[1 - (PP)])                                               \
+    __syncthreads();                                                                              \
+    SSM_ROTATE                                                                                    \
   }
 
     // prologue: chunk 0 into LDS, chunk 1 into registers
     SSM_LOAD_CHUNK(rs[0], 0)
     SSM_LOAD_CHUNK(rs[1], 1)
-    SSM_STORE_TILE(0, rs[0])
+    SSM_STORE_TILE(0, 0, rs[0])
     __syncthreads();
 
     const int last_j = nch + (OUT ? 3 : 1);
-    for (int j = 0; j < last_j; j += 2) {
-      SSM_ITER(j, 0)
-      if (j + 1 < last_j) SSM_ITER(j + 1, 1)
+    SSM_ITER(0, 0)
+    if (1 < last_j) SSM_ITER(1, 1)
+    if (2 < last_j) SSM_ITER(2, 0)
+    int j = 3;
+    const int nfull = len / kT;
+    for (; j + 3 < nfull; j += 2) {
+      SSM_ITER_STEADY(j, 1)
+      SSM_ITER_STEADY(j + 1, 0)
+    }
+    for (; j < last_j; j += 2) {
+      SSM_ITER(j, 1)
+      if (j + 1 < last_j) SSM_ITER(j + 1, 0)
     }
 #undef SSM_LOAD_CHUNK
+#undef SSM_LOAD_CHUNK_FULL
 #undef SSM_STORE_TILE
 #undef SSM_PREP
 #undef SSM_FINALIZE
-#undef SSM_STEP
+#undef SSM_PRE
+#undef SSM_CHAIN
 #undef SSM_SCAN
+#undef SSM_STORE_Y
+#undef SSM_ROTATE
 #undef SSM_ITER
+#undef SSM_ITER_STEADY
 
     // ---- unit end: hand the state on ----
     if (MODE == 2) {
@@ -474,8 +547,9 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   const int64_t nch_total = (p.seqlen + kT - 1) / kT;
   const int cus = cu_count();
   const bool chained = a.groups >= cus / 2;
-  // units: ~8 per CU when chained (balance), ~4 per CU worth of parallel segments otherwise
-  const int64_t target_units = chained ? 8LL * cus : 4LL * cus;
+  // work units per CU: chained -> enough units for balance, few enough that the per-unit
+  // pipeline fill and drain stay small; two-pass -> enough parallel segments to fill the GPU
+  const int64_t target_units = chained ? (int64_t)SSM_CHAINED_UNITS_PER_CU * cus : (int64_t)SSM_SPLIT_UNITS_PER_CU * cus;
   int64_t K = std::max<int64_t>(1, std::min<int64_t>(nch_total, (target_units + a.groups - 1) / a.groups));
   int64_t seg_chunks = (nch_total + K - 1) / K;
   a.seg_len = seg_chunks * kT;
