@@ -3,40 +3,41 @@
 // Why this shape.  At dstate = 16 the scan costs ~110 VALU issue slots per
 // element (16 exps at half rate plus 4 FMA-class ops per state, softplus and
 // SiLU) against ~8 bytes of HBM traffic, so on MI355X it is bound by the
-// vector ALUs, not by HBM.  The design therefore spends no VALU work that the
-// plain recurrence does not need, and finds parallelism without recomputation:
+// vector ALUs, not by HBM.  The design spends no VALU work that the plain
+// recurrence does not need and finds parallelism without recomputation.
 //
-//  * Workgroup = 64 consecutive channels (b, d0..d0+63) x G waves.  Wave g owns
-//    states n in [g*N/G, (g+1)*N/G) of all 64 channels, one channel per lane.
-//    B_t[n] and C_t[n] are then uniform across the wave and live in SGPRs
-//    (scalar loads straight from global memory), so they cost no VALU or LDS
-//    bandwidth.  The readout sum over n is split across waves and combined
-//    through LDS.
-//  * Per element work that does not depend on n (softplus of the step, Delta*u,
-//    D*u, SiLU(z), the partial-sum reduction, the bf16 conversions) is done once,
-//    spread over all G waves by time step ("prep" and "finalize").
-//  * The sequence is processed in chunks of kT steps through a three-stage
-//    pipeline -- prep(j+1) | scan(j) | finalize(j-1) -- with one workgroup
-//    barrier per chunk.  Waves 0..G/2-1 run the scan stage first and waves
-//    G/2..G-1 last, so the two waves sharing a SIMD overlap VALU-heavy and
-//    LDS-heavy stages.  u, delta, z are fetched with 16-byte coalesced loads two
+//  * Workgroup = 64 consecutive channels (b, d0..d0+63), one channel per lane,
+//    and 8 waves in two roles.  Waves 0..3 are SCANNERS: scanner s owns states
+//    n in [s*N/4, (s+1)*N/4) of all 64 channels and runs only the recurrence
+//    and the partial readout of its states -- a long stream of independent
+//    VALU work.  Waves 4..7 are HELPERS: they load u, delta, z, B, C, compute
+//    Delta = softplus(delta + dt_bias), Delta*u, D*u and SiLU(z) once per
+//    element, sum the four partial readouts, gate, round and store y.  A SIMD
+//    hosts one scanner and one helper, so the helper's latency-bound work hides
+//    under the scanner's arithmetic.
+//  * B_t[n] and C_t[n] are uniform across a scanner wave.  A scanner holds them
+//    in VGPRs, lane l carrying step (l mod 16) -- every 16-lane row holds the
+//    same 16 values -- and the consuming VALU instruction reads "lane t of my
+//    row" through the DPP row_newbcast source modifier: a free broadcast.
+//  * The sequence is processed in chunks of kT = 16 steps through a three-stage
+//    pipeline -- prep(j) | scan(j-1) | finalize(j-2) -- with one workgroup
+//    barrier per chunk.  u, delta, z, B, C are fetched with 16-byte loads two
 //    chunks ahead and staged through LDS; y leaves through an LDS tile as
-//    16-byte coalesced stores.  Only y and the final state are written to HBM
-//    (fusion with on-chip intermediates: Mamba summary (junchaoiu.github.io),
-//    方法 step 2; tech.kj168168.com essay §二.3).
+//    16-byte coalesced stores.  Only y and the final state reach HBM (fusion
+//    with on-chip intermediates: Mamba summary (junchaoiu.github.io), 方法 step
+//    2; tech.kj168168.com essay §二.3).
 //
 // Sequence parallelism (chunked two-level scan: "Mamba close reading"
 // (jsqmd.com) §2.2 and the sketch of §7; mlqm.cn tutorial §6).  The sequence is
 // cut into K segments; work unit (k, group) scans segment k of a channel group.
 //  MODE 0 (chained): persistent workgroups take units in order from an atomic
 //    ticket; unit (k, grp) starts from the end state of unit (k-1, grp), handed
-//    over through global memory with a release/acquire flag.  Units are ordered
-//    k-major, so a unit's predecessor was taken at least `groups` tickets
-//    earlier and has normally finished: no recomputation, full sequential
-//    exactness of the carry.  Used when there are enough channel groups to
-//    occupy the GPU.  The hand-over uses device-scope atomic loads and stores
-//    only (no agent-scope fences: on this multi-XCD part those write back or
-//    invalidate whole L2 caches).
+//    over through global memory with a flag.  Units are ordered k-major, so a
+//    unit's predecessor was taken at least `groups` tickets earlier and has
+//    normally finished: no recomputation, exact sequential carry.  Used when
+//    there are enough channel groups to occupy the GPU.  The hand-over uses
+//    device-scope atomic loads and stores only (no agent-scope fences: on this
+//    multi-XCD part those write back or invalidate whole L2 caches).
 //  MODE 1 (output) with K = 1: one segment per group, no carry at all.
 //  MODE 2 (aggregate) + carry kernel + MODE 1 (output): for few channel groups
 //    (very long sequences).  Every segment but the last first computes its end
@@ -65,9 +66,13 @@ namespace chunked {
 #define SSM_SPLIT_UNITS_PER_CU 4
 #endif
 
-constexpr int kT = 16;  // time steps per chunk
+constexpr int kT = 16;  // time steps per chunk (= lanes of a DPP row)
 constexpr int kW = 64;  // channels per group = lanes per wave
-
+constexpr int kS = 4;   // scanner waves
+constexpr int kH = 4;   // helper waves
+constexpr int kThreads = (kS + kH) * kW;
+constexpr int kHT = kH * kW;  // helper threads
+constexpr int kTPH = kT / kH; // steps per helper thread per chunk
 
 struct Args {
   const void* u;
@@ -114,60 +119,60 @@ __device__ __forceinline__ void lds_store_elem(unsigned char* row, int e, float 
 }
 
 // LDS of one workgroup.
-template <int N, int G, typename TI, bool OUT>
+template <int N, typename TI, bool OUT>
 struct Smem {
   static constexpr int ROWB = kT * sizeof(TI) + 4;  // padded row stride (bytes): conflict-free column access
-  unsigned char tile[2][3][kW * ROWB];               // u, delta, z of one chunk, [channel][t]
+  // u, delta, z of a chunk, [channel][t].  4-deep ring: chunk c is staged in iteration c-1,
+  // read by prep in iteration c and by finalize in iteration c+2, and its slot is reused for
+  // chunk c+4 in iteration c+3 -- always after a barrier that follows its last read.
+  unsigned char tile[4][3][kW * ROWB];
   float2 dtdu[2][kT][kW];                            // (Delta, Delta*u), [t][channel]
-  float part[OUT ? 2 : 1][OUT ? G : 1][kT][kW];      // per-wave partial readouts
+  float part[OUT ? 2 : 1][OUT ? kS : 1][kT][kW];     // partial readouts of the scanners
   unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
-  float bc[3][2][N][kT];                             // B, C of a chunk in fp32 (3-deep ring)
-  float red[G][kW];
+  float bc[4][2][N][kT];                             // B, C of a chunk in fp32 (ring, as tile)
+  float red[kH][kW];
   int unit;
 };
 
-// B_t[n] and C_t[n] are uniform across a wave.  For each chunk of kT = 16 steps
-// a wave holds them in VGPRs, lane l carrying step (l mod 16) -- every 16-lane
-// row holds the same 16 values -- and the consuming VALU instruction reads
-// "lane t of my row" through the DPP row_newbcast source modifier.  The
-// broadcast is free (part of the multiply / FMA) and needs no scalar registers.
-// The loader threads stage each chunk's B and C rows into LDS as fp32 and every
-// wave reads its vectors with one LDS load each, so a DPP source register is
-// only ever written by an LDS load, never by a VALU instruction (a VALU write
-// followed within two instructions by a DPP read of the same register is a
-// hazard the compiler does not see through inline assembly).
+// The DPP broadcast operands of the scanners are read from LDS (bc above), so a
+// DPP source register is only ever written by an LDS load, never by a VALU
+// instruction: a VALU write followed within two instructions by a DPP read of
+// the same register is a hazard the compiler does not see through inline
+// assembly (tests/test_isa.py checks the generated code for it).
 #define SSM_DPP_MUL(dst, bc, other, T) \
   asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #T " row_mask:0xf bank_mask:0xf" : "=v"(dst) : "v"(bc), "v"(other))
 #define SSM_DPP_FMAC(acc, bc, other, T) \
   asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #T " row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(bc), "v"(other))
 
-// Every 16-byte piece of u, delta, z, y and every 16-step group of B and C is
-// either entirely before the end of the unit or entirely after it: the fast
-// path requires seqlen to be a multiple of the piece length, and segments are
-// multiples of kT.  So tails need only whole-piece predicates.
-template <int N, int G, typename TI, int MODE>
-__global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
-  constexpr int NPW = N / G;         // states per wave
+// Every 16-byte piece of u, delta, z, y, B and C is either entirely before the
+// end of the unit or entirely after it: the fast path requires seqlen to be a
+// multiple of the piece length, and segments are multiples of kT.  So tails
+// need only whole-piece predicates.
+template <int N, typename TI, int MODE>
+__global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
+  constexpr int NPW = N / kS;        // states per scanner
   constexpr int ES = sizeof(TI);     // I/O element bytes
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
   constexpr int PPR = kT / EPP;      // pieces per tile row
-  constexpr int NTHR = kW * G;
   constexpr int XPIECES = 3 * kW * PPR;          // u, delta, z tiles of one chunk
   constexpr int PIECES = XPIECES + 2 * N * PPR;  // ... and the B, C rows of the chunk
-  constexpr int LPT = (PIECES + NTHR - 1) / NTHR;
-  constexpr int TPG = kT / G;  // prep / finalize steps per thread
+  constexpr int LPT = (PIECES + kHT - 1) / kHT;  // pieces per helper thread
   constexpr bool OUT = MODE != 2;
-  constexpr int ROWB = Smem<N, G, TI, OUT>::ROWB;
-  static_assert(kT == 16, "the DPP broadcast addresses the 16 lanes of a row");
-  static_assert(kT % G == 0 && N % G == 0, "bad split");
-  static_assert(kW * PPR <= NTHR, "one y piece per thread");
+  constexpr int ROWB = Smem<N, TI, OUT>::ROWB;
+  // steps per group of the scanner's exp-ahead / recurrence split (bounds the registers)
+  constexpr int SG = NPW <= 2 ? 16 : NPW <= 4 ? 8 : 4;
+  static_assert(N % kS == 0 && NPW >= 1, "dstate must be a multiple of 4");
+  static_assert(kW * PPR <= kHT, "one y piece per helper thread");
 
-  __shared__ Smem<N, G, TI, OUT> sm;
+  __shared__ Smem<N, TI, OUT> sm;
 
   const int tid = threadIdx.x;
-  const int g = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index (uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kW);  // wave index (uniform)
+  const bool scanner = wv < kS;
   const int lane = tid % kW;
-  const int lt = lane & (kT - 1);  // the step this lane carries in the B/C vectors
+  const int lt = lane & (kT - 1);            // the step this lane carries in the B/C vectors
+  const int hw = wv - kS;                    // helper index (helpers only)
+  const int htid = tid - kS * kW;            // helper thread index (helpers only)
 
   for (int iter = 0;; ++iter) {
     int unit;
@@ -187,26 +192,66 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
     const int64_t t_begin = (int64_t)k * a.seg_len;
     const int len = (int)((t_begin + a.seg_len < L ? a.seg_len : L - t_begin));  // steps in this unit
     const int nch = (len + kT - 1) / kT;
+    const int nfull = len / kT;
 
-    // this lane's channel (scan, prep and finalize all use channel d0 + lane)
+    // this lane's channel
     const int c = d0 + lane;
     const bool active = c < a.dim;
     const int cc = active ? c : (int)a.dim - 1;
     const int64_t ch = (int64_t)b * a.dim + cc;
+
+    // ---- scanner state --------------------------------------------------
+    float A2[NPW], h[NPW];
+    if (scanner) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + wv * NPW + j] * kLog2e;
+    }
+    // incoming state (the flag wait involves thread 0, a scanner, and a barrier for all)
+    if (MODE == 0 && k > 0) {
+      if (tid == 0) {
+        const int* f = a.flags + (unit - a.groups);
+        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
+          if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __syncthreads();
+      if (scanner) {
+        // Hand-over protocol (the writer is at the unit end): flag and state are
+        // device-scope atomics, coherent across the XCDs' L2 caches without any
+        // cache-wide write-back or invalidation; the state loads are issued only
+        // after the flag has been observed (thread 0) and a workgroup barrier.
+        const float* cp = a.carry + (int64_t)grp * N * kW;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)
+          h[j] = __hip_atomic_load(cp + (wv * NPW + j) * kW + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (scanner) {
+      if (MODE == 1 && a.seg_h) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + wv * NPW + j];
+      } else if (MODE != 2 && k == 0 && a.h0) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) h[j] = a.h0[ch * N + wv * NPW + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) h[j] = 0.0f;
+      }
+    }
+
+    // ---- helper state -----------------------------------------------------
     const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
     const float Dd = a.D ? a.D[cc] : 0.0f;
     const bool gated = a.z != nullptr;
     const bool sp = a.softplus != 0;
-    float A2[NPW], h[NPW];
-#pragma unroll
-    for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + g * NPW + j] * kLog2e;
-
-    // per-thread global pointers of this unit: loader pieces, the y piece, B/C elements
-    const TI* lsrc[LPT];
-    int lstep[LPT];  // first step (relative to t_begin) of each loader piece within a chunk
+    float sdt = 0.0f;
+    uint4 rs[2][LPT];                  // loader pieces of chunks in flight (chunk c in rs[c & 1])
+    const TI* lsrc[LPT];               // NULL: piece unused or past a tensor's rows
+    const TI* lsrc_f[LPT];             // unconditional-load version (a harmless valid address)
+    int lstep[LPT];                    // first step of the piece within a chunk
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int p = tid + i * NTHR;
+      const int p = htid + i * kHT;
       const int q = p % PPR;
       const TI* src = nullptr;
       if (p < XPIECES) {
@@ -219,72 +264,35 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
       }
       lsrc[i] = src;
       lstep[i] = q * EPP;
+      lsrc_f[i] = src ? src : (const TI*)a.u + t_begin + q * EPP;
     }
-    const int yrow = tid / PPR, yq = tid % PPR;
-    TI* ydst = (OUT && tid < kW * PPR && d0 + yrow < a.dim)
+    const int yrow = htid / PPR, yq = htid % PPR;
+    TI* ydst = (OUT && !scanner && htid < kW * PPR && d0 + yrow < a.dim)
                    ? (TI*)a.y + ((int64_t)b * a.dim + d0 + yrow) * L + t_begin + yq * EPP
                    : nullptr;
 
-    // ---- incoming state -------------------------------------------------
-    if (MODE == 0 && k > 0) {
-      // Hand-over protocol (see the writer at the unit end): flag and state are
-      // device-scope atomics, coherent across the XCDs' L2 caches without any
-      // cache-wide write-back or invalidation; the state loads are issued only
-      // after the flag has been observed (thread 0) and a workgroup barrier.
-      if (tid == 0) {
-        const int* f = a.flags + (unit - a.groups);
-        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
-          if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      __syncthreads();
-      const float* cp = a.carry + (int64_t)grp * N * kW;
-#pragma unroll
-      for (int j = 0; j < NPW; ++j)
-        h[j] = __hip_atomic_load(cp + (g * NPW + j) * kW + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (MODE == 1 && a.seg_h) {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + g * NPW + j];
-    } else if (MODE != 2 && k == 0 && a.h0) {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) h[j] = a.h0[ch * N + g * NPW + j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) h[j] = 0.0f;
-    }
-
-    float sdt = 0.0f;
-    float dsk[3][TPG], gat[3][TPG];  // D*u and silu(z) of chunks j-2, j-1, j (this thread's steps)
-    uint4 rs[2][LPT];                // u/delta/z/B/C pieces of chunks in flight (chunk c in rs[c & 1])
-    // unconditional-load pointers for full chunks: an unused piece reads a harmless valid address
-    const TI* lsrc_f[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) lsrc_f[i] = lsrc[i] ? lsrc[i] : (const TI*)a.u + t_begin + lstep[i];
-
-    // ---------------- pipeline stages (TB: LDS double-buffer index of the chunk) --------------
-    // global -> registers: 16-byte pieces of chunk CJ (zero past the end)
+    // ---------------- helper stages (TB: LDS double-buffer index of the chunk) -------------
+    // global -> registers: pieces of chunk CJ (zero past the end)
 #define SSM_LOAD_CHUNK(R, CJ)                                                                       \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
     const int st0 = (CJ) * kT + lstep[i];                                                           \
     R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
                                   : make_uint4(0, 0, 0, 0);                                         \
   }
-    // same for a chunk known to be full: no predicates
 #define SSM_LOAD_CHUNK_FULL(R, CJ)                                                                  \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
     // registers -> LDS: the u/delta/z tile of chunk CJ, and its B/C rows as fp32
 #define SSM_STORE_TILE(CJ, TB, R)                                                                    \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                  \
-    const int p = tid + i * NTHR;                                                                    \
+    const int p = htid + i * kHT;                                                                    \
     const int q = p % PPR;                                                                           \
     if (p < XPIECES) {                                                                               \
       const int tensor = p / (kW * PPR), row = (p / PPR) % kW;                                       \
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[TB][tensor][row * ROWB + q * 16]);       \
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.tile[(CJ) & 3][tensor][row * ROWB + q * 16]); \
       dst[0] = R[i].x; dst[1] = R[i].y; dst[2] = R[i].z; dst[3] = R[i].w;                            \
     } else if (p < PIECES) {                                                                         \
       const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;                       \
-      float* dst = &sm.bc[(CJ) % 3][tensor][n][q * EPP];                                             \
+      float* dst = &sm.bc[(CJ) & 3][tensor][n][q * EPP];                                             \
       const uint32_t w[4] = {R[i].x, R[i].y, R[i].z, R[i].w};                                        \
       _Pragma("unroll") for (int e = 0; e < EPP; ++e) {                                              \
         if constexpr (ES == 2) dst[e] = (e & 1) ? __builtin_bit_cast(float, w[e >> 1] & 0xffff0000u)  \
@@ -297,96 +305,39 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
     // TAIL: steps past the end of the unit become identity steps (Delta = 0).
 #define SSM_PREP(J, TB, TAIL)                                                                     \
   {                                                                                               \
-    const unsigned char* ru = &sm.tile[TB][0][lane * ROWB];                                       \
-    const unsigned char* rd = &sm.tile[TB][1][lane * ROWB];                                       \
-    const unsigned char* rz = &sm.tile[TB][2][lane * ROWB];                                       \
-    float xv[TPG], uv[TPG], zv[TPG];                                                              \
-    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
-      xv[i] = lds_elem<TI>(rd, g * TPG + i);                                                      \
-      uv[i] = lds_elem<TI>(ru, g * TPG + i);                                                      \
-      zv[i] = lds_elem<TI>(rz, g * TPG + i);                                                      \
+    const unsigned char* ru = &sm.tile[(J) & 3][0][lane * ROWB];                                  \
+    const unsigned char* rd = &sm.tile[(J) & 3][1][lane * ROWB];                                  \
+    float xv[kTPH], uv[kTPH];                                                                     \
+    _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
+      xv[i] = lds_elem<TI>(rd, hw * kTPH + i);                                                    \
+      uv[i] = lds_elem<TI>(ru, hw * kTPH + i);                                                    \
     }                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
-      const int tl = g * TPG + i;                                                                 \
+    _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
+      const int tl = hw * kTPH + i;                                                               \
       const float x = xv[i] + bias;                                                               \
-      float dt = sp ? softplus(x) : x;                                                            \
-      if (TAIL && (J) * kT + tl >= len) dt = 0.0f;                                                \
+      float dt = softplus(x);                  /* branch-free: the flag selects, no branch */     \
+      dt = sp ? dt : x;                                                                           \
+      if (TAIL) dt = (J) * kT + tl < len ? dt : 0.0f;                                             \
       sm.dtdu[TB][tl][lane] = make_float2(dt, dt * uv[i]);                                        \
       if (MODE == 2) sdt += dt;                                                                   \
-      if (OUT) {                                                                                  \
-        dsk[2][i] = Dd * uv[i];                                                                   \
-        gat[2][i] = gated ? silu(zv[i]) : 1.0f;                                                   \
-      }                                                                                           \
     }                                                                                             \
   }
-    // finalize chunk J: sum the G partial readouts, add D*u, gate, round into the y tile
-#define SSM_FINALIZE(TB)                                                                          \
+    // finalize a chunk (LDS buffer TB): sum the partial readouts, add D*u, gate, round into the y tile
+#define SSM_FINALIZE(J, TB)                                                                       \
   if (OUT) {                                                                                      \
     unsigned char* ry = &sm.ytile[OUT ? (TB) : 0][lane * ROWB];                                   \
-    float pp[TPG][G];                                                                             \
-    _Pragma("unroll") for (int i = 0; i < TPG; ++i)                                               \
-      _Pragma("unroll") for (int w = 0; w < G; ++w) pp[i][w] = sm.part[OUT ? (TB) : 0][w][g * TPG + i][lane]; \
-    _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                             \
-      float acc = pp[i][0];                                                                       \
-      _Pragma("unroll") for (int w = 1; w < G; ++w) acc += pp[i][w];                              \
-      lds_store_elem<TI>(ry, g * TPG + i, (acc + dsk[0][i]) * gat[0][i]);                         \
+    const unsigned char* ru = &sm.tile[(J) & 3][0][lane * ROWB];                                  \
+    const unsigned char* rz = &sm.tile[(J) & 3][2][lane * ROWB];                                  \
+    float pp[kTPH][kS], uv[kTPH], zv[kTPH];                                                       \
+    _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
+      _Pragma("unroll") for (int w = 0; w < kS; ++w) pp[i][w] = sm.part[OUT ? (TB) : 0][w][hw * kTPH + i][lane]; \
+      uv[i] = lds_elem<TI>(ru, hw * kTPH + i);                                                    \
+      zv[i] = lds_elem<TI>(rz, hw * kTPH + i);                                                    \
     }                                                                                             \
-  }
-    // scan, first part: for step T, Abar = exp(Delta*A) and Delta*u*B_t[n] (independent of h)
-#define SSM_PRE(T)                                                                                \
-  _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                            \
-    abv[T][jj] = ex2(ddv[T].x * A2[jj]);                                                          \
-    SSM_DPP_MUL(buv[T][jj], bB[jj], ddv[T].y, T);                                                 \
-  }
-    // scan, second part: the recurrence and the readout C_t . h_t of step T
-#define SSM_CHAIN(T)                                                                              \
-  {                                                                                               \
-    float p = 0.0f;                                                                               \
-    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
-      h[jj] = __builtin_fmaf(abv[T][jj], h[jj], buv[T][jj]);                                      \
-      if (OUT) {                                                                                  \
-        if (jj == 0) SSM_DPP_MUL(p, bC[jj], h[jj], T);                                            \
-        else SSM_DPP_FMAC(p, bC[jj], h[jj], T);                                                   \
-      }                                                                                           \
-    }                                                                                             \
-    if (OUT) pv[T] = p;                                                                           \
-  }
-    // scan chunk CJ (LDS buffer TB) over this wave's states
-#define SSM_SCAN(CJ, TB)                                                                          \
-  {                                                                                               \
-    float bB[NPW], bC[NPW];                                                                       \
-    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
-      bB[jj] = sm.bc[(CJ) % 3][0][g * NPW + jj][lt];                                              \
-      bC[jj] = sm.bc[(CJ) % 3][1][g * NPW + jj][lt];                                              \
-    }                                                                                             \
-    float2 ddv[kT];                                                                               \
-    _Pragma("unroll") for (int t = 0; t < kT; ++t) ddv[t] = sm.dtdu[TB][t][lane];                 \
-    float abv[kT][NPW], buv[kT][NPW], pv[OUT ? kT : 1];                                           \
-    /* exps and products of a group of steps first, then that group's recurrence; the group */    \
-    /* shrinks with the states per wave so that the registers stay bounded                   */    \
-    if constexpr (NPW <= 2) {                                                                     \
-      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7)      \
-      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) \
-      SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6)   \
-      SSM_CHAIN(7) SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10) SSM_CHAIN(11) SSM_CHAIN(12)            \
-      SSM_CHAIN(13) SSM_CHAIN(14) SSM_CHAIN(15)                                                   \
-    } else if constexpr (NPW <= 4) {                                                              \
-      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7)      \
-      SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6)   \
-      SSM_CHAIN(7)                                                                                \
-      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) \
-      SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10) SSM_CHAIN(11) SSM_CHAIN(12) SSM_CHAIN(13)           \
-      SSM_CHAIN(14) SSM_CHAIN(15)                                                                 \
-    } else {                                                                                      \
-      SSM_PRE(0) SSM_PRE(1) SSM_PRE(2) SSM_PRE(3) SSM_CHAIN(0) SSM_CHAIN(1) SSM_CHAIN(2) SSM_CHAIN(3) \
-      SSM_PRE(4) SSM_PRE(5) SSM_PRE(6) SSM_PRE(7) SSM_CHAIN(4) SSM_CHAIN(5) SSM_CHAIN(6) SSM_CHAIN(7) \
-      SSM_PRE(8) SSM_PRE(9) SSM_PRE(10) SSM_PRE(11) SSM_CHAIN(8) SSM_CHAIN(9) SSM_CHAIN(10)       \
-      SSM_CHAIN(11)                                                                               \
-      SSM_PRE(12) SSM_PRE(13) SSM_PRE(14) SSM_PRE(15) SSM_CHAIN(12) SSM_CHAIN(13) SSM_CHAIN(14)   \
-      SSM_CHAIN(15)                                                                               \
-    }                                                                                             \
-    if (OUT) {                                                                                    \
-      _Pragma("unroll") for (int t = 0; t < kT; ++t) sm.part[OUT ? (TB) : 0][g][t][lane] = pv[t]; \
+    _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
+      const float acc = (pp[i][0] + pp[i][1]) + (pp[i][2] + pp[i][3]);                            \
+      const float g = gated ? silu(zv[i]) : 1.0f;  /* select, not a branch */                     \
+      lds_store_elem<TI>(ry, hw * kTPH + i, (acc + Dd * uv[i]) * g);                              \
     }                                                                                             \
   }
     // y tile of chunk CJ (LDS buffer TB) -> global, 16-byte pieces
@@ -395,88 +346,149 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(&sm.ytile[OUT ? (TB) : 0][yrow * ROWB + yq * 16]); \
     *reinterpret_cast<uint4*>(ydst + (CJ) * kT) = make_uint4(src[0], src[1], src[2], src[3]);       \
   }
-#define SSM_ROTATE                                                                                \
-  _Pragma("unroll") for (int i = 0; i < TPG; ++i) {                                               \
-    dsk[0][i] = dsk[1][i]; dsk[1][i] = dsk[2][i];                                                 \
-    gat[0][i] = gat[1][i]; gat[1][i] = gat[2][i];                                                 \
+
+    // ---------------- scanner stage ---------------------------------------------------------
+    // step T, first part: Abar = exp(Delta*A) and Delta*u*B_t[n] (independent of h)
+#define SSM_PRE(T)                                                                                \
+  _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                            \
+    abv[(T) % SG][jj] = ex2(ddv[T].x * A2[jj]);                                                   \
+    SSM_DPP_MUL(buv[(T) % SG][jj], bB[jj], ddv[T].y, T);                                          \
   }
-    // general iteration J (register parity PP = J & 1): every stage checks its range
-#define SSM_ITER(J, PP)                                                                           \
+    // step T, second part: the recurrence and the readout C_t . h_t
+#define SSM_CHAIN(T)                                                                              \
+  {                                                                                               \
+    float p = 0.0f;                                                                               \
+    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
+      h[jj] = __builtin_fmaf(abv[(T) % SG][jj], h[jj], buv[(T) % SG][jj]);                        \
+      if (OUT) {                                                                                  \
+        if (jj == 0) SSM_DPP_MUL(p, bC[jj], h[jj], T);                                            \
+        else SSM_DPP_FMAC(p, bC[jj], h[jj], T);                                                   \
+      }                                                                                           \
+    }                                                                                             \
+    if (OUT) pv[T] = p;                                                                           \
+  }
+#define SSM_PRE4(T0) SSM_PRE(T0) SSM_PRE(T0 + 1) SSM_PRE(T0 + 2) SSM_PRE(T0 + 3)
+#define SSM_CHAIN4(T0) SSM_CHAIN(T0) SSM_CHAIN(T0 + 1) SSM_CHAIN(T0 + 2) SSM_CHAIN(T0 + 3)
+    // scan chunk CJ (LDS buffer TB) over this scanner's states
+#define SSM_SCAN(CJ, TB)                                                                          \
+  {                                                                                               \
+    float bB[NPW], bC[NPW];                                                                       \
+    _Pragma("unroll") for (int jj = 0; jj < NPW; ++jj) {                                          \
+      bB[jj] = sm.bc[(CJ) & 3][0][wv * NPW + jj][lt];                                             \
+      bC[jj] = sm.bc[(CJ) & 3][1][wv * NPW + jj][lt];                                             \
+    }                                                                                             \
+    float2 ddv[kT];                                                                               \
+    _Pragma("unroll") for (int t = 0; t < kT; ++t) ddv[t] = sm.dtdu[TB][t][lane];                 \
+    float abv[SG][NPW], buv[SG][NPW], pv[OUT ? kT : 1];                                           \
+    /* exps and products of a group of steps first, then that group's recurrence */               \
+    if constexpr (SG == 16) {                                                                     \
+      SSM_PRE4(0) SSM_PRE4(4) SSM_PRE4(8) SSM_PRE4(12)                                            \
+      SSM_CHAIN4(0) SSM_CHAIN4(4) SSM_CHAIN4(8) SSM_CHAIN4(12)                                    \
+    } else if constexpr (SG == 8) {                                                               \
+      SSM_PRE4(0) SSM_PRE4(4) SSM_CHAIN4(0) SSM_CHAIN4(4)                                         \
+      SSM_PRE4(8) SSM_PRE4(12) SSM_CHAIN4(8) SSM_CHAIN4(12)                                       \
+    } else {                                                                                      \
+      SSM_PRE4(0) SSM_CHAIN4(0) SSM_PRE4(4) SSM_CHAIN4(4)                                         \
+      SSM_PRE4(8) SSM_CHAIN4(8) SSM_PRE4(12) SSM_CHAIN4(12)                                       \
+    }                                                                                             \
+    if (OUT) {                                                                                    \
+      _Pragma("unroll") for (int t = 0; t < kT; ++t) sm.part[OUT ? (TB) : 0][wv][t][lane] = pv[t]; \
+    }                                                                                             \
+  }
+
+    // ---------------- iterations ------------------------------------------------------------
+    // Iteration J: helpers prefetch chunk J+2, store y(J-3), prep(J), finalize(J-2) and stage
+    // chunk J+1 into LDS; scanners scan(J-1).  One workgroup barrier per iteration.  The two
+    // roles run separate loops with the same barrier sequence, so their registers never
+    // overlap.  Steady-state iterations (all stages active, full chunks) use compile-time LDS
+    // buffer indices and no stage predicates.
+    const int last_j = nch + (OUT ? 3 : 1);
+    if (scanner) {
+      __syncthreads();  // prologue
+      int j = 0;
+      for (; j < 3 && j < last_j; ++j) {
+        if (j >= 1 && j <= nch) SSM_SCAN(j - 1, (j - 1) & 1)
+        __syncthreads();
+      }
+      for (; j + 3 < nfull; j += 2) {
+        SSM_SCAN(j - 1, 0)  // j odd: chunk j-1 is even
+        __syncthreads();
+        SSM_SCAN(j, 1)
+        __syncthreads();
+      }
+      for (; j < last_j; ++j) {
+        if (j >= 1 && j <= nch) SSM_SCAN(j - 1, (j - 1) & 1)
+        __syncthreads();
+      }
+    } else {
+#define SSM_HELPER_ITER(J, PP)                                                                    \
   {                                                                                               \
     SSM_LOAD_CHUNK(rs[PP], (J) + 2)                                                               \
     if ((J) >= 3) SSM_STORE_Y((J) - 3, ((J) - 3) & 1, true)                                       \
     if ((J) < nch) SSM_PREP(J, (J) & 1, true)                                                     \
-    if ((J) >= 1 && (J) <= nch) SSM_SCAN((J) - 1, ((J) - 1) & 1)                                  \
-    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE(((J) - 2) & 1)                                   \
+    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE((J) - 2, ((J) - 2) & 1)                         \
     if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, ((J) + 1) & 1, rs[1 - (PP)])                       \
     __syncthreads();                                                                              \
-    SSM_ROTATE                                                                                    \
   }
-    // steady-state iteration: all stages active, all chunks full, compile-time buffers; prep,
-    // scan and finalize form one straight-line block the compiler can interleave
-#define SSM_ITER_STEADY(J, PP)                                                                    \
+#define SSM_HELPER_STEADY(J, PP)                                                                  \
   {                                                                                               \
     SSM_LOAD_CHUNK_FULL(rs[PP], (J) + 2)                                                          \
     SSM_STORE_Y((J) - 3, 1 - (PP), false)                                                         \
     SSM_PREP(J, PP, false)                                                                        \
-    SSM_SCAN((J) - 1, 1 - (PP))                                                                   \
-    SSM_FINALIZE(PP)                                                                              \
+    SSM_FINALIZE((J) - 2, PP)                                                                     \
     SSM_STORE_TILE((J) + 1, 1 - (PP), rs[1 - (PP)])                                               \
     __syncthreads();                                                                              \
-    SSM_ROTATE                                                                                    \
   }
-
-    // prologue: chunk 0 into LDS, chunk 1 into registers
-    SSM_LOAD_CHUNK(rs[0], 0)
-    SSM_LOAD_CHUNK(rs[1], 1)
-    SSM_STORE_TILE(0, 0, rs[0])
-    __syncthreads();
-
-    const int last_j = nch + (OUT ? 3 : 1);
-    SSM_ITER(0, 0)
-    if (1 < last_j) SSM_ITER(1, 1)
-    if (2 < last_j) SSM_ITER(2, 0)
-    int j = 3;
-    const int nfull = len / kT;
-    for (; j + 3 < nfull; j += 2) {
-      SSM_ITER_STEADY(j, 1)
-      SSM_ITER_STEADY(j + 1, 0)
-    }
-    for (; j < last_j; j += 2) {
-      SSM_ITER(j, 1)
-      if (j + 1 < last_j) SSM_ITER(j + 1, 0)
+      // prologue: chunk 0 into LDS, chunk 1 into registers
+      SSM_LOAD_CHUNK(rs[0], 0)
+      SSM_LOAD_CHUNK(rs[1], 1)
+      SSM_STORE_TILE(0, 0, rs[0])
+      __syncthreads();
+      SSM_HELPER_ITER(0, 0)
+      if (1 < last_j) SSM_HELPER_ITER(1, 1)
+      if (2 < last_j) SSM_HELPER_ITER(2, 0)
+      int j = 3;
+      for (; j + 3 < nfull; j += 2) {
+        SSM_HELPER_STEADY(j, 1)
+        SSM_HELPER_STEADY(j + 1, 0)
+      }
+      for (; j < last_j; j += 2) {
+        SSM_HELPER_ITER(j, 1)
+        if (j + 1 < last_j) SSM_HELPER_ITER(j + 1, 0)
+      }
+#undef SSM_HELPER_ITER
+#undef SSM_HELPER_STEADY
     }
 #undef SSM_LOAD_CHUNK
 #undef SSM_LOAD_CHUNK_FULL
 #undef SSM_STORE_TILE
 #undef SSM_PREP
 #undef SSM_FINALIZE
+#undef SSM_STORE_Y
 #undef SSM_PRE
 #undef SSM_CHAIN
+#undef SSM_PRE4
+#undef SSM_CHAIN4
 #undef SSM_SCAN
-#undef SSM_STORE_Y
-#undef SSM_ROTATE
-#undef SSM_ITER
-#undef SSM_ITER_STEADY
 
     // ---- unit end: hand the state on ----
     if (MODE == 2) {
-      if (active) {
+      if (scanner && active) {
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + g * NPW + j] = h[j];
+        for (int j2 = 0; j2 < NPW; ++j2) a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + wv * NPW + j2] = h[j2];
       }
-      sm.red[g][lane] = sdt;
+      if (!scanner) sm.red[hw][lane] = sdt;
       __syncthreads();
-      if (g == 0 && active) {
+      if (wv == kS && active) {
         float s2 = sm.red[0][lane];
-        for (int w = 1; w < G; ++w) s2 += sm.red[w][lane];
+        for (int w = 1; w < kH; ++w) s2 += sm.red[w][lane];
         a.seg_dt[(int64_t)k * a.batch * a.dim + ch] = s2;
       }
     } else {
       if (k == a.nseg - 1) {
-        if (a.last_state && active) {
+        if (scanner && a.last_state && active) {
 #pragma unroll
-          for (int j = 0; j < NPW; ++j) a.last_state[ch * N + g * NPW + j] = h[j];
+          for (int j2 = 0; j2 < NPW; ++j2) a.last_state[ch * N + wv * NPW + j2] = h[j2];
         }
       } else if (MODE == 0) {
         // Publish the end state: device-scope stores, then wait until every one of
@@ -484,10 +496,12 @@ __global__ __launch_bounds__(kW* G) void scan_chunked_kernel(const Args a) {
         // barrier, so the flag -- stored after the barrier -- can only become
         // visible after the state.  The signal fences keep the compiler from
         // moving the stores across the wait.
-        float* cp = a.carry + (int64_t)grp * N * kW;
+        if (scanner) {
+          float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
-        for (int j = 0; j < NPW; ++j)
-          __hip_atomic_store(cp + (g * NPW + j) * kW + lane, h[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int j2 = 0; j2 < NPW; ++j2)
+            __hip_atomic_store(cp + (wv * NPW + j2) * kW + lane, h[j2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -537,7 +551,6 @@ int cu_count() {
 
 template <int N, typename TI>
 hipError_t run(const ScanParams& p, hipStream_t stream) {
-  constexpr int G = N >= 8 ? 8 : N;
   Args a{};
   a.u = p.u; a.delta = p.delta; a.z = p.z; a.B = p.B; a.C = p.C; a.A = p.A; a.D = p.D; a.dt_bias = p.dt_bias;
   a.h0 = p.h0; a.y = p.y; a.last_state = p.last_state;
@@ -571,7 +584,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     err = hipGetLastError();
     if (err == hipSuccess) {
       const int grid = std::min(a.units, cus);
-      hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 0>), dim3(grid), dim3(kW * G), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0>), dim3(grid), dim3(kThreads), 0, stream, a);
       err = hipGetLastError();
     }
   } else if (K > 1) {
@@ -581,7 +594,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.seg_dt = a.seg_h + (size_t)K * chans * N;
     Args agg = a;
     agg.units = (int)((K - 1) * a.groups);  // the last segment's aggregate is never needed
-    hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 2>), dim3(agg.units), dim3(kW * G), 0, stream, agg);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2>), dim3(agg.units), dim3(kThreads), 0, stream, agg);
     err = hipGetLastError();
     if (err == hipSuccess) {
       const int64_t threads = chans * N;
@@ -590,13 +603,13 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 1>), dim3(a.units), dim3(kW * G), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1>), dim3(a.units), dim3(kThreads), 0, stream, a);
       err = hipGetLastError();
     }
   } else {
     // one segment: a plain output pass from h0 / zeros
     a.nseg = 1;
-    hipLaunchKernelGGL((scan_chunked_kernel<N, G, TI, 1>), dim3(a.units), dim3(kW * G), 0, stream, a);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1>), dim3(a.units), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
   }
   if (scratch) {
@@ -623,8 +636,8 @@ hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
 bool chunked_supported(const ScanParams& p) {
   const int es = p.dtype == kBF16 ? 2 : 4;
   auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
-  return p.dstate >= 4 && (p.seqlen * es) % 16 == 0 && p.seqlen < (1LL << 31) && p.dim < (1LL << 30) && p.batch < (1LL << 30) &&
-         al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C);
+  return p.dstate >= 4 && (p.seqlen * es) % 16 == 0 && p.seqlen < (1LL << 31) && p.dim < (1LL << 30) &&
+         p.batch < (1LL << 30) && al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C);
 }
 
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream) {
