@@ -103,6 +103,19 @@ int selective_state_update(float* state, const void* u, const void* delta, const
                            const void* C, const float* D, const void* z, const float* dt_bias, void* y,
                            int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream);
 
+/*
+ * Launch plan selective_scan_fwd would use for these sizes on a GPU with `num_cus`
+ * compute units (host-only; no GPU needed).  Writes 5 int64 values to `out`:
+ *   out[0] mode: 0 chained segments (persistent workgroups hand states on),
+ *                1 one pass per channel group, 2 aggregate + carry + output passes,
+ *                3 generic kernels (dstate < 4 or rows not a whole number of 16 bytes)
+ *   out[1] channel groups of 64, out[2] segments per group, out[3] steps per segment,
+ *   out[4] work units.
+ * Pointer alignment, checked per call, can also route a call to the generic kernels.
+ */
+int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype, int num_cus,
+                  int64_t* out);
+
 /* Text describing the calling thread's most recent non-OK status ("" if none). */
 const char* ssm_last_error(void);
 

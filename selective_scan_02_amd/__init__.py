@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["load", "lib_path", "scan_fwd", "state_update", "SsmError", "STATUS", "selective_scan_fwd",
+__all__ = ["load", "lib_path", "scan_fwd", "state_update", "scan_plan", "SsmError", "STATUS", "selective_scan_fwd",
            "selective_state_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_state_update", "ssm_last_error", "ssm_abi_version")
+EXPORTS = ("selective_scan_fwd", "selective_state_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -56,8 +56,21 @@ def load():
         lib.ssm_last_error.restype = ctypes.c_char_p
         lib.ssm_abi_version.argtypes = []
         lib.ssm_abi_version.restype = I
+        lib.ssm_scan_plan.argtypes = [I64, I64, I64, I64, I, I, ctypes.POINTER(ctypes.c_int64)]
+        lib.ssm_scan_plan.restype = I
         _lib = lib
     return _lib
+
+
+PLAN_MODES = {0: "chained", 1: "single", 2: "two-pass", 3: "generic"}
+
+
+def scan_plan(batch: int, dim: int, dstate: int, seqlen: int, dtype=torch.bfloat16, num_cus: int = 256) -> dict:
+    """The launch plan selective_scan_fwd uses for these sizes (host-only, no GPU)."""
+    out = (ctypes.c_int64 * 5)()
+    code = BF16 if dtype in (torch.bfloat16, "bf16", BF16) else F32
+    _check(load().ssm_scan_plan(batch, dim, dstate, seqlen, code, num_cus, out))
+    return {"mode": PLAN_MODES[out[0]], "groups": out[1], "segments": out[2], "seg_len": out[3], "units": out[4]}
 
 
 def last_error() -> str:

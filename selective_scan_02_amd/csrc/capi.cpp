@@ -63,6 +63,28 @@ const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
+int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype, int num_cus,
+                  int64_t* out) {
+  g_last_error.clear();
+  if (!out) return fail(SSM_ERR_NULL_ARG, "out is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0 || num_cus < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes");
+  if (!ssm::dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  const int64_t es = dtype == SSM_BF16 ? 2 : 4;
+  // the chunked kernels need dstate >= 4 and rows that are a whole number of 16-byte pieces
+  // (pointer alignment is checked per call); everything else takes the generic kernels
+  const bool chunked = dstate >= 4 && (seqlen * es) % 16 == 0 && seqlen > 0;
+  if (!chunked) {
+    out[0] = 3; out[1] = 0; out[2] = 0; out[3] = 0; out[4] = 0;
+    return SSM_OK;
+  }
+  const ssm::ScanPlan pl = ssm::plan_scan(batch, dim, seqlen, num_cus);
+  out[0] = pl.mode; out[1] = pl.groups; out[2] = pl.nseg; out[3] = pl.seg_len; out[4] = pl.units;
+  return SSM_OK;
+}
+
 int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                        const float* D, const void* z, const float* dt_bias, int softplus, void* y,
                        float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,

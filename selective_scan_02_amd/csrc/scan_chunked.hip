@@ -59,9 +59,6 @@
 namespace ssm {
 namespace chunked {
 
-#ifndef SSM_CHAINED_UNITS_PER_CU
-#define SSM_CHAINED_UNITS_PER_CU 8
-#endif
 #ifndef SSM_SPLIT_UNITS_PER_CU
 #define SSM_SPLIT_UNITS_PER_CU 4
 #endif
@@ -549,6 +546,43 @@ int cu_count() {
   return n;
 }
 
+}  // namespace chunked
+
+// Launch shape of the chunked scan for a given problem and CU count.
+//  * groups >= CUs: chained segments (mode 0).  A segment costs its chunks plus ~kUnitOverhead
+//    chunk-times of pipeline fill/drain and hand-over; the run takes ceil(units / CUs)
+//    rounds of one segment each.  K minimises that.
+//  * CUs/2 <= groups < CUs: one segment per group (mode 1) -- splitting a chain cannot
+//    shorten it when every chain already has a CU of its own.
+//  * fewer groups (long sequences): aggregate / carry / output passes (mode 2) over enough
+//    parallel segments to fill the GPU (SSM_SPLIT_UNITS_PER_CU per CU).
+ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus) {
+  using namespace chunked;
+  constexpr int64_t kUnitOverhead = 4;
+  ScanPlan pl{};
+  pl.groups = batch * ((dim + kW - 1) / kW);
+  const int64_t nch_total = std::max<int64_t>(1, (seqlen + kT - 1) / kT);
+  int64_t K = 1;
+  if (pl.groups >= cus) {
+    int64_t best = -1;
+    for (int64_t k = 1; k <= std::min<int64_t>(nch_total, 32); ++k) {
+      const int64_t rounds = (k * pl.groups + cus - 1) / cus;
+      const int64_t cost = rounds * ((nch_total + k - 1) / k + kUnitOverhead);
+      if (best < 0 || cost < best) { best = cost; K = k; }
+    }
+  } else if (2 * pl.groups < cus) {
+    const int64_t target_units = (int64_t)SSM_SPLIT_UNITS_PER_CU * cus;
+    K = std::max<int64_t>(1, std::min<int64_t>(nch_total, (target_units + pl.groups - 1) / pl.groups));
+  }
+  pl.seg_len = ((nch_total + K - 1) / K) * kT;
+  pl.nseg = std::max<int64_t>(1, (seqlen + pl.seg_len - 1) / pl.seg_len);
+  pl.mode = pl.nseg == 1 ? 1 : (pl.groups >= cus ? 0 : 2);
+  pl.units = pl.nseg * pl.groups;
+  return pl;
+}
+
+namespace chunked {
+
 template <int N, typename TI>
 hipError_t run(const ScanParams& p, hipStream_t stream) {
   Args a{};
@@ -556,19 +590,14 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.h0 = p.h0; a.y = p.y; a.last_state = p.last_state;
   a.batch = p.batch; a.dim = p.dim; a.L = p.seqlen; a.softplus = p.softplus;
   a.gpr = (int)((p.dim + kW - 1) / kW);
-  a.groups = (int)(p.batch * a.gpr);
-  const int64_t nch_total = (p.seqlen + kT - 1) / kT;
   const int cus = cu_count();
-  const bool chained = a.groups >= cus / 2;
-  // work units per CU: chained -> enough units for balance, few enough that the per-unit
-  // pipeline fill and drain stay small; two-pass -> enough parallel segments to fill the GPU
-  const int64_t target_units = chained ? (int64_t)SSM_CHAINED_UNITS_PER_CU * cus : (int64_t)SSM_SPLIT_UNITS_PER_CU * cus;
-  int64_t K = std::max<int64_t>(1, std::min<int64_t>(nch_total, (target_units + a.groups - 1) / a.groups));
-  int64_t seg_chunks = (nch_total + K - 1) / K;
-  a.seg_len = seg_chunks * kT;
-  K = (p.seqlen + a.seg_len - 1) / a.seg_len;
-  a.nseg = (int)K;
-  a.units = (int)(K * a.groups);
+  const ScanPlan pl = plan_scan(p.batch, p.dim, p.seqlen, cus);
+  a.groups = (int)pl.groups;
+  a.seg_len = pl.seg_len;
+  a.nseg = (int)pl.nseg;
+  a.units = (int)pl.units;
+  const int64_t K = pl.nseg;
+  const bool chained = pl.mode == 0;
   const int64_t chans = p.batch * p.dim;
   hipError_t err = hipSuccess;
   void* scratch = nullptr;

@@ -40,6 +40,15 @@ struct StepParams {
   int dtype;
 };
 
+struct ScanPlan {
+  int mode;          // 0 chained segments, 1 one pass, 2 aggregate/carry/output
+  int64_t groups;    // channel groups of 64
+  int64_t nseg;      // segments per group
+  int64_t seg_len;   // steps per segment
+  int64_t units;     // groups * nseg
+};
+ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
+
 bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment

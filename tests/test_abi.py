@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_state_update", "ssm_last_error", "ssm_abi_version"):
+    for name in ("selective_scan_fwd", "selective_state_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
 
@@ -138,3 +138,34 @@ def test_empty_sequence_allows_null_sequence_tensors(lib):
     # seqlen == 0: u, delta, B, C, y are empty and may be NULL; A is still required
     assert lib.selective_scan_fwd(*scan_args(seqlen=0, A=None, u=None)) == NULL_ARG
     assert "A" in ssm.last_error()
+
+
+def test_scan_plan_workloads(lib):
+    # 2.8B-shaped layer: 320 channel groups on 256 CUs -> 4 chained segments, 5 units per CU
+    p = ssm.scan_plan(4, 5120, 16, 2048)
+    assert p == {"mode": "chained", "groups": 320, "segments": 4, "seg_len": 512, "units": 1280}
+    # 130M-shaped layer: 192 groups < 256 CUs -> one pass per group
+    p = ssm.scan_plan(8, 1536, 16, 2048)
+    assert p["mode"] == "single" and p["groups"] == 192 and p["segments"] == 1
+    # 1M-step DNA-like scan: 4 groups -> aggregate/carry/output over ~4 units per CU
+    p = ssm.scan_plan(1, 256, 16, 1 << 20, torch_dtype_f32())
+    assert p["mode"] == "two-pass" and p["groups"] == 4 and p["units"] >= 1024
+    assert p["seg_len"] % 16 == 0 and p["segments"] * p["seg_len"] >= 1 << 20
+    # tiny fp32 workload: one group, short -> two-pass over a few segments
+    p = ssm.scan_plan(1, 16, 4, 64, torch_dtype_f32())
+    assert p["groups"] == 1 and p["segments"] * p["seg_len"] >= 64
+    # generic kernels: dstate < 4, or rows that are not whole 16-byte pieces
+    assert ssm.scan_plan(1, 64, 2, 256)["mode"] == "generic"
+    assert ssm.scan_plan(1, 64, 16, 777)["mode"] == "generic"
+
+
+def test_scan_plan_chained_segments_balance(lib):
+    for b, d, L in [(4, 5120, 2048), (2, 10240, 1000), (1, 20480, 512), (8, 5120, 4096)]:
+        p = ssm.scan_plan(b, d, 16, L)
+        assert p["mode"] in ("chained", "single")
+        assert p["segments"] * p["seg_len"] >= L and p["seg_len"] % 16 == 0
+
+
+def torch_dtype_f32():
+    import torch
+    return torch.float32

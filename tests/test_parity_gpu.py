@@ -99,8 +99,9 @@ SHAPES = [
 # Launch-shape coverage of the fast path: chained segments (many channel groups),
 # the two-pass aggregate/carry/output split (few groups, long sequences), one segment.
 LAUNCH_CASES = [
-    ("chained", 2, 8192, 16, 1000, "bf16", 512),
-    ("chained-f32", 1, 16384, 16, 512, "f32", 512),
+    ("chained", 2, 10240, 16, 1000, "bf16", 512),
+    ("chained-f32", 1, 20480, 16, 512, "f32", 512),
+    ("chained-n64", 2, 10240, 64, 296, "bf16", 256),
     ("two-pass", 1, 256, 16, 100_000, "f32", 24),
     ("two-pass-bf16", 2, 64, 16, 65_536, "bf16", 24),
     ("single-segment", 1, 128, 16, 16, "bf16", None),
@@ -110,7 +111,10 @@ LAUNCH_CASES = [
 @pytest.mark.parametrize("case", LAUNCH_CASES, ids=lambda c: c[0])
 def test_launch_shapes(case):
     name, b, d, n, L, dt, k = case
-    note(f"launch shape {name}: B={b} D={d} N={n} L={L} {dt}")
+    plan = ssm.scan_plan(b, d, n, L, torch.bfloat16 if dt == "bf16" else torch.float32)
+    note(f"launch shape {name}: B={b} D={d} N={n} L={L} {dt} plan={plan}")
+    expected = {"chained": "chained", "two-pass": "two-pass", "single-segment": "single"}
+    assert plan["mode"] == next(v for k, v in expected.items() if name.startswith(k))
     x = gen.random_scan_inputs(b, d, n, L, dt, seed=len(name))
     check_scan(x, chans=None if k is None else sampled(x, k, 7))
 
