@@ -5,12 +5,14 @@
 A step is one selective_scan_fwd over one batch of the workload (softplus,
 discretisation, chunked scan with carries, readout, D skip, SiLU gate, final
 state), with every input already resident in HBM.  Default workload: the
-2.8B-shaped layer (B=4, D=5120, N=16, L=2048, bf16 I/O, fp32 state).  The
-decode step (B=256, D=5120, N=16) is timed too and reported under "decode".
+2.8B-shaped layer (B=4, D=5120, N=16, L=2048, bf16 I/O, fp32 state).
 
-Prints one JSON line: elements/s (B*L*D), the roofline of the dominant kernel
-(ALU-bound: VALU issue slots per element, see ALGO_SLOTS) with its HBM
-bandwidth alongside, and the CPU fp64 oracle timed on this host as baseline.
+Prints one JSON line: elements/s (B*L*D) of that workload, the roofline of
+its scan kernel (ALU-bound: VALU issue slots per element, see algo_slots)
+with the HBM bandwidth alongside, and the CPU fp64 oracle timed on this host
+as baseline.  Also reported: the long-sequence scan (B=1, D=256, N=16,
+L=2^20, fp32) under "long", and the decode step (B=256, D=5120, N=16, 128
+steps) under "decode", flushed and back to back.
 """
 from __future__ import annotations
 
@@ -47,6 +49,11 @@ def algo_slots(N: int, gate: bool = True, skip: bool = True, softplus: bool = Tr
     return s
 
 
+# HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, per launch, scaled by
+# the same counters' reading for plain copies of known size; null until measured for the current kernel.
+TRAFFIC = {2: 362.2e6}
+
+
 def algo_bytes(B, D, N, L, es, gate=True, last_state=True):
     """HBM bytes of one scan: u, delta, (z) read, y written; B, C read; A, D, dt_bias; final state."""
     x = B * D * L * es * (3 + (1 if gate else 0))
@@ -63,8 +70,56 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-long", action="store_true", help="skip the long-sequence (L=2^20) scan figure")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the scan, run 5 plain device copies of MIB MiB each (reference dispatches for "
+                        "HBM byte counters)")
     return p.parse_args()
+
+
+def time_scan(torch, gen, ssm, w, steps, warmup, x=None):
+    """Time `steps` selective_scan_fwd calls on workload w; inputs resident in HBM.
+    Consecutive steps rotate over enough input copies to exceed the 256 MB last-level cache."""
+    import numpy as np
+    x = gen.scan_inputs(w) if x is None else x
+    B, D, N, L = w.batch, w.dim, w.dstate, w.seqlen
+    es = 2 if w.dtype == "bf16" else 4
+    elems = B * D * L
+    bytes_step = algo_bytes(B, D, N, L, es)
+    copies = max(1, min(4, int(np.ceil(1.0e9 / bytes_step))))
+    ins = [{k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()} for _ in range(copies)]
+    y = torch.empty_like(ins[0]["u"])
+    last = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        g = ins[i % copies]
+        ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"], True, y=y,
+                     last_state=last)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # every launch of the call goes to torch's current stream (the binding passes it), so
+    # events recorded on that stream bracket exactly the kernels of the timed steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / steps
+    slots = algo_slots(N)
+    tops = elems * slots / (ms * 1e-3) / 1e12
+    gbs = bytes_step / (ms * 1e-3) / 1e9
+    plan = ssm.scan_plan(B, D, N, L, torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                         torch.cuda.get_device_properties(0).multi_processor_count)
+    del ins, y, last
+    return dict(ms=ms, value=elems / (ms * 1e-3), elems=elems, slots=slots, tops=tops, gbs=gbs,
+                bytes_step=bytes_step, copies=copies, plan=plan, wall=t_wall)
 
 
 def main():
@@ -85,74 +140,68 @@ def main():
     torch.cuda.set_device(0)
     w = gen.WORKLOADS[args.workload]
     x = gen.scan_inputs(w)
+    r = time_scan(torch, gen, ssm, w, args.steps, args.warmup, x)
     B, D, N, L = w.batch, w.dim, w.dstate, w.seqlen
-    es = 2 if w.dtype == "bf16" else 4
-    elems = B * D * L
-    bytes_step = algo_bytes(B, D, N, L, es)
-    # rotate input copies so consecutive steps do not re-read from the 256 MB last-level cache
-    copies = max(1, min(4, int(np.ceil(1.0e9 / bytes_step))))
-    ins = []
-    for _ in range(copies):
-        ins.append({k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()})
-    y = torch.empty_like(ins[0]["u"])
-    last = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
-
-    def step(i):
-        g = ins[i % copies]
-        ssm.scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"], True, y=y,
-                     last_state=last)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    value = elems / (ms * 1e-3)
-
-    slots = algo_slots(N)
-    achieved_tops = elems * slots / (ms * 1e-3) / 1e12
-    hbm_gbs = bytes_step / (ms * 1e-3) / 1e9
     out = {
         "metric": "selective-scan fwd elements/s (B*L*D_inner)",
-        "value": value,
+        "value": r["value"],
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": r["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "d_inner": D, "d_state": N, "seqlen": L, "io_dtype": w.dtype,
-                   "state_dtype": "f32", "parallelism": "single-gpu", "input_copies_rotated": copies},
-        "roofline": {"bound": "alu", "achieved": achieved_tops, "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
-                     "frac": achieved_tops / PEAK_VALU_TOPS, "traffic": None,
-                     "ops_per_element": slots, "op": "fp32 VALU issue slot per lane (exp/log/rcp = 2)",
-                     "kernel": "selective_scan_fwd (whole call)"},
-        "hbm": {"achieved": hbm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_gbs / PEAK_HBM_GBS,
-                "bytes_per_step": bytes_step},
-        "wall_s_timed": t_wall,
+                   "state_dtype": "f32", "parallelism": "single-gpu", "input_copies_rotated": r["copies"],
+                   "launch_plan": r["plan"]},
+        "roofline": {"bound": "alu", "achieved": r["tops"], "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+                     "frac": r["tops"] / PEAK_VALU_TOPS, "traffic": TRAFFIC.get(args.workload),
+                     "ops_per_element": r["slots"], "op": "fp32 VALU issue slot per lane (exp/log/rcp = 2)",
+                     "kernel": "scan_chunked_kernel (the call's one scan kernel, plus a one-block flag clear "
+                               "when segments are chained)"},
+        "hbm": {"achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": r["gbs"] / PEAK_HBM_GBS,
+                "bytes_per_step": r["bytes_step"]},
+        "wall_s_timed": r["wall"],
     }
-
+    if not args.no_long and args.workload != 3:
+        wl = gen.WORKLOADS[3]
+        rl = time_scan(torch, gen, ssm, wl, max(3, args.steps // 10), 1)
+        out["long"] = {"workload": wl.name, "ms_per_step": rl["ms"], "value": rl["value"], "unit": "elements/s",
+                       "alu": {"achieved": rl["tops"], "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+                               "frac": rl["tops"] / PEAK_VALU_TOPS},
+                       "hbm": {"achieved": rl["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": rl["gbs"] / PEAK_HBM_GBS, "bytes_per_step": rl["bytes_step"]},
+                       "launch_plan": rl["plan"]}
     if not args.no_decode:
         out["decode"] = bench_decode(torch, gen, ssm, args)
-
+    if args.copy_calibration:
+        out["copy_calibration"] = copy_calibration(torch, args.copy_calibration)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np, gen, x, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
+def copy_calibration(torch, mib):
+    """Plain device-to-device copies of a known size: what a byte counter reads for them
+    gives the counter's scale (bytes counted per byte moved)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copies": 5, "bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4}
+
+
 def bench_decode(torch, gen, ssm, args):
+    """Decode steps of the 2.8B-shaped serving batch, 128 in a row on one state.
+    Reported twice: back to back (the 84 MB state stays in the 256 MB last-level cache) and
+    with the cache flushed before every step (a 1 GiB device read between steps, outside
+    the per-step events), which is the HBM-bound figure."""
     w = gen.WORKLOADS[4]
     p = {k: v.cuda() for k, v in gen.decode_params(4).items()}
     state = gen.decode_state(4).cuda()
@@ -167,38 +216,62 @@ def bench_decode(torch, gen, ssm, args):
         one(s)
     torch.cuda.synchronize()
     n = w.seqlen
+    stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for s in range(n):
         one(s)
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s in range(n):
+        torch.sum(flush, out=sink)  # reads 1 GiB: evicts the state, leaves no dirty lines behind
+        evs[s][0].record(stream)
+        one(s)
+        evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms_flushed = sum(a.elapsed_time(b) for a, b in evs) / n
+    del flush
     rows = w.batch * w.dim
     bytes_step = rows * w.dstate * 4 * 2 + rows * 2 * 4 + 2 * w.batch * w.dstate * 2 + w.dim * (w.dstate + 2) * 4
     gbs = bytes_step / (ms * 1e-3) / 1e9
-    return {"workload": w.name, "steps": n, "us_per_step": ms * 1e3, "rows_per_s": rows / (ms * 1e-3),
-            "hbm_achieved_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": bytes_step,
-            "note": "steady state: the 84 MB state stays resident in the 256 MB last-level cache between steps"}
+    gbs_f = bytes_step / (ms_flushed * 1e-3) / 1e9
+    return {"workload": w.name, "steps": n, "bytes_per_step": bytes_step,
+            "flushed": {"us_per_step": ms_flushed * 1e3, "rows_per_s": rows / (ms_flushed * 1e-3),
+                        "hbm_achieved_GBs": gbs_f, "hbm_frac": gbs_f / PEAK_HBM_GBS},
+            "steady": {"us_per_step": ms * 1e3, "rows_per_s": rows / (ms * 1e-3), "hbm_achieved_GBs": gbs,
+                       "hbm_frac": gbs / PEAK_HBM_GBS,
+                       "note": "back to back: the state stays resident in the last-level cache"}}
 
 
 def cpu_baseline(np, gen, x, w, target_s):
+    """The fp64 CPU oracle on the same workload.  When the whole workload takes less than
+    `target_s`, it is run repeatedly until `target_s` has elapsed; otherwise the first k
+    channels, with k chosen from a timed probe, form the sample."""
     import oracle
     threads = oracle.max_threads()
     total = w.batch * w.dim
+    args = (x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["dt_bias"], True)
     probe = np.arange(min(total, 256))
     t = time.perf_counter()
-    oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["dt_bias"], True, chans=probe)
+    oracle.scan(*args, chans=probe)
     dt = max(time.perf_counter() - t, 1e-6)
     k = int(min(total, max(len(probe), len(probe) * target_s / dt)))
-    chans = np.arange(k)
+    chans = None if k == total else np.arange(k)
+    reps, sec = 0, 0.0
     t = time.perf_counter()
-    oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["dt_bias"], True, chans=chans)
-    sec = time.perf_counter() - t
-    el = k * w.seqlen
+    while reps == 0 or sec < target_s:
+        oracle.scan(*args, chans=chans)
+        reps += 1
+        sec = time.perf_counter() - t
+    el = reps * k * w.seqlen
+    what = (f"the whole workload ({total} (b, d) channels x L={w.seqlen}) run {reps} times" if k == total
+            else f"the first {k} of {total} (b, d) channels, full length L={w.seqlen}")
     return {"value": el / sec, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {k} of {total} (b, d) channels of the same workload, full length L={w.seqlen} "
-                      f"({el} elements, {sec:.1f} s, fp64, OpenMP over channels)"}
+            "sample": f"{what}: {el} elements in {sec:.1f} s, fp64, OpenMP over channels"}
 
 
 if __name__ == "__main__":
