@@ -62,6 +62,12 @@ namespace chunked {
 #ifndef SSM_SPLIT_UNITS_PER_CU
 #define SSM_SPLIT_UNITS_PER_CU 4
 #endif
+#ifndef SSM_HELPER_PRIO
+#define SSM_HELPER_PRIO 1
+#endif
+#ifndef SSM_GATE_BLEND
+#define SSM_GATE_BLEND 1
+#endif
 
 constexpr int kT = 16;  // time steps per chunk (= lanes of a DPP row)
 constexpr int kW = 64;  // channels per group = lanes per wave
@@ -86,7 +92,7 @@ struct Args {
   float* seg_h;   // MODE 1/2: [K, batch*dim, N]
   float* seg_dt;  // MODE 2:   [K, batch*dim]
   float* carry;   // MODE 0:   [groups, N, 64]
-  int* flags;     // MODE 0:   [units]
+  int* flags;     // MODE 0:   [units, kS] one per scanner wave
   int* ticket;    // MODE 0:   1 counter
   int64_t batch, dim, L, seg_len;
   int gpr;     // channel groups per batch row
@@ -122,13 +128,13 @@ struct Smem {
   // u, delta, z of a chunk, [channel][t].  4-deep ring: chunk c is staged in iteration c-1,
   // read by prep in iteration c and by finalize in iteration c+2, and its slot is reused for
   // chunk c+4 in iteration c+3 -- always after a barrier that follows its last read.
-  unsigned char tile[4][3][kW * ROWB];
+  unsigned char tile[4][OUT ? 3 : 2][kW * ROWB];
   float2 dtdu[2][kT][kW];                            // (Delta, Delta*u), [t][channel]
   float part[OUT ? 2 : 1][OUT ? kS : 1][kT][kW];     // partial readouts of the scanners
   unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
   float bc[4][2][N][kT];                             // B, C of a chunk in fp32 (ring, as tile)
   float red[kH][kW];
-  int unit;
+  int unit[2];  // MODE 0: this unit's ticket and the next one (by iteration parity)
 };
 
 // The DPP broadcast operands of the scanners are read from LDS (bc above), so a
@@ -151,10 +157,11 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
   constexpr int ES = sizeof(TI);     // I/O element bytes
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
   constexpr int PPR = kT / EPP;      // pieces per tile row
-  constexpr int XPIECES = 3 * kW * PPR;          // u, delta, z tiles of one chunk
-  constexpr int PIECES = XPIECES + 2 * N * PPR;  // ... and the B, C rows of the chunk
-  constexpr int LPT = (PIECES + kHT - 1) / kHT;  // pieces per helper thread
   constexpr bool OUT = MODE != 2;
+  constexpr int XT = OUT ? 3 : 2;                // staged tiles: u, delta (and z for the output)
+  constexpr int XPIECES = XT * kW * PPR;         // pieces of those tiles in one chunk
+  constexpr int PIECES = XPIECES + (OUT ? 2 : 1) * N * PPR;  // ... and the B (and C) rows
+  constexpr int LPT = (PIECES + kHT - 1) / kHT;  // pieces per helper thread
   constexpr int ROWB = Smem<N, TI, OUT>::ROWB;
   // steps per group of the scanner's exp-ahead / recurrence split (bounds the registers)
   constexpr int SG = NPW <= 2 ? 16 : NPW <= 4 ? 8 : 4;
@@ -174,9 +181,13 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
   for (int iter = 0;; ++iter) {
     int unit;
     if (MODE == 0) {
-      if (tid == 0) sm.unit = atomicAdd(a.ticket, 1);
-      __syncthreads();
-      unit = __builtin_amdgcn_readfirstlane(sm.unit);
+      // The first ticket is taken here; every later one is taken by a helper thread during the
+      // previous unit (one unit ahead), so a unit starts without an atomic round trip.
+      if (iter == 0) {
+        if (tid == 0) sm.unit[0] = atomicAdd(a.ticket, 1);
+        __syncthreads();
+      }
+      unit = __builtin_amdgcn_readfirstlane(sm.unit[iter & 1]);
     } else {
       unit = iter == 0 ? (int)blockIdx.x : a.units;
     }
@@ -203,21 +214,21 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + wv * NPW + j] * kLog2e;
     }
-    // incoming state (the flag wait involves thread 0, a scanner, and a barrier for all)
+    // incoming state.  MODE 0: each scanner wave waits for the flag of the matching scanner
+    // wave of the predecessor unit and loads its own rows of the hand-over state; the helpers
+    // meanwhile start loading the unit's first chunks.
     if (MODE == 0 && k > 0) {
-      if (tid == 0) {
-        const int* f = a.flags + (unit - a.groups);
-        for (int spin = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin) {
+      if (scanner) {
+        const int* f = a.flags + (int64_t)(unit - a.groups) * kS + wv;
+        for (int spin = 0;
+             __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
+             ++spin) {
           if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
           __builtin_amdgcn_s_sleep(1);
         }
-      }
-      __syncthreads();
-      if (scanner) {
-        // Hand-over protocol (the writer is at the unit end): flag and state are
-        // device-scope atomics, coherent across the XCDs' L2 caches without any
-        // cache-wide write-back or invalidation; the state loads are issued only
-        // after the flag has been observed (thread 0) and a workgroup barrier.
+        // Hand-over protocol (the writer is at the unit end): flag and state are device-scope
+        // atomics, coherent across the XCDs' L2 caches without any cache-wide write-back or
+        // invalidation; the state loads are issued only after the flag has been observed.
         const float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
         for (int j = 0; j < NPW; ++j)
@@ -240,6 +251,8 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
     const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
     const float Dd = a.D ? a.D[cc] : 0.0f;
     const bool gated = a.z != nullptr;
+    uint32_t gmask = gated ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(gmask));  // opaque: the gate select below stays a bit blend, not a branch
     const bool sp = a.softplus != 0;
     float sdt = 0.0f;
     uint4 rs[2][LPT];                  // loader pieces of chunks in flight (chunk c in rs[c & 1])
@@ -270,14 +283,17 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
 
     // ---------------- helper stages (TB: LDS double-buffer index of the chunk) -------------
     // global -> registers: pieces of chunk CJ (zero past the end)
+    // (a wave whose lanes all lie past the last piece of round i skips that round's load)
 #define SSM_LOAD_CHUNK(R, CJ)                                                                       \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
     const int st0 = (CJ) * kT + lstep[i];                                                           \
-    R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
-                                  : make_uint4(0, 0, 0, 0);                                         \
+    R[i] = make_uint4(0, 0, 0, 0);                                                                  \
+    if (i * kHT + hw * kW < PIECES && lsrc[i] && st0 < len)                                         \
+      R[i] = *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT);                                  \
   }
 #define SSM_LOAD_CHUNK_FULL(R, CJ)                                                                  \
-  _Pragma("unroll") for (int i = 0; i < LPT; ++i) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i)                                                   \
+    if (i * kHT + hw * kW < PIECES) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
     // registers -> LDS: the u/delta/z tile of chunk CJ, and its B/C rows as fp32
 #define SSM_STORE_TILE(CJ, TB, R)                                                                    \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                  \
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
   if (OUT) {                                                                                      \
     unsigned char* ry = &sm.ytile[OUT ? (TB) : 0][lane * ROWB];                                   \
     const unsigned char* ru = &sm.tile[(J) & 3][0][lane * ROWB];                                  \
-    const unsigned char* rz = &sm.tile[(J) & 3][2][lane * ROWB];                                  \
+    const unsigned char* rz = &sm.tile[(J) & 3][OUT ? 2 : 0][lane * ROWB];                         \
     float pp[kTPH][kS], uv[kTPH], zv[kTPH];                                                       \
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
       _Pragma("unroll") for (int w = 0; w < kS; ++w) pp[i][w] = sm.part[OUT ? (TB) : 0][w][hw * kTPH + i][lane]; \
@@ -333,7 +349,9 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
     }                                                                                             \
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
       const float acc = (pp[i][0] + pp[i][1]) + (pp[i][2] + pp[i][3]);                            \
-      const float g = gated ? silu(zv[i]) : 1.0f;  /* select, not a branch */                     \
+      const float g = SSM_GATE_BLEND                                                              \
+          ? __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, silu(zv[i])) & gmask) | (0x3f800000u & ~gmask)) \
+          : (gated ? silu(zv[i]) : 1.0f);                                                         \
       lds_store_elem<TI>(ry, hw * kTPH + i, (acc + Dd * uv[i]) * g);                              \
     }                                                                                             \
   }
@@ -436,10 +454,14 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
     SSM_STORE_TILE((J) + 1, 1 - (PP), rs[1 - (PP)])                                               \
     __syncthreads();                                                                              \
   }
-      // prologue: chunk 0 into LDS, chunk 1 into registers
+      if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(SSM_HELPER_PRIO);
+      // prologue: chunk 0 into LDS, chunk 1 into registers; MODE 0: the next unit's ticket
       SSM_LOAD_CHUNK(rs[0], 0)
       SSM_LOAD_CHUNK(rs[1], 1)
+      int next_unit = 0;
+      if (MODE == 0 && htid == 0) next_unit = atomicAdd(a.ticket, 1);
       SSM_STORE_TILE(0, 0, rs[0])
+      if (MODE == 0 && htid == 0) sm.unit[(iter + 1) & 1] = next_unit;  // read after this unit's barriers
       __syncthreads();
       SSM_HELPER_ITER(0, 0)
       if (1 < last_j) SSM_HELPER_ITER(1, 1)
@@ -453,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
         SSM_HELPER_ITER(j, 1)
         if (j + 1 < last_j) SSM_HELPER_ITER(j + 1, 0)
       }
+      if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(0);
 #undef SSM_HELPER_ITER
 #undef SSM_HELPER_STEADY
     }
@@ -488,22 +511,22 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
           for (int j2 = 0; j2 < NPW; ++j2) a.last_state[ch * N + wv * NPW + j2] = h[j2];
         }
       } else if (MODE == 0) {
-        // Publish the end state: device-scope stores, then wait until every one of
-        // them is acknowledged (s_waitcnt 0: all counters drained) before the
-        // barrier, so the flag -- stored after the barrier -- can only become
-        // visible after the state.  The signal fences keep the compiler from
-        // moving the stores across the wait.
+        // Publish the end state, per scanner wave: device-scope stores of its rows, then wait
+        // until every one of them is acknowledged (s_waitcnt 0) before storing the wave's flag,
+        // so the flag can only become visible after the state.  The signal fences keep the
+        // compiler from moving the stores across the wait.  No workgroup barrier: the helpers
+        // go on to the next unit meanwhile.
         if (scanner) {
           float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
           for (int j2 = 0; j2 < NPW; ++j2)
             __hip_atomic_store(cp + (wv * NPW + j2) * kW + lane, h[j2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_waitcnt(0);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (lane == 0)
+            __hip_atomic_store(a.flags + (int64_t)unit * kS + wv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(a.flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (MODE != 0) break;
@@ -603,12 +626,12 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   void* scratch = nullptr;
   if (chained && K > 1) {
     const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
-    const size_t bytes = carry_bytes + (size_t)(a.units + 64) * sizeof(int);
+    const size_t bytes = carry_bytes + ((size_t)a.units * kS + 64) * sizeof(int);
     if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
     a.carry = (float*)scratch;
     a.ticket = (int*)((char*)scratch + carry_bytes);
     a.flags = a.ticket + 64;
-    const int nints = a.units + 64;
+    const int nints = a.units * kS + 64;
     hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
     err = hipGetLastError();
     if (err == hipSuccess) {
