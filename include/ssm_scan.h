@@ -106,11 +106,15 @@ int selective_state_update(float* state, const void* u, const void* delta, const
 /*
  * Launch plan selective_scan_fwd would use for these sizes on a GPU with `num_cus`
  * compute units (host-only; no GPU needed).  Writes 5 int64 values to `out`:
- *   out[0] mode: 0 chained segments (persistent workgroups hand states on),
- *                1 one pass per channel group, 2 aggregate + carry + output passes,
- *                3 generic kernels (dstate < 4 or rows not a whole number of 16 bytes)
- *   out[1] channel groups of 64, out[2] segments per group, out[3] steps per segment,
- *   out[4] work units.
+ *   out[0] mode: 0 intervals (the channel groups' sequences laid end to end and cut into
+ *                one equal interval per workgroup; a sequence split between two
+ *                workgroups hands its state on), 1 one pass per channel group,
+ *                2 aggregate + carry + output passes, 3 generic kernels (dstate < 4 or
+ *                rows not a whole number of 16 bytes)
+ *   out[1] channel groups of 64;
+ *   out[2] segments per group (modes 1, 2) or intervals (mode 0);
+ *   out[3] steps per segment or per interval;
+ *   out[4] workgroups of the output pass.
  * Pointer alignment, checked per call, can also route a call to the generic kernels.
  */
 int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype, int num_cus,

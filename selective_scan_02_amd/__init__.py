@@ -62,7 +62,7 @@ def load():
     return _lib
 
 
-PLAN_MODES = {0: "chained", 1: "single", 2: "two-pass", 3: "generic"}
+PLAN_MODES = {0: "intervals", 1: "single", 2: "two-pass", 3: "generic"}
 
 
 def scan_plan(batch: int, dim: int, dstate: int, seqlen: int, dtype=torch.bfloat16, num_cus: int = 256) -> dict:

@@ -29,15 +29,22 @@
 //
 // Sequence parallelism (chunked two-level scan: "Mamba close reading"
 // (jsqmd.com) §2.2 and the sketch of §7; mlqm.cn tutorial §6).  The sequence is
-// cut into K segments; work unit (k, group) scans segment k of a channel group.
-//  MODE 0 (chained): persistent workgroups take units in order from an atomic
-//    ticket; unit (k, grp) starts from the end state of unit (k-1, grp), handed
-//    over through global memory with a flag.  Units are ordered k-major, so a
-//    unit's predecessor was taken at least `groups` tickets earlier and has
-//    normally finished: no recomputation, exact sequential carry.  Used when
-//    there are enough channel groups to occupy the GPU.  The hand-over uses
-//    device-scope atomic loads and stores only (no agent-scope fences: on this
-//    multi-XCD part those write back or invalidate whole L2 caches).
+// cut into segments that run in parallel, with exact carries between them.
+//  MODE 0 (intervals), when there are at least as many channel groups as CUs:
+//    the chains of the G channel groups (tch chunks each) are laid end to end and
+//    cut into one interval of W = ceil(G * tch / CUs) chunks per workgroup.
+//    W >= tch, so an interval holds whole chains plus at most a tail piece of its
+//    first chain and a head piece of its last: a chain is split at most once.  A
+//    workgroup takes its interval from an atomic ticket and runs the head piece
+//    first, then the whole chains, then the tail piece, which starts from the
+//    state the previous interval's workgroup hands over at the split point,
+//    through global memory, with one flag per scanner wave.  That head was the
+//    first piece its workgroup ran, finished at least W - tch chunk-times
+//    before the tail starts, so the wait is normally over: no recomputation,
+//    exact sequential carry, and a workgroup pays the pipeline's fill and drain
+//    once per piece (two or three pieces).  The hand-over uses device-scope
+//    atomic loads and stores only (no agent-scope fences: on this multi-XCD
+//    part those write back or invalidate whole L2 caches).
 //  MODE 1 (output) with K = 1: one segment per group, no carry at all.
 //  MODE 2 (aggregate) + carry kernel + MODE 1 (output): for few channel groups
 //    (very long sequences).  Every segment but the last first computes its end
@@ -45,10 +52,11 @@
 //    exp(A * sum Delta)); a carry kernel turns these into incoming states; the
 //    output pass reruns each segment from its incoming state.
 //
-// Deadlock freedom of MODE 0: a unit waits only on a unit with a smaller
-// ticket, which was taken by a workgroup that is already running; the oldest
-// unfinished unit never waits.  The wait is additionally bounded (it gives up
-// after ~2^26 polls), so every wave always reaches the exit.
+// Deadlock freedom of MODE 0: a tail piece waits only for the head piece of the
+// interval with the previous ticket.  That workgroup took its ticket earlier, so
+// it is running or done, and it runs its head first, which waits for nothing.
+// The wait is additionally bounded (it gives up after ~2^26 polls), so every
+// wave always reaches the exit.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,6 +72,9 @@ namespace chunked {
 #endif
 #ifndef SSM_HELPER_PRIO
 #define SSM_HELPER_PRIO 1
+#endif
+#ifndef SSM_PREFETCH
+#define SSM_PREFETCH 3  // chunks of loads in flight per helper thread (1..3)
 #endif
 #ifndef SSM_GATE_BLEND
 #define SSM_GATE_BLEND 1
@@ -91,14 +102,16 @@ struct Args {
   float* last_state;
   float* seg_h;   // MODE 1/2: [K, batch*dim, N]
   float* seg_dt;  // MODE 2:   [K, batch*dim]
-  float* carry;   // MODE 0:   [groups, N, 64]
-  int* flags;     // MODE 0:   [units, kS] one per scanner wave
+  float* carry;   // MODE 0:   [groups, N, 64] state at a chain's split point
+  int* flags;     // MODE 0:   [groups, kS] one per chain and scanner wave
   int* ticket;    // MODE 0:   1 counter
   int64_t batch, dim, L, seg_len;
+  int64_t tch;    // MODE 0: chunks per chain (ceil(L / kT))
+  int64_t wlen;   // MODE 0: chunks per interval
   int gpr;     // channel groups per batch row
   int groups;  // batch * gpr
   int nseg;    // K
-  int units;   // K * groups
+  int units;   // MODE 1/2: K * groups; MODE 0: intervals (workgroups)
   int softplus;
 };
 
@@ -121,6 +134,25 @@ __device__ __forceinline__ void lds_store_elem(unsigned char* row, int e, float 
   }
 }
 
+// Source of loader piece p of a chunk-0 view of unit (b, d0, t_begin): u, delta, z rows of the
+// group's channels (XT tensors), then the batch row's B (and C) rows; NULL when the piece is
+// unused or the channel lies past dim.
+template <typename TI, int N, int XT, int PPR, int EPP>
+__device__ __forceinline__ const TI* piece_src(const Args& a, int p, int b, int d0, int64_t t_begin) {
+  constexpr int XPIECES = XT * kW * PPR;
+  constexpr int PIECES = XPIECES + (XT == 3 ? 2 : 1) * N * PPR;
+  const int q = p % PPR;
+  if (p < XPIECES) {
+    const int tensor = p / (kW * PPR), row = (p / PPR) % kW;
+    const TI* base = tensor == 0 ? (const TI*)a.u : tensor == 1 ? (const TI*)a.delta : (const TI*)a.z;
+    if (base && d0 + row < a.dim) return base + ((int64_t)b * a.dim + d0 + row) * a.L + t_begin + q * EPP;
+  } else if (p < PIECES) {
+    const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;
+    return (tensor == 0 ? (const TI*)a.B : (const TI*)a.C) + ((int64_t)b * N + n) * a.L + t_begin + q * EPP;
+  }
+  return nullptr;
+}
+
 // LDS of one workgroup.
 template <int N, typename TI, bool OUT>
 struct Smem {
@@ -132,9 +164,9 @@ struct Smem {
   float2 dtdu[2][kT][kW];                            // (Delta, Delta*u), [t][channel]
   float part[OUT ? 2 : 1][OUT ? kS : 1][kT][kW];     // partial readouts of the scanners
   unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
-  float bc[4][2][N][kT];                             // B, C of a chunk in fp32 (ring, as tile)
+  alignas(16) float bc[4][2][N][kT];                 // B, C of a chunk in fp32 (ring, as tile)
   float red[kH][kW];
-  int unit[2];  // MODE 0: this unit's ticket and the next one (by iteration parity)
+  int unit;     // MODE 0: this workgroup's interval
 };
 
 // The DPP broadcast operands of the scanners are read from LDS (bc above), so a
@@ -178,27 +210,74 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
   const int hw = wv - kS;                    // helper index (helpers only)
   const int htid = tid - kS * kW;            // helper thread index (helpers only)
 
+  uint4 rs[4][LPT];       // helpers: loader pieces of chunks in flight (chunk c in rs[c % 4])
+
+  // Set this scanner wave's hand-over flag of chain U: every store of its state must be
+  // acknowledged first (s_waitcnt 0), so the flag can only become visible after the state.  The
+  // signal fences keep the compiler from moving memory operations across the wait.
+#define SSM_PUBLISH(U)                                                                            \
+  {                                                                                               \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                      \
+    __builtin_amdgcn_s_waitcnt(0);                                                                \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                      \
+    if (lane == 0)                                                                                \
+      __hip_atomic_store(a.flags + (int64_t)(U) * kS + wv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+  }
+
+  // MODE 0: this workgroup's interval [is, ie) of the chains laid end to end (chunk units),
+  // taken from a ticket, and how it splits into pieces (see the launch notes above).
+  int64_t is = 0, ie = 0, cf = 0, cl = 0;
+  bool itail = false, ihead = false;
+  int npieces = 1;
+  if (MODE == 0) {
+    if (tid == 0) sm.unit = atomicAdd(a.ticket, 1);
+    __syncthreads();
+    const int ival = __builtin_amdgcn_readfirstlane(sm.unit);
+    if (ival >= a.units) return;  // uniform: the whole workgroup leaves
+    is = (int64_t)ival * a.wlen;
+    ie = is + a.wlen < (int64_t)a.groups * a.tch ? is + a.wlen : (int64_t)a.groups * a.tch;
+    cf = is / a.tch;
+    cl = (ie - 1) / a.tch;
+    itail = is > cf * a.tch;        // the first chain starts before the interval: wait for its head
+    ihead = ie < (cl + 1) * a.tch;  // the last chain goes on after it: hand its state over
+    npieces = (int)(cl - cf + 1);
+  }
+
   for (int iter = 0;; ++iter) {
-    int unit;
+    int grp, k = 0;
+    int64_t t_begin;
+    int len;
+    bool wait_in = false, hand_out = false;  // MODE 0: state from / to another workgroup
+    const int64_t L = a.L;
     if (MODE == 0) {
-      // The first ticket is taken here; every later one is taken by a helper thread during the
-      // previous unit (one unit ahead), so a unit starts without an atomic round trip.
-      if (iter == 0) {
-        if (tid == 0) sm.unit[0] = atomicAdd(a.ticket, 1);
-        __syncthreads();
+      if (iter >= npieces) break;
+      // order: the head of the last chain first (it never waits, and the next interval's
+      // workgroup waits for it), then the whole chains, then the tail of the first chain
+      int64_t cid;
+      if (ihead && iter == 0) cid = cl;
+      else {
+        const int q = iter - (ihead ? 1 : 0);
+        const int nfullc = npieces - (ihead ? 1 : 0) - (itail ? 1 : 0);
+        cid = q < nfullc ? cf + (itail ? 1 : 0) + q : cf;
       }
-      unit = __builtin_amdgcn_readfirstlane(sm.unit[iter & 1]);
+      const int64_t c0 = cid * a.tch > is ? cid * a.tch : is;
+      const int64_t c1 = (cid + 1) * a.tch < ie ? (cid + 1) * a.tch : ie;
+      grp = (int)cid;
+      t_begin = (c0 - cid * a.tch) * kT;
+      const int64_t t_end = (c1 - cid * a.tch) * kT < L ? (c1 - cid * a.tch) * kT : L;
+      len = (int)(t_end - t_begin);
+      wait_in = c0 > cid * a.tch;
+      hand_out = c1 < (cid + 1) * a.tch;
     } else {
-      unit = iter == 0 ? (int)blockIdx.x : a.units;
+      const int unit = iter == 0 ? (int)blockIdx.x : a.units;
+      if (unit >= a.units) break;
+      k = unit / a.groups;
+      grp = unit - k * a.groups;
+      t_begin = (int64_t)k * a.seg_len;
+      len = (int)((t_begin + a.seg_len < L ? a.seg_len : L - t_begin));  // steps in this unit
     }
-    if (unit >= a.units) break;
-    const int k = unit / a.groups;
-    const int grp = unit - k * a.groups;
     const int b = grp / a.gpr;
     const int d0 = (grp - b * a.gpr) * kW;
-    const int64_t L = a.L;
-    const int64_t t_begin = (int64_t)k * a.seg_len;
-    const int len = (int)((t_begin + a.seg_len < L ? a.seg_len : L - t_begin));  // steps in this unit
     const int nch = (len + kT - 1) / kT;
     const int nfull = len / kT;
 
@@ -214,12 +293,12 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
 #pragma unroll
       for (int j = 0; j < NPW; ++j) A2[j] = a.A[(int64_t)cc * N + wv * NPW + j] * kLog2e;
     }
-    // incoming state.  MODE 0: each scanner wave waits for the flag of the matching scanner
-    // wave of the predecessor unit and loads its own rows of the hand-over state; the helpers
-    // meanwhile start loading the unit's first chunks.
-    if (MODE == 0 && k > 0) {
+    // incoming state.  MODE 0 tail piece: each scanner wave waits for the flag of the matching
+    // scanner wave of the chain's head piece and loads its own rows of the hand-over state; the
+    // helpers meanwhile start loading the piece's first chunks.
+    if (MODE == 0 && wait_in) {
       if (scanner) {
-        const int* f = a.flags + (int64_t)(unit - a.groups) * kS + wv;
+        const int* f = a.flags + (int64_t)grp * kS + wv;
         for (int spin = 0;
              __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
              ++spin) {
@@ -238,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
       if (MODE == 1 && a.seg_h) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + wv * NPW + j];
-      } else if (MODE != 2 && k == 0 && a.h0) {
+      } else if (MODE != 2 && t_begin == 0 && a.h0) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) h[j] = a.h0[ch * N + wv * NPW + j];
       } else {
@@ -255,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
     asm volatile("" : "+v"(gmask));  // opaque: the gate select below stays a bit blend, not a branch
     const bool sp = a.softplus != 0;
     float sdt = 0.0f;
-    uint4 rs[2][LPT];                  // loader pieces of chunks in flight (chunk c in rs[c & 1])
     const TI* lsrc[LPT];               // NULL: piece unused or past a tensor's rows
     const TI* lsrc_f[LPT];             // unconditional-load version (a harmless valid address)
     int lstep[LPT];                    // first step of the piece within a chunk
@@ -263,15 +341,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
     for (int i = 0; i < LPT; ++i) {
       const int p = htid + i * kHT;
       const int q = p % PPR;
-      const TI* src = nullptr;
-      if (p < XPIECES) {
-        const int tensor = p / (kW * PPR), row = (p / PPR) % kW;
-        const TI* base = tensor == 0 ? (const TI*)a.u : tensor == 1 ? (const TI*)a.delta : (const TI*)a.z;
-        if (base && d0 + row < a.dim) src = base + ((int64_t)b * a.dim + d0 + row) * L + t_begin + q * EPP;
-      } else if (p < PIECES) {
-        const int pp = p - XPIECES, tensor = pp / (N * PPR), n = (pp / PPR) % N;
-        src = (tensor == 0 ? (const TI*)a.B : (const TI*)a.C) + ((int64_t)b * N + n) * L + t_begin + q * EPP;
-      }
+      const TI* src = piece_src<TI, N, XT, PPR, EPP>(a, p, b, d0, t_begin);
       lsrc[i] = src;
       lstep[i] = q * EPP;
       lsrc_f[i] = src ? src : (const TI*)a.u + t_begin + q * EPP;
@@ -283,17 +353,17 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
 
     // ---------------- helper stages (TB: LDS double-buffer index of the chunk) -------------
     // global -> registers: pieces of chunk CJ (zero past the end)
-    // (a wave whose lanes all lie past the last piece of round i skips that round's load)
+    // The steady-state version loads unconditionally (lanes without a piece read a valid
+    // address of u): a load issued on only some paths would make the compiler wait for every
+    // load in flight before the next use, which would undo the prefetch.
 #define SSM_LOAD_CHUNK(R, CJ)                                                                       \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                 \
     const int st0 = (CJ) * kT + lstep[i];                                                           \
-    R[i] = make_uint4(0, 0, 0, 0);                                                                  \
-    if (i * kHT + hw * kW < PIECES && lsrc[i] && st0 < len)                                         \
-      R[i] = *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT);                                  \
+    R[i] = (lsrc[i] && st0 < len) ? *reinterpret_cast<const uint4*>(lsrc[i] + (CJ) * kT)           \
+                                  : make_uint4(0, 0, 0, 0);                                         \
   }
 #define SSM_LOAD_CHUNK_FULL(R, CJ)                                                                  \
-  _Pragma("unroll") for (int i = 0; i < LPT; ++i)                                                   \
-    if (i * kHT + hw * kW < PIECES) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
+  _Pragma("unroll") for (int i = 0; i < LPT; ++i) R[i] = *reinterpret_cast<const uint4*>(lsrc_f[i] + (CJ) * kT);
     // registers -> LDS: the u/delta/z tile of chunk CJ, and its B/C rows as fp32
 #define SSM_STORE_TILE(CJ, TB, R)                                                                    \
   _Pragma("unroll") for (int i = 0; i < LPT; ++i) {                                                  \
@@ -436,44 +506,51 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
         __syncthreads();
       }
     } else {
-#define SSM_HELPER_ITER(J, PP)                                                                    \
+    // Loads run SSM_PREFETCH iterations ahead: iteration J stages chunk J+1 (from register
+    // slot (J+1) % 4) into LDS and issues the loads of chunk J+1+SSM_PREFETCH into another
+    // slot, so up to SSM_PREFETCH chunks are in flight.  Iterations are unrolled by 4 so every
+    // slot and LDS buffer index is a compile-time constant (S4 = J % 4).
+#define SSM_HELPER_ITER(J, S4)                                                                    \
   {                                                                                               \
-    SSM_LOAD_CHUNK(rs[PP], (J) + 2)                                                               \
-    if ((J) >= 3) SSM_STORE_Y((J) - 3, ((J) - 3) & 1, true)                                       \
-    if ((J) < nch) SSM_PREP(J, (J) & 1, true)                                                     \
-    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE((J) - 2, ((J) - 2) & 1)                         \
-    if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, ((J) + 1) & 1, rs[1 - (PP)])                       \
+    if ((J) >= 3) SSM_STORE_Y((J) - 3, ((S4) + 1) & 1, true)                                      \
+    if ((J) < nch) SSM_PREP(J, (S4) & 1, true)                                                    \
+    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE((J) - 2, (S4) & 1)                              \
+    if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, 0, rs[((S4) + 1) % 4])                              \
+    if ((J) + 1 + SSM_PREFETCH < nch) SSM_LOAD_CHUNK(rs[((S4) + 1 + SSM_PREFETCH) % 4], (J) + 1 + SSM_PREFETCH) \
     __syncthreads();                                                                              \
   }
-#define SSM_HELPER_STEADY(J, PP)                                                                  \
+#define SSM_HELPER_STEADY(J, S4)                                                                  \
   {                                                                                               \
-    SSM_LOAD_CHUNK_FULL(rs[PP], (J) + 2)                                                          \
-    SSM_STORE_Y((J) - 3, 1 - (PP), false)                                                         \
-    SSM_PREP(J, PP, false)                                                                        \
-    SSM_FINALIZE((J) - 2, PP)                                                                     \
-    SSM_STORE_TILE((J) + 1, 1 - (PP), rs[1 - (PP)])                                               \
+    SSM_STORE_Y((J) - 3, ((S4) + 1) & 1, false)                                                   \
+    SSM_PREP(J, (S4) & 1, false)                                                                  \
+    SSM_FINALIZE((J) - 2, (S4) & 1)                                                               \
+    SSM_STORE_TILE((J) + 1, 0, rs[((S4) + 1) % 4])                                                \
+    SSM_LOAD_CHUNK_FULL(rs[((S4) + 1 + SSM_PREFETCH) % 4], (J) + 1 + SSM_PREFETCH)                \
     __syncthreads();                                                                              \
   }
       if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(SSM_HELPER_PRIO);
-      // prologue: chunk 0 into LDS, chunk 1 into registers; MODE 0: the next unit's ticket
+      // prologue: chunk 0 into LDS, chunks 1..SSM_PREFETCH in flight
       SSM_LOAD_CHUNK(rs[0], 0)
-      SSM_LOAD_CHUNK(rs[1], 1)
-      int next_unit = 0;
-      if (MODE == 0 && htid == 0) next_unit = atomicAdd(a.ticket, 1);
+      _Pragma("unroll") for (int c = 1; c <= SSM_PREFETCH; ++c) {
+        if (c < nch) SSM_LOAD_CHUNK(rs[c], c)
+      }
       SSM_STORE_TILE(0, 0, rs[0])
-      if (MODE == 0 && htid == 0) sm.unit[(iter + 1) & 1] = next_unit;  // read after this unit's barriers
       __syncthreads();
       SSM_HELPER_ITER(0, 0)
       if (1 < last_j) SSM_HELPER_ITER(1, 1)
-      if (2 < last_j) SSM_HELPER_ITER(2, 0)
+      if (2 < last_j) SSM_HELPER_ITER(2, 2)
       int j = 3;
-      for (; j + 3 < nfull; j += 2) {
-        SSM_HELPER_STEADY(j, 1)
+      for (; j + 4 + SSM_PREFETCH < nfull; j += 4) {  // every chunk loaded here is full
+        SSM_HELPER_STEADY(j, 3)
         SSM_HELPER_STEADY(j + 1, 0)
+        SSM_HELPER_STEADY(j + 2, 1)
+        SSM_HELPER_STEADY(j + 3, 2)
       }
-      for (; j < last_j; j += 2) {
-        SSM_HELPER_ITER(j, 1)
+      for (; j < last_j; j += 4) {
+        SSM_HELPER_ITER(j, 3)
         if (j + 1 < last_j) SSM_HELPER_ITER(j + 1, 0)
+        if (j + 2 < last_j) SSM_HELPER_ITER(j + 2, 1)
+        if (j + 3 < last_j) SSM_HELPER_ITER(j + 3, 2)
       }
       if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(0);
 #undef SSM_HELPER_ITER
@@ -504,33 +581,27 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
         for (int w = 1; w < kH; ++w) s2 += sm.red[w][lane];
         a.seg_dt[(int64_t)k * a.batch * a.dim + ch] = s2;
       }
-    } else {
-      if (k == a.nseg - 1) {
-        if (scanner && a.last_state && active) {
+    } else if (MODE == 0 && hand_out) {
+      // A head piece: store the state at the split point (device-scope atomics, coherent
+      // across the XCDs' L2 caches without cache-wide write-back or invalidation), then set
+      // the flags once the stores are acknowledged.
+      if (scanner) {
+        float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
-          for (int j2 = 0; j2 < NPW; ++j2) a.last_state[ch * N + wv * NPW + j2] = h[j2];
-        }
-      } else if (MODE == 0) {
-        // Publish the end state, per scanner wave: device-scope stores of its rows, then wait
-        // until every one of them is acknowledged (s_waitcnt 0) before storing the wave's flag,
-        // so the flag can only become visible after the state.  The signal fences keep the
-        // compiler from moving the stores across the wait.  No workgroup barrier: the helpers
-        // go on to the next unit meanwhile.
-        if (scanner) {
-          float* cp = a.carry + (int64_t)grp * N * kW;
+        for (int j2 = 0; j2 < NPW; ++j2)
+          __hip_atomic_store(cp + (wv * NPW + j2) * kW + lane, h[j2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        SSM_PUBLISH(grp)
+      }
+    } else if (MODE == 0 || k == a.nseg - 1) {
+      // the piece ends the chain: final state
+      if (scanner && a.last_state && active) {
 #pragma unroll
-          for (int j2 = 0; j2 < NPW; ++j2)
-            __hip_atomic_store(cp + (wv * NPW + j2) * kW + lane, h[j2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          __builtin_amdgcn_s_waitcnt(0);
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          if (lane == 0)
-            __hip_atomic_store(a.flags + (int64_t)unit * kS + wv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int j2 = 0; j2 < NPW; ++j2) a.last_state[ch * N + wv * NPW + j2] = h[j2];
       }
     }
     if (MODE != 0) break;
   }
+#undef SSM_PUBLISH
 }
 
 __global__ void zero_ints(int* p, int n) {
@@ -572,34 +643,35 @@ int cu_count() {
 }  // namespace chunked
 
 // Launch shape of the chunked scan for a given problem and CU count.
-//  * groups >= CUs: chained segments (mode 0).  A segment costs its chunks plus ~kUnitOverhead
-//    chunk-times of pipeline fill/drain and hand-over; the run takes ceil(units / CUs)
-//    rounds of one segment each.  K minimises that.
-//  * CUs/2 <= groups < CUs: one segment per group (mode 1) -- splitting a chain cannot
-//    shorten it when every chain already has a CU of its own.
+//  * groups >= CUs: intervals (mode 0): one workgroup per interval of the chains laid end to
+//    end, W = ceil(groups * chunks / CUs) chunks each (every workgroup gets the same work;
+//    a chain is split at most once).
+//  * CUs/2 <= groups < CUs: one pass per group (mode 1) -- splitting a chain cannot shorten
+//    it when every chain already has a CU of its own.
 //  * fewer groups (long sequences): aggregate / carry / output passes (mode 2) over enough
 //    parallel segments to fill the GPU (SSM_SPLIT_UNITS_PER_CU per CU).
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus) {
   using namespace chunked;
-  constexpr int64_t kUnitOverhead = 4;
   ScanPlan pl{};
   pl.groups = batch * ((dim + kW - 1) / kW);
   const int64_t nch_total = std::max<int64_t>(1, (seqlen + kT - 1) / kT);
-  int64_t K = 1;
   if (pl.groups >= cus) {
-    int64_t best = -1;
-    for (int64_t k = 1; k <= std::min<int64_t>(nch_total, 32); ++k) {
-      const int64_t rounds = (k * pl.groups + cus - 1) / cus;
-      const int64_t cost = rounds * ((nch_total + k - 1) / k + kUnitOverhead);
-      if (best < 0 || cost < best) { best = cost; K = k; }
-    }
-  } else if (2 * pl.groups < cus) {
+    const int64_t total = pl.groups * nch_total;
+    const int64_t w = (total + cus - 1) / cus;
+    pl.mode = 0;
+    pl.units = (total + w - 1) / w;
+    pl.nseg = pl.units;
+    pl.seg_len = w * kT;
+    return pl;
+  }
+  int64_t K = 1;
+  if (2 * pl.groups < cus) {
     const int64_t target_units = (int64_t)SSM_SPLIT_UNITS_PER_CU * cus;
     K = std::max<int64_t>(1, std::min<int64_t>(nch_total, (target_units + pl.groups - 1) / pl.groups));
   }
   pl.seg_len = ((nch_total + K - 1) / K) * kT;
   pl.nseg = std::max<int64_t>(1, (seqlen + pl.seg_len - 1) / pl.seg_len);
-  pl.mode = pl.nseg == 1 ? 1 : (pl.groups >= cus ? 0 : 2);
+  pl.mode = pl.nseg == 1 ? 1 : 2;
   pl.units = pl.nseg * pl.groups;
   return pl;
 }
@@ -620,23 +692,23 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.nseg = (int)pl.nseg;
   a.units = (int)pl.units;
   const int64_t K = pl.nseg;
-  const bool chained = pl.mode == 0;
   const int64_t chans = p.batch * p.dim;
   hipError_t err = hipSuccess;
   void* scratch = nullptr;
-  if (chained && K > 1) {
+  if (pl.mode == 0) {
+    a.tch = (p.seqlen + kT - 1) / kT;
+    a.wlen = pl.seg_len / kT;
     const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
-    const size_t bytes = carry_bytes + ((size_t)a.units * kS + 64) * sizeof(int);
+    const size_t bytes = carry_bytes + ((size_t)a.groups * kS + 64) * sizeof(int);
     if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
     a.carry = (float*)scratch;
     a.ticket = (int*)((char*)scratch + carry_bytes);
     a.flags = a.ticket + 64;
-    const int nints = a.units * kS + 64;
+    const int nints = a.groups * kS + 64;
     hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
     err = hipGetLastError();
     if (err == hipSuccess) {
-      const int grid = std::min(a.units, cus);
-      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0>), dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0>), dim3(a.units), dim3(kThreads), 0, stream, a);
       err = hipGetLastError();
     }
   } else if (K > 1) {

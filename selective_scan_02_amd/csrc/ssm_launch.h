@@ -41,11 +41,11 @@ struct StepParams {
 };
 
 struct ScanPlan {
-  int mode;          // 0 chained segments, 1 one pass, 2 aggregate/carry/output
+  int mode;          // 0 intervals, 1 one pass, 2 aggregate/carry/output
   int64_t groups;    // channel groups of 64
-  int64_t nseg;      // segments per group
-  int64_t seg_len;   // steps per segment
-  int64_t units;     // groups * nseg
+  int64_t nseg;      // segments per group (modes 1, 2); intervals (mode 0)
+  int64_t seg_len;   // steps per segment or per interval
+  int64_t units;     // workgroups of the output pass
 };
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
 

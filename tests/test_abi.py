@@ -141,9 +141,9 @@ def test_empty_sequence_allows_null_sequence_tensors(lib):
 
 
 def test_scan_plan_workloads(lib):
-    # 2.8B-shaped layer: 320 channel groups on 256 CUs -> 4 chained segments, 5 units per CU
+    # 2.8B-shaped layer: 320 channel groups of 128 chunks on 256 CUs -> 256 intervals of 160 chunks
     p = ssm.scan_plan(4, 5120, 16, 2048)
-    assert p == {"mode": "chained", "groups": 320, "segments": 4, "seg_len": 512, "units": 1280}
+    assert p == {"mode": "intervals", "groups": 320, "segments": 256, "seg_len": 2560, "units": 256}
     # 130M-shaped layer: 192 groups < 256 CUs -> one pass per group
     p = ssm.scan_plan(8, 1536, 16, 2048)
     assert p["mode"] == "single" and p["groups"] == 192 and p["segments"] == 1
@@ -159,11 +159,19 @@ def test_scan_plan_workloads(lib):
     assert ssm.scan_plan(1, 64, 16, 777)["mode"] == "generic"
 
 
-def test_scan_plan_chained_segments_balance(lib):
-    for b, d, L in [(4, 5120, 2048), (2, 10240, 1000), (1, 20480, 512), (8, 5120, 4096)]:
+def test_scan_plan_intervals_cover_and_balance(lib):
+    # intervals: every workgroup but the last gets the same number of chunks, the intervals
+    # cover all chains exactly, and an interval is at least one chain long (a chain is split
+    # at most once, and a tail piece starts no earlier than the head it continues ends)
+    for b, d, L in [(4, 5120, 2048), (2, 10240, 1000), (1, 20480, 512), (8, 5120, 4096), (4, 4096, 2048),
+                    (1, 64 * 257, 2048), (8, 5120, 512)]:
         p = ssm.scan_plan(b, d, 16, L)
-        assert p["mode"] in ("chained", "single")
-        assert p["segments"] * p["seg_len"] >= L and p["seg_len"] % 16 == 0
+        chunks = -(-L // 16)
+        total = p["groups"] * chunks
+        w = p["seg_len"] // 16
+        assert p["mode"] == "intervals" and p["seg_len"] % 16 == 0
+        assert p["units"] == -(-total // w) and (p["units"] - 1) * w < total <= p["units"] * w
+        assert w >= chunks and p["units"] <= 256
 
 
 def torch_dtype_f32():

@@ -96,12 +96,16 @@ SHAPES = [
 ]
 
 
-# Launch-shape coverage of the fast path: chained segments (many channel groups),
+# Launch-shape coverage of the fast path: intervals (many channel groups; sequences split
+# between workgroups, an interval exactly one sequence long, several sequences per interval),
 # the two-pass aggregate/carry/output split (few groups, long sequences), one segment.
 LAUNCH_CASES = [
-    ("chained", 2, 10240, 16, 1000, "bf16", 512),
-    ("chained-f32", 1, 20480, 16, 512, "f32", 512),
-    ("chained-n64", 2, 10240, 64, 296, "bf16", 256),
+    ("intervals", 2, 10240, 16, 1000, "bf16", 512),
+    ("intervals-f32", 1, 20480, 16, 512, "f32", 512),
+    ("intervals-n64", 2, 10240, 64, 296, "bf16", 256),
+    ("intervals-unsplit", 4, 4096, 16, 256, "bf16", 256),
+    ("intervals-small-slack", 1, 64 * 257, 16, 512, "bf16", 384),
+    ("intervals-multi", 8, 5120, 8, 160, "f32", 256),
     ("two-pass", 1, 256, 16, 100_000, "f32", 24),
     ("two-pass-bf16", 2, 64, 16, 65_536, "bf16", 24),
     ("single-segment", 1, 128, 16, 16, "bf16", None),
@@ -113,7 +117,7 @@ def test_launch_shapes(case):
     name, b, d, n, L, dt, k = case
     plan = ssm.scan_plan(b, d, n, L, torch.bfloat16 if dt == "bf16" else torch.float32)
     note(f"launch shape {name}: B={b} D={d} N={n} L={L} {dt} plan={plan}")
-    expected = {"chained": "chained", "two-pass": "two-pass", "single-segment": "single"}
+    expected = {"intervals": "intervals", "two-pass": "two-pass", "single-segment": "single"}
     assert plan["mode"] == next(v for k, v in expected.items() if name.startswith(k))
     x = gen.random_scan_inputs(b, d, n, L, dt, seed=len(name))
     check_scan(x, chans=None if k is None else sampled(x, k, 7))
