@@ -17,7 +17,7 @@
  *                           two execution forms and "推理框架需要管理完全不同的请求状态";
  *                           mlqm.cn tutorial §9.2, the single-step update).
  *
- * Per channel d, state n and step t (h_{-1} = 0 for the scan):
+ * Per channel d, state n and step t (h_{-1} = 0 for the scan unless resumed from a state):
  *   Delta_t   = softplus(delta_t + dt_bias[d])   (softplus flag off: delta_t + dt_bias[d])
  *   Abar_t[n] = exp(Delta_t * A[d,n])            ZOH transition (mlqm.cn §3.2;
  *                                                "Mamba close reading" (jsqmd.com) §1.2)
@@ -88,6 +88,25 @@ int selective_scan_fwd(const void* u, const void* delta, const float* A, const v
                        int dtype, void* stream);
 
 /*
+ * Forward selective scan resumed from a given state: h_{-1} = initial_state instead of 0.
+ * This is prefill in pieces -- the state a prefill writes is the state the next piece (or
+ * the decode steps) continues from ("AI inference series (14)", wiblog.cn: prefill runs
+ * the whole-sequence scan and writes the final state; the request state is then carried
+ * forward).  A scan of a+b steps equals a scan of the first a steps followed by this call
+ * on the next b steps from its last_state.
+ *
+ *   initial_state : [batch, dim, dstate] fp32, NULL = zeros (then identical to
+ *                   selective_scan_fwd).  It may be the very same buffer as last_state
+ *                   (the state is advanced in place); any other overlap with an output
+ *                   is SSM_ERR_ALIAS.  seqlen == 0 copies it to last_state.
+ * Every other argument, requirement and error is as for selective_scan_fwd.
+ */
+int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const void* z, const float* dt_bias, int softplus,
+                              const float* initial_state, void* y, float* last_state, int64_t batch,
+                              int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
+
+/*
  * One decode step for `batch` independent requests, state updated IN PLACE.
  *
  *   state       : [batch, dim, dstate] fp32, read as h_{t-1} and overwritten with h_t
@@ -123,10 +142,10 @@ int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, in
 /* Text describing the calling thread's most recent non-OK status ("" if none). */
 const char* ssm_last_error(void);
 
-/* ABI version of this header (incremented on incompatible changes). */
+/* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

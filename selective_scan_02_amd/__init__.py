@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["load", "lib_path", "scan_fwd", "state_update", "scan_plan", "SsmError", "STATUS", "selective_scan_fwd",
-           "selective_state_update", "last_error"]
+           "selective_scan_fwd_resume", "selective_state_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_PKG, "libssm_scan.so")
@@ -27,7 +27,8 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_state_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "ssm_scan_plan",
+           "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -50,6 +51,8 @@ def load():
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.selective_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
         lib.selective_scan_fwd.restype = I
+        lib.selective_scan_fwd_resume.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I, P]
+        lib.selective_scan_fwd_resume.restype = I
         lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.selective_state_update.restype = I
         lib.ssm_last_error.argtypes = []
@@ -118,14 +121,20 @@ def selective_scan_fwd(*args) -> int:
     return int(load().selective_scan_fwd(*args))
 
 
+def selective_scan_fwd_resume(*args) -> int:
+    return int(load().selective_scan_fwd_resume(*args))
+
+
 def selective_state_update(*args) -> int:
     return int(load().selective_state_update(*args))
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True,
-             return_last_state: bool = True, y=None, last_state=None):
+             return_last_state: bool = True, y=None, last_state=None, initial_state=None):
     """Forward selective scan.  u, delta, z: [batch, dim, L]; B, C: [batch, N, L]
-    (dtype of u); A: [dim, N] fp32; D, dt_bias: [dim] fp32.  Returns (y, last_state)."""
+    (dtype of u); A: [dim, N] fp32; D, dt_bias: [dim] fp32.  Returns (y, last_state).
+    ``initial_state`` [batch, dim, N] fp32 resumes the scan from that state (it may be
+    passed as ``last_state`` too, to advance it in place)."""
     lib = load()
     if u.dim() != 3 or A.dim() != 2:
         raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
@@ -148,9 +157,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     if last_state is not None:
         _require(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    rc = lib.selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                                1 if softplus else 0, _ptr(y), _ptr(last_state), batch, dim, N, L,
-                                _dtype_code(u), _stream(dev))
+    if initial_state is not None:
+        _require(initial_state, "initial_state", (batch, dim, N), torch.float32, dev)
+        rc = lib.selective_scan_fwd_resume(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                           _ptr(dt_bias), 1 if softplus else 0, _ptr(initial_state), _ptr(y),
+                                           _ptr(last_state), batch, dim, N, L, _dtype_code(u), _stream(dev))
+    else:
+        rc = lib.selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(dt_bias), 1 if softplus else 0, _ptr(y), _ptr(last_state), batch, dim, N,
+                                    L, _dtype_code(u), _stream(dev))
     _check(rc)
     return y, last_state
 

@@ -85,10 +85,14 @@ int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, in
   return SSM_OK;
 }
 
-int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                       const float* D, const void* z, const float* dt_bias, int softplus, void* y,
-                       float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+int scan_impl(const char* who, const void* u, const void* delta, const float* A, const void* B, const void* C,
+              const float* D, const void* z, const float* dt_bias, int softplus, const float* h0, void* y,
+              float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+              void* stream) {
   g_last_error.clear();
   // With seqlen == 0 the sequence tensors are empty and may be NULL.
   if (seqlen != 0) {
@@ -111,6 +115,7 @@ int selective_scan_fwd(const void* u, const void* delta, const float* A, const v
   if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
   const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nx = (uint64_t)batch * dim * seqlen, nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
   const Range ins[] = {{"u", u, nx * es, es},
                        {"delta", delta, nx * es, es},
                        {"z", z, nx * es, es},
@@ -118,23 +123,45 @@ int selective_scan_fwd(const void* u, const void* delta, const float* A, const v
                        {"C", C, nbc * es, es},
                        {"A", A, (uint64_t)dim * dstate * 4, 4},
                        {"D", D, (uint64_t)dim * 4, 4},
-                       {"dt_bias", dt_bias, (uint64_t)dim * 4, 4}};
-  const Range ry{"y", y, nx * es, es}, rl{"last_state", last_state, (uint64_t)batch * dim * dstate * 4, 4};
+                       {"dt_bias", dt_bias, (uint64_t)dim * 4, 4},
+                       {"initial_state", h0, nst, 4}};
+  const Range ry{"y", y, nx * es, es}, rl{"last_state", last_state, nst, 4};
   for (const Range& r : ins)
     if (int rc = check_aligned(r)) return rc;
   if (int rc = check_aligned(ry)) return rc;
   if (int rc = check_aligned(rl)) return rc;
   for (const Range& r : ins) {
     if (overlap(ry, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
-    if (overlap(rl, r)) return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
+    // the state may be advanced in place: last_state == initial_state exactly
+    if (overlap(rl, r) && !(r.p == h0 && last_state == h0)) return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
   }
   if (overlap(ry, rl)) return fail(SSM_ERR_ALIAS, "y overlaps last_state");
 
   ssm::ScanParams p{};
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
-  p.softplus = softplus; p.y = y; p.last_state = last_state; p.h0 = nullptr;
+  p.softplus = softplus; p.y = y; p.last_state = last_state; p.h0 = h0;
   p.batch = batch; p.dim = dim; p.dstate = dstate; p.seqlen = seqlen; p.dtype = dtype;
-  return hip_status(ssm::launch_scan_fwd(p, (hipStream_t)stream), "selective_scan_fwd launch");
+  return hip_status(ssm::launch_scan_fwd(p, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus, void* y,
+                       float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                       void* stream) {
+  return scan_impl("selective_scan_fwd launch", u, delta, A, B, C, D, z, dt_bias, softplus, nullptr, y, last_state,
+                   batch, dim, dstate, seqlen, dtype, stream);
+}
+
+int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const void* z, const float* dt_bias, int softplus,
+                              const float* initial_state, void* y, float* last_state, int64_t batch,
+                              int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream) {
+  return scan_impl("selective_scan_fwd_resume launch", u, delta, A, B, C, D, z, dt_bias, softplus, initial_state,
+                   y, last_state, batch, dim, dstate, seqlen, dtype, stream);
 }
 
 int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,

@@ -81,7 +81,10 @@ __global__ __launch_bounds__(kWave) void scan_segment_kernel(SegArgs a) {
   float A2[N], h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) A2[n] = a.A[dd * N + n] * kLog2e;
-  if (MODE == 0 && seg > 0) {
+  // With several segments every output segment, the first included, starts from the carry
+  // pass's incoming state (seg_h[0] = initial state): the initial state is then read only by
+  // the carry pass, so it may be the same buffer as last_state, which this pass writes.
+  if (MODE == 0 && a.seg_h) {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = a.seg_h[((int64_t)seg * a.batch * a.dim + ch) * N + n];
   } else if (MODE == 0 && a.h0) {
@@ -125,6 +128,13 @@ __global__ __launch_bounds__(kWave) void scan_segment_kernel(SegArgs a) {
 #pragma unroll
     for (int n = 0; n < N; ++n) a.last_state[ch * N + n] = h[n];
   }
+}
+
+// last_state for an empty sequence: the initial state (or zeros), by a kernel rather than a
+// memset or copy node, so the call stays safe to capture in a graph.
+__global__ __launch_bounds__(256) void empty_sequence_state(float* last, const float* h0, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) last[i] = h0 ? h0[i] : 0.0f;
 }
 
 // One thread per (channel, n): turn segment aggregates into incoming states, in place.
@@ -215,10 +225,11 @@ bool dstate_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 |
 
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream) {
   if (p.seqlen == 0) {
-    if (p.last_state) {
-      const size_t bytes = (size_t)p.batch * p.dim * p.dstate * sizeof(float);
-      if (p.h0) return hipMemcpyAsync(p.last_state, p.h0, bytes, hipMemcpyDeviceToDevice, stream);
-      return hipMemsetAsync(p.last_state, 0, bytes, stream);
+    if (p.last_state && p.last_state != p.h0) {
+      const int64_t n = p.batch * p.dim * p.dstate;
+      hipLaunchKernelGGL(empty_sequence_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.last_state,
+                         p.h0, n);
+      return hipGetLastError();
     }
     return hipSuccess;
   }

@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_state_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
+    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "ssm_scan_plan",
+                 "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
 
@@ -52,7 +53,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
 
 
 def scan_args(**over):
@@ -61,6 +62,11 @@ def scan_args(**over):
     a.update(over)
     return [a[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "dt_bias", "softplus", "y", "last", "batch", "dim",
                            "dstate", "seqlen", "dtype", "stream")]
+
+
+def resume_args(h0=addr(11), **over):
+    a = scan_args(**over)
+    return a[:9] + [h0] + a[9:]
 
 
 def step_args(**over):
@@ -118,6 +124,21 @@ def test_alias(lib):
     assert lib.selective_state_update(*step_args(state=addr(2))) == ALIAS
     assert lib.selective_state_update(*step_args(y=addr(1) + 16)) == ALIAS
     assert "overlaps" in ssm.last_error()
+
+
+def test_resume_validation(lib):
+    # the resumed scan validates like the plain one, plus the initial state
+    assert lib.selective_scan_fwd_resume(*resume_args(u=None)) == NULL_ARG
+    assert lib.selective_scan_fwd_resume(*resume_args(dtype=5)) == BAD_DTYPE
+    assert lib.selective_scan_fwd_resume(*resume_args(dstate=3)) == UNSUPPORTED
+    assert lib.selective_scan_fwd_resume(*resume_args(h0=addr(11) + 2)) == MISALIGNED
+    # y may not overlap the initial state; last_state may only be the very same buffer
+    assert lib.selective_scan_fwd_resume(*resume_args(h0=addr(9) + 64)) == ALIAS
+    assert "initial_state" in ssm.last_error()
+    assert lib.selective_scan_fwd_resume(*resume_args(h0=addr(10) + 64)) == ALIAS
+    assert lib.selective_scan_fwd_resume(*resume_args(h0=addr(10), last=addr(10) + 4)) == ALIAS
+    # last_state overlapping the initial state only in part
+    assert lib.selective_scan_fwd_resume(*resume_args(h0=addr(10), last=addr(10) - 4)) == ALIAS
 
 
 def test_error_text_is_per_call(lib):

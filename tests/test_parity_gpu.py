@@ -312,3 +312,80 @@ def test_prefill_then_decode_handoff():
     for i, t in enumerate(range(L, L + k)):
         assert oracle.rel_err(f64(ys[i]), yr[..., t]) <= TOL["bf16"]
     assert oracle.rel_err(f64(state), lr) <= 1e-4
+
+
+# ----------------------------- scan resumed from a state (prefill in pieces) ----
+RESUME_CASES = [
+    ("intervals", 2, 10240, 16, 1000, "bf16", 384),
+    ("single", 2, 4096, 16, 512, "bf16", 384),
+    ("two-pass", 1, 256, 16, 100_000, "f32", 16),
+    ("generic-n2", 2, 100, 2, 777, "f32", None),
+    ("generic-odd-length", 1, 130, 16, 301, "bf16", None),
+    ("tiny", 1, 16, 4, 64, "f32", None),
+]
+
+
+def random_state(b, d, n, seed):
+    g = np.random.default_rng(seed)
+    return torch.from_numpy(g.standard_normal((b, d, n), dtype=np.float32))
+
+
+@pytest.mark.parametrize("case", RESUME_CASES, ids=lambda c: c[0])
+def test_resume_from_state(case):
+    name, b, d, n, L, dt, k = case
+    note(f"resume {name}: B={b} D={d} N={n} L={L} {dt} plan={ssm.scan_plan(b, d, n, L, torch.bfloat16 if dt == 'bf16' else torch.float32)}")
+    x = gen.random_scan_inputs(b, d, n, L, dt, seed=3 + len(name))
+    h0 = random_state(b, d, n, seed=len(name))
+    chans = None if k is None else sampled(x, k, 11)
+    y, last = gpu_scan(x, initial_state=h0.cuda())
+    yr, lr = ref_scan(x, h0=h0 if chans is None else h0.reshape(-1, n)[chans], chans=chans)
+    if chans is not None:
+        idx = torch.as_tensor(chans, device=y.device)
+        y, last = y.reshape(-1, y.shape[-1])[idx], last.reshape(-1, n)[idx]
+    ey, el = oracle.rel_err(f64(y), yr), oracle.rel_err(f64(last), lr)
+    note(f"  y err {ey:.3e}  last_state err {el:.3e}")
+    assert ey <= TOL[dt] and el <= TOL[dt]
+
+
+@pytest.mark.parametrize("case", RESUME_CASES, ids=lambda c: c[0])
+def test_resume_in_place_matches_separate_buffers(case):
+    # initial_state and last_state the very same buffer: the state is advanced in place,
+    # with exactly the result of separate buffers
+    name, b, d, n, L, dt, _ = case
+    note(f"resume in place {name}")
+    x = gen.random_scan_inputs(b, d, n, L, dt, seed=5 + len(name))
+    h0 = random_state(b, d, n, seed=7 + len(name)).cuda()
+    y1, last1 = gpu_scan(x, initial_state=h0)
+    st = h0.clone()
+    y2, last2 = gpu_scan(x, initial_state=st, last_state=st)
+    assert last2.data_ptr() == st.data_ptr()
+    assert torch.equal(y1, y2) and torch.equal(last1, st)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_in_pieces_equals_whole_scan(dt):
+    # scan(first a steps) then resume(next b steps) from its final state == scan(a + b)
+    a_len, b_len = 1008, 536
+    x = gen.random_scan_inputs(2, 200, 16, a_len + b_len, dt, seed=21)
+    note(f"prefill in pieces {dt}: {a_len} + {b_len} steps")
+    g = dev(x)
+    part = lambda lo, hi: {k: g[k][..., lo:hi].contiguous() for k in ("u", "delta", "z", "B", "C")}
+    p1, p2 = part(0, a_len), part(a_len, a_len + b_len)
+    _, st = ssm.scan_fwd(p1["u"], p1["delta"], g["A"], p1["B"], p1["C"], g["D"], p1["z"], g["dt_bias"])
+    y2, st2 = ssm.scan_fwd(p2["u"], p2["delta"], g["A"], p2["B"], p2["C"], g["D"], p2["z"], g["dt_bias"],
+                           initial_state=st, last_state=st)
+    torch.cuda.synchronize()
+    yr, lr = ref_scan(x)
+    ey, el = oracle.rel_err(f64(y2), yr[..., a_len:]), oracle.rel_err(f64(st2), lr)
+    note(f"  y err {ey:.3e}  last_state err {el:.3e}")
+    assert ey <= TOL[dt] and el <= TOL[dt]
+
+
+def test_resume_empty_sequence_copies_state():
+    x = gen.random_scan_inputs(2, 70, 16, 0, "f32", seed=1)
+    h0 = random_state(2, 70, 16, seed=2).cuda()
+    _, last = gpu_scan(x, initial_state=h0)
+    assert torch.equal(last, h0)
+    st = h0.clone()
+    gpu_scan(x, initial_state=st, last_state=st)
+    assert torch.equal(st, h0)
