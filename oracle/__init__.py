@@ -48,6 +48,8 @@ def _load():
         lib.oracle_scan.restype = I
         lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P, I64, P, P, I]
         lib.oracle_step.restype = I
+        lib.oracle_conv1d.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I, P, P, I]
+        lib.oracle_conv1d.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -184,3 +186,26 @@ def rel_err(got, ref) -> float:
     rms = float(np.sqrt(np.mean(r * r)))
     floor = max(rms, np.finfo(np.float64).tiny)
     return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), floor)))
+
+
+def conv1d(x, weight, bias=None, silu=True, state=None, threads: int = 0):
+    """Causal depthwise conv (+ SiLU) in fp64.  x [B,D,L] (fp32 or bf16), weight [D,K],
+    bias [D] fp32, state [B,D,K-1] (inputs before step 0, oldest first; None = zeros).
+    Returns (out [B,D,L], state_out [B,D,K-1]) as float64 numpy arrays."""
+    keep = []
+    batch, dim, seqlen = (int(s) for s in x.shape)
+    width = int(weight.shape[1])
+    px, dtype = _raw(x, keep)
+    ps = None
+    if state is not None:
+        st = state.detach().cpu().double().numpy() if isinstance(state, torch.Tensor) else np.asarray(state, np.float64)
+        st = np.ascontiguousarray(st.reshape(batch * dim, width - 1), dtype=np.float64)
+        keep.append(st)
+        ps = st.ctypes.data
+    out = np.empty((batch * dim, seqlen), dtype=np.float64)
+    st_out = np.empty((batch * dim, max(width - 1, 1)), dtype=np.float64)
+    rc = _load().oracle_conv1d(px, _f32(weight, keep), _f32(bias, keep), ps, 1 if silu else 0, batch, dim, seqlen,
+                               width, dtype, out.ctypes.data, st_out.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d failed ({rc})")
+    return out.reshape(batch, dim, seqlen), st_out[:, :width - 1].reshape(batch, dim, width - 1)

@@ -158,3 +158,54 @@ int oracle_step(const double* state_in, const void* u, const void* delta, const 
   }
   return 0;
 }
+
+/*
+ * Causal depthwise 1-D convolution with an optional SiLU, the step just before the
+ * selective SSM in the Mamba block ("Mamba: Linear-Time Sequence Modeling ..."
+ * summary (junchaoiu.github.io), 方法 third step: linear expansion, 1-D convolution
+ * for local features, SiLU; mlqm.cn tutorial §7.1: causal 1-D convolution then SiLU
+ * ahead of the selective SSM).  Per channel (b, d) and step t, with width K:
+ *
+ *   v_t   = bias[d] + sum_{k=0..K-1} w[d,k] * x[t - (K-1) + k]
+ *   out_t = silu(v_t) if silu_on else v_t
+ *
+ * where x at steps before 0 comes from the caller's convolution state: the K-1
+ * inputs preceding this sequence, oldest first (state_in[row*(K-1) + j] is the input
+ * at step j - (K-1)); state_in NULL = zeros.  The decode path keeps exactly that
+ * window per request ("AI inference series (14)" (wiblog.cn): a decode step keeps
+ * only the updated state and the little history the local convolution needs).
+ * state_out (may be NULL) receives the K-1 inputs ending at step L-1 -- the state a
+ * following call continues from.  Layouts: x, out [B,D,L] (x of `dtype`); w [D,K],
+ * bias [D] fp32; states [B*D, K-1] double.  state_in and state_out may alias.
+ */
+int oracle_conv1d(const void* x, const float* w, const float* bias, const double* state_in, int silu_on,
+                  int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int dtype, double* out,
+                  double* state_out, int nthreads) {
+  if (batch < 0 || dim < 0 || seqlen < 0 || width < 1 || width > 64) return -2;
+  set_threads(nthreads);
+  const int64_t L = seqlen, K = width, rows = batch * dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t d = r % dim;
+    double hist[64]; /* inputs at steps -(K-1) .. -1 */
+    for (int64_t j = 0; j < K - 1; ++j) hist[j] = state_in ? state_in[r * (K - 1) + j] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      double v = bias ? (double)bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t s = t - (K - 1) + k; /* input step */
+        const double xs = s >= 0 ? elem(x, r * L + s, dtype) : hist[K - 1 + s];
+        v += (double)w[d * K + k] * xs;
+      }
+      out[r * L + t] = silu_on ? silu(v) : v;
+    }
+    if (state_out) {
+      double nw[64];
+      for (int64_t j = 0; j < K - 1; ++j) {
+        const int64_t s = L - (K - 1) + j;
+        nw[j] = s >= 0 ? elem(x, r * L + s, dtype) : hist[K - 1 + s];
+      }
+      for (int64_t j = 0; j < K - 1; ++j) state_out[r * (K - 1) + j] = nw[j];
+    }
+  }
+  return 0;
+}
