@@ -12,8 +12,9 @@ its scan kernel (ALU-bound: VALU issue slots per element, see algo_slots)
 with the HBM bandwidth alongside, and the CPU fp64 oracle timed on this host
 as baseline.  Also reported: the long-sequence scan (B=1, D=256, N=16,
 L=2^20, fp32) under "long", the same layer prefilled as four scans resumed
-from each other's state under "resume", and the decode step (B=256, D=5120,
-N=16, 128 steps) under "decode", flushed and back to back.
+from each other's state under "resume", the decode step (B=256, D=5120,
+N=16, 128 steps) under "decode", flushed and back to back, and the causal
+conv1d + SiLU ahead of the scan (sequence and decode step) under "conv1d".
 """
 from __future__ import annotations
 
@@ -73,6 +74,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the long-sequence (L=2^20) scan figure")
     p.add_argument("--no-resume", action="store_true", help="skip the prefill-in-pieces figure")
+    p.add_argument("--no-conv", action="store_true", help="skip the causal conv1d figures")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the scan, run 5 plain device copies of MIB MiB each (reference dispatches for "
@@ -182,6 +184,8 @@ def main():
         out["resume"] = bench_resume(torch, gen, ssm, w, x, max(5, args.steps // 5))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, gen, ssm, args)
+    if not args.no_conv:
+        out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(torch, args.copy_calibration)
     if not args.no_cpu_baseline:
@@ -221,6 +225,56 @@ def bench_resume(torch, gen, ssm, w, x, steps, pieces=4):
             "ms_per_step": ms, "value": el / (ms * 1e-3), "unit": "elements/s",
             "alu_frac": el * algo_slots(N) / (ms * 1e-3) / 1e12 / PEAK_VALU_TOPS,
             "note": "inputs resident (no rotation): the pieces' 337 MB exceed the last-level cache"}
+
+
+def bench_conv(torch, np, ssm, steps, K=4):
+    """Causal conv1d + SiLU (width 4) on the 2.8B-shaped layer's input [4, 5120, 2048] bf16, and its
+    decode step on the 2.8B-shaped serving batch [256, 5120].  Both are HBM-bound: the sequence
+    kernel moves 2 + 2 bytes per element (x in, out), the step 12 + 12 bytes of fp32 window state
+    plus 2 + 2 bytes of x and out per row."""
+    g = np.random.default_rng(0)
+    B, D, L = 4, 5120, 2048
+    xs = [torch.from_numpy(g.standard_normal((B, D, L), dtype=np.float32)).to(torch.bfloat16).cuda() for _ in range(3)]
+    w = torch.from_numpy(g.standard_normal((D, K), dtype=np.float32) * 0.5).cuda()
+    b = torch.from_numpy(g.standard_normal(D, dtype=np.float32) * 0.1).cuda()
+    out = torch.empty_like(xs[0])
+    st = torch.empty((B, D, K - 1), dtype=torch.float32, device="cuda")
+    for i in range(3):
+        ssm.conv1d_fwd(xs[i], w, b, True, None, out=out, state_out=st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        ssm.conv1d_fwd(xs[i % 3], w, b, True, None, out=out, state_out=st)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    by = B * D * L * 4 + B * D * (K - 1) * 4 + D * (K + 1) * 4
+    gbs = by / (ms * 1e-3) / 1e9
+    res = {"fwd": {"shape": [B, D, L], "width": K, "dtype": "bf16", "us_per_call": ms * 1e3,
+                   "elements_per_s": B * D * L / (ms * 1e-3), "hbm_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                   "bytes_per_call": by, "inputs_rotated": 3}}
+    R, Dd = 256, 5120
+    state = torch.from_numpy(g.standard_normal((R, Dd, K - 1), dtype=np.float32)).cuda()
+    xt = [torch.from_numpy(g.standard_normal((R, Dd), dtype=np.float32)).to(torch.bfloat16).cuda() for _ in range(8)]
+    yo = torch.empty((R, Dd), dtype=torch.bfloat16, device="cuda")
+    for i in range(4):
+        ssm.conv1d_update(state, xt[i], w, b, True, out=yo)
+    torch.cuda.synchronize()
+    n = 128
+    e0.record(stream)
+    for i in range(n):
+        ssm.conv1d_update(state, xt[i % 8], w, b, True, out=yo)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    by = R * Dd * ((K - 1) * 8 + 4) + Dd * (K + 1) * 4
+    gbs = by / (ms * 1e-3) / 1e9
+    res["update"] = {"shape": [R, Dd], "width": K, "dtype": "bf16", "steps": n, "us_per_step": ms * 1e3,
+                     "hbm_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": by,
+                     "note": "back to back: the 15.7 MB window state stays in the last-level cache"}
+    return res
 
 
 def copy_calibration(torch, mib):

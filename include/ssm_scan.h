@@ -123,6 +123,43 @@ int selective_state_update(float* state, const void* u, const void* delta, const
                            int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream);
 
 /*
+ * Causal depthwise 1-D convolution with an optional SiLU: the step before the selective
+ * SSM in the Mamba block (Mamba summary (junchaoiu.github.io), 方法 third step: linear
+ * expansion, 1-D convolution for local features, SiLU; mlqm.cn tutorial §7.1: causal
+ * 1-D convolution then SiLU ahead of the selective SSM).  Per row (b, d), step t:
+ *
+ *   v_t = bias[d] + sum_{k=0..width-1} weight[d,k] * x[t-(width-1)+k]
+ *   out_t = silu(v_t) if silu else v_t
+ *
+ *   x, out        : [batch, dim, seqlen] (dtype); out must not overlap an input
+ *   weight        : [dim, width] fp32, width in 1..4;  bias : [dim] fp32, NULL = 0
+ *   conv_state_in : [batch, dim, width-1] fp32, the width-1 inputs before step 0,
+ *                   oldest first; NULL = zeros
+ *   conv_state_out: [batch, dim, width-1] fp32 output, the last width-1 inputs (the
+ *                   state the next piece or the decode steps continue from); NULL = not
+ *                   written.  Must not overlap conv_state_in or any other argument.
+ * A request keeps this window next to its SSM state ("AI inference series (14)",
+ * wiblog.cn: per-request conv state and SSM state).  Required: x, weight, out (x and
+ * out may be NULL when seqlen == 0).  Errors as for selective_scan_fwd; width outside
+ * 1..4 is SSM_ERR_UNSUPPORTED.
+ */
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const float* conv_state_in,
+                      int silu, void* out, float* conv_state_out, int64_t batch, int64_t dim, int64_t seqlen,
+                      int64_t width, int dtype, void* stream);
+
+/*
+ * One decode step of the convolution for every row, the window advanced in place:
+ * out = silu(bias + weight . [conv_state, x]) and conv_state <- [conv_state[1:], x].
+ *
+ *   conv_state : [batch, dim, width-1] fp32, read and UPDATED IN PLACE
+ *   x, out     : [batch, dim] (dtype);  weight, bias, silu, width as above
+ * Required: conv_state (unless width == 1), x, weight, out; out must not overlap an input
+ * or the state.
+ */
+int causal_conv1d_update(float* conv_state, const void* x, const float* weight, const float* bias, int silu,
+                         void* out, int64_t batch, int64_t dim, int64_t width, int dtype, void* stream);
+
+/*
  * Launch plan selective_scan_fwd would use for these sizes on a GPU with `num_cus`
  * compute units (host-only; no GPU needed).  Writes 5 int64 values to `out`:
  *   out[0] mode: 0 intervals (the channel groups' sequences laid end to end and cut into
@@ -145,7 +182,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -17,8 +17,9 @@ import os
 
 import torch
 
-__all__ = ["load", "lib_path", "scan_fwd", "state_update", "scan_plan", "SsmError", "STATUS", "selective_scan_fwd",
-           "selective_scan_fwd_resume", "selective_state_update", "last_error"]
+__all__ = ["load", "lib_path", "scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
+           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+           "causal_conv1d_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_PKG, "libssm_scan.so")
@@ -27,8 +28,8 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "ssm_scan_plan",
-           "ssm_last_error", "ssm_abi_version")
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+           "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -55,6 +56,10 @@ def load():
         lib.selective_scan_fwd_resume.restype = I
         lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.selective_state_update.restype = I
+        lib.causal_conv1d_fwd.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
+        lib.causal_conv1d_fwd.restype = I
+        lib.causal_conv1d_update.argtypes = [P, P, P, P, I, P, I64, I64, I64, I, P]
+        lib.causal_conv1d_update.restype = I
         lib.ssm_last_error.argtypes = []
         lib.ssm_last_error.restype = ctypes.c_char_p
         lib.ssm_abi_version.argtypes = []
@@ -129,6 +134,14 @@ def selective_state_update(*args) -> int:
     return int(load().selective_state_update(*args))
 
 
+def causal_conv1d_fwd(*args) -> int:
+    return int(load().causal_conv1d_fwd(*args))
+
+
+def causal_conv1d_update(*args) -> int:
+    return int(load().causal_conv1d_update(*args))
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True,
              return_last_state: bool = True, y=None, last_state=None, initial_state=None):
     """Forward selective scan.  u, delta, z: [batch, dim, L]; B, C: [batch, N, L]
@@ -197,3 +210,50 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, y=None)
                                     _stream(dev))
     _check(rc)
     return y
+
+
+def conv1d_fwd(x, weight, bias=None, silu: bool = True, state=None, return_state: bool = True, out=None,
+               state_out=None):
+    """Causal depthwise conv1d (+ SiLU).  x: [batch, dim, L] (fp32 or bf16); weight: [dim, K]
+    fp32 (K <= 4); bias: [dim] fp32; state: [batch, dim, K-1] fp32 inputs before step 0.
+    Returns (out, state_out) -- state_out holds the last K-1 inputs."""
+    lib = load()
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [batch, dim, seqlen] and weight [dim, width]")
+    batch, dim, L = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    _require(x, "x", (batch, dim, L), x.dtype, dev)
+    _require(weight, "weight", (dim, K), torch.float32, dev)
+    _require(bias, "bias", (dim,), torch.float32, dev)
+    _require(state, "state", (batch, dim, K - 1), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", (batch, dim, L), x.dtype, dev)
+    if return_state and state_out is None:
+        state_out = torch.empty((batch, dim, K - 1), dtype=torch.float32, device=dev)
+    _require(state_out, "state_out", (batch, dim, K - 1), torch.float32, dev)
+    _check(lib.causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state), 1 if silu else 0, _ptr(out),
+                                 _ptr(state_out), batch, dim, L, K, _dtype_code(x), _stream(dev)))
+    return out, state_out
+
+
+def conv1d_update(state, x, weight, bias=None, silu: bool = True, out=None):
+    """One decode step of the conv; ``state`` [batch, dim, K-1] fp32 is advanced in place.
+    x: [batch, dim].  Returns out [batch, dim]."""
+    lib = load()
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be [batch, dim] and weight [dim, width]")
+    batch, dim = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    _require(state, "state", (batch, dim, K - 1), torch.float32, dev)
+    _require(x, "x", (batch, dim), x.dtype, dev)
+    _require(weight, "weight", (dim, K), torch.float32, dev)
+    _require(bias, "bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", (batch, dim), x.dtype, dev)
+    _check(lib.causal_conv1d_update(_ptr(state), _ptr(x), _ptr(weight), _ptr(bias), 1 if silu else 0, _ptr(out),
+                                    batch, dim, K, _dtype_code(x), _stream(dev)))
+    return out

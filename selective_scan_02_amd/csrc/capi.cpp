@@ -207,4 +207,73 @@ int selective_state_update(float* state, const void* u, const void* delta, const
   return hip_status(ssm::launch_state_update(p, (hipStream_t)stream), "selective_state_update launch");
 }
 
+int causal_conv1d_fwd(const void* x, const float* weight, const float* bias, const float* conv_state_in,
+                      int silu, void* out, float* conv_state_out, int64_t batch, int64_t dim, int64_t seqlen,
+                      int64_t width, int dtype, void* stream) {
+  g_last_error.clear();
+  if (seqlen != 0) {
+    if (!x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+    if (!out) return fail(SSM_ERR_NULL_ARG, "out is NULL");
+  }
+  if (!weight) return fail(SSM_ERR_NULL_ARG, "weight is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || seqlen < 0 || width < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld seqlen=%lld width=%lld", (long long)batch,
+                (long long)dim, (long long)seqlen, (long long)width);
+  if (width > 4) return fail(SSM_ERR_UNSUPPORTED, "width=%lld not in 1..4", (long long)width);
+  if (too_big(batch, dim, seqlen) || too_big(batch, dim, width)) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (silu != 0 && silu != 1) return fail(SSM_ERR_BAD_SHAPE, "silu must be 0 or 1");
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim * seqlen, nst = (uint64_t)batch * dim * (width - 1) * 4;
+  const Range ins[] = {{"x", x, nx * es, es},
+                       {"weight", weight, (uint64_t)dim * width * 4, 4},
+                       {"bias", bias, (uint64_t)dim * 4, 4},
+                       {"conv_state_in", conv_state_in, nst, 4}};
+  const Range ro{"out", out, nx * es, es}, rs{"conv_state_out", conv_state_out, nst, 4};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(ro)) return rc;
+  if (int rc = check_aligned(rs)) return rc;
+  for (const Range& r : ins) {
+    if (overlap(ro, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+    if (overlap(rs, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
+  }
+  if (overlap(ro, rs)) return fail(SSM_ERR_ALIAS, "out overlaps conv_state_out");
+  ssm::ConvParams p{x, weight, bias, conv_state_in, silu, out, conv_state_out, batch, dim, seqlen, width, dtype};
+  return hip_status(ssm::launch_conv1d_fwd(p, (hipStream_t)stream), "causal_conv1d_fwd launch");
+}
+
+int causal_conv1d_update(float* conv_state, const void* x, const float* weight, const float* bias, int silu,
+                         void* out, int64_t batch, int64_t dim, int64_t width, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!conv_state && width > 1) return fail(SSM_ERR_NULL_ARG, "conv_state is NULL");
+  if (!x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+  if (!weight) return fail(SSM_ERR_NULL_ARG, "weight is NULL");
+  if (!out) return fail(SSM_ERR_NULL_ARG, "out is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || width < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld width=%lld", (long long)batch, (long long)dim,
+                (long long)width);
+  if (width > 4) return fail(SSM_ERR_UNSUPPORTED, "width=%lld not in 1..4", (long long)width);
+  if (too_big(batch, dim, width)) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (silu != 0 && silu != 1) return fail(SSM_ERR_BAD_SHAPE, "silu must be 0 or 1");
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim;
+  const Range ins[] = {{"x", x, nx * es, es},
+                       {"weight", weight, (uint64_t)dim * width * 4, 4},
+                       {"bias", bias, (uint64_t)dim * 4, 4}};
+  const Range rs{"conv_state", conv_state, nx * (width - 1) * 4, 4}, ro{"out", out, nx * es, es};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(rs)) return rc;
+  if (int rc = check_aligned(ro)) return rc;
+  for (const Range& r : ins) {
+    if (overlap(rs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps %s", r.name);
+    if (overlap(ro, r)) return fail(SSM_ERR_ALIAS, "out overlaps %s", r.name);
+  }
+  if (overlap(ro, rs)) return fail(SSM_ERR_ALIAS, "out overlaps conv_state");
+  ssm::ConvStepParams p{conv_state, x, weight, bias, silu, out, batch, dim, width, dtype};
+  return hip_status(ssm::launch_conv1d_update(p, (hipStream_t)stream), "causal_conv1d_update launch");
+}
+
 }  // extern "C"

@@ -40,6 +40,29 @@ struct StepParams {
   int dtype;
 };
 
+struct ConvParams {
+  const void* x;
+  const float* weight;     // [dim, width]
+  const float* bias;       // nullable [dim]
+  const float* state_in;   // nullable [batch, dim, width-1]
+  int silu;
+  void* out;
+  float* state_out;        // nullable [batch, dim, width-1]
+  int64_t batch, dim, seqlen, width;
+  int dtype;
+};
+
+struct ConvStepParams {
+  float* state;            // [batch, dim, width-1], updated in place
+  const void* x;           // [batch, dim]
+  const float* weight;
+  const float* bias;
+  int silu;
+  void* out;               // [batch, dim]
+  int64_t batch, dim, width;
+  int dtype;
+};
+
 struct ScanPlan {
   int mode;          // 0 intervals, 1 one pass, 2 aggregate/carry/output
   int64_t groups;    // channel groups of 64
@@ -55,5 +78,7 @@ hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any
 bool chunked_supported(const ScanParams& p);
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
+hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream);
+hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream);
 
 }  // namespace ssm

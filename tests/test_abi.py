@@ -40,8 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "ssm_scan_plan",
-                 "ssm_last_error", "ssm_abi_version"):
+    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+                 "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
 
@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
 
 
 def scan_args(**over):
@@ -198,3 +198,39 @@ def test_scan_plan_intervals_cover_and_balance(lib):
 def torch_dtype_f32():
     import torch
     return torch.float32
+
+
+def conv_args(**over):
+    a = dict(x=addr(1), w=addr(2), bias=addr(3), st_in=addr(4), silu=1, out=addr(5), st_out=addr(6), batch=2,
+             dim=64, seqlen=100, width=4, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("x", "w", "bias", "st_in", "silu", "out", "st_out", "batch", "dim", "seqlen", "width",
+                           "dtype", "stream")]
+
+
+def conv_step_args(**over):
+    a = dict(state=addr(1), x=addr(2), w=addr(3), bias=addr(4), silu=1, out=addr(5), batch=2, dim=64, width=4,
+             dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("state", "x", "w", "bias", "silu", "out", "batch", "dim", "width", "dtype", "stream")]
+
+
+def test_conv_validation(lib):
+    f, u = lib.causal_conv1d_fwd, lib.causal_conv1d_update
+    assert f(*conv_args(x=None)) == NULL_ARG
+    assert f(*conv_args(w=None)) == NULL_ARG
+    assert f(*conv_args(out=None)) == NULL_ARG
+    assert f(*conv_args(seqlen=0, x=None, out=None, w=None)) == NULL_ARG  # weight still required
+    assert f(*conv_args(width=5)) == UNSUPPORTED and "width" in ssm.last_error()
+    assert f(*conv_args(width=0)) == BAD_SHAPE
+    assert f(*conv_args(silu=3)) == BAD_SHAPE
+    assert f(*conv_args(dtype=4)) == BAD_DTYPE
+    assert f(*conv_args(x=addr(1) + 1)) == MISALIGNED
+    assert f(*conv_args(out=addr(1) + 64)) == ALIAS                 # out inside x
+    assert f(*conv_args(st_out=addr(4) + 8)) == ALIAS               # state out overlapping state in
+    assert f(*conv_args(st_out=addr(4))) == ALIAS and "conv_state_out" in ssm.last_error()
+    assert u(*conv_step_args(state=None)) == NULL_ARG
+    assert u(*conv_step_args(x=None)) == NULL_ARG
+    assert u(*conv_step_args(width=7)) == UNSUPPORTED
+    assert u(*conv_step_args(out=addr(1) + 4)) == ALIAS             # out inside the state
+    assert u(*conv_step_args(state=addr(3))) == ALIAS               # state overlapping the weights
