@@ -10,10 +10,12 @@
 //   v_t = bias[d] + sum_{k<K} w[d,k] * x[t-(K-1)+k],   out_t = silu(v_t) (or v_t)
 //
 // Both kernels are bound by HBM: K FMAs and one SiLU per element against
-// 2 x (element size) bytes.  conv1d_fwd_kernel: a wave covers 512 consecutive
-// steps of one row, 8 per lane, loaded and stored as 16-byte pieces; the K-1
-// inputs before a lane's first step come from the previous lane by a cross-lane
-// shift (lane 0 reads them from memory, or from the state before step 0).
+// 2 x (element size) bytes.  conv1d_fwd_kernel: a wave covers 4 runs of 64
+// lanes x 16 bytes of consecutive steps of one row (each load or store
+// instruction moves one contiguous kilobyte); the K-1 inputs before a lane's
+// piece come from the previous lane by a cross-lane shift, lane 0 taking them
+// from lane 63 of the previous run, or from memory (or the state before step 0)
+// at the wave's start.
 // conv1d_update_kernel: one thread per row shifts the window in place.
 #include <hip/hip_runtime.h>
 
@@ -22,9 +24,6 @@
 
 namespace ssm {
 namespace {
-
-constexpr int kEPT = 8;               // steps per lane
-constexpr int kWaveSteps = 64 * kEPT;  // steps per wave
 
 struct ConvArgs {
   const void* x;
@@ -38,103 +37,130 @@ struct ConvArgs {
   int vec;              // rows are whole 16-byte pieces and x, out are 16-byte aligned
 };
 
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[kEPT]) {
-  if constexpr (sizeof(T) == 2) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __builtin_bit_cast(float, w4[i] << 16);
-      v[2 * i + 1] = __builtin_bit_cast(float, w4[i] & 0xffff0000u);
-    }
-  } else {
-    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
+// A wave covers kRuns consecutive runs of 64 lanes x 16 bytes of one row: every load and
+// store instruction moves one contiguous kilobyte, and each lane keeps kRuns pieces in flight.
+constexpr int kRuns = 4;
+template <typename T> constexpr int kPS = 16 / sizeof(T);  // steps per 16-byte piece
 
-template <typename T>
-__device__ __forceinline__ void store8(T* p, const float (&o)[kEPT]) {
-  if constexpr (sizeof(T) == 2) {
-    uint32_t w4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)o[2 * i]);
-      const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)o[2 * i + 1]);
-      w4[i] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4*>(p) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  } else {
-    reinterpret_cast<float4*>(p)[0] = make_float4(o[0], o[1], o[2], o[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(o[4], o[5], o[6], o[7]);
-  }
-}
-
-template <int K, typename T>
-__global__ __launch_bounds__(256) void conv1d_fwd_kernel(const ConvArgs a) {
+// One wave's runs.  FULL (uniform per wave): every piece lies inside the row and rows are
+// 16-byte aligned, so the pieces move as 16-byte vectors; otherwise element by element with
+// bounds checks.  The two cases are separate code, so the values stay in registers.
+template <int K, typename T, bool FULL>
+__device__ __forceinline__ void conv_wave(const ConvArgs& a, int64_t row, int64_t w0, int lane) {
   constexpr int H = K > 1 ? K - 1 : 1;
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= a.rows * a.nseg) return;  // uniform per wave
-  const int64_t row = wave / a.nseg;
-  const int64_t t0 = (wave - row * a.nseg) * kWaveSteps + (int64_t)lane * kEPT;
+  constexpr int PS = kPS<T>;
+  constexpr int kRunSteps = 64 * PS;
   const int64_t L = a.L;
   const int64_t d = row % a.dim;
   const T* xr = (const T*)a.x + row * L;
-  const bool full = a.vec && t0 + kEPT <= L;
+  T* orow = (T*)a.out + row * L;
 
-  float v[kEPT];
-  if (full) {
-    load8(xr + t0, v);
+  float v[kRuns][PS];
+  if constexpr (FULL) {
+    uint4 q[kRuns];
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) q[r] = *reinterpret_cast<const uint4*>(xr + w0 + r * kRunSteps + lane * PS);
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+      const uint32_t w4[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          v[r][2 * j] = __builtin_bit_cast(float, w4[j] << 16);
+          v[r][2 * j + 1] = __builtin_bit_cast(float, w4[j] & 0xffff0000u);
+        } else {
+          v[r][j] = __builtin_bit_cast(float, w4[j]);
+        }
+      }
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) v[e] = t0 + e < L ? ld(xr, t0 + e) : 0.0f;
-  }
-  // inputs at steps t0-(K-1) .. t0-1: the previous lane's last K-1 values
-  float hst[H];
+    for (int r = 0; r < kRuns; ++r) {
+      const int64_t t0 = w0 + r * kRunSteps + lane * PS;
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) hst[j] = __shfl_up(v[kEPT - (K - 1) + j], 1, 64);
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) {
-      const int64_t s = t0 - (K - 1) + j;
-      hst[j] = s >= 0 ? ld(xr, s) : (a.st_in ? a.st_in[row * (K - 1) + (K - 1) + s] : 0.0f);
+      for (int e = 0; e < PS; ++e) v[r][e] = t0 + e < L ? ld(xr, t0 + e) : 0.0f;
     }
   }
   float w[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) w[k] = a.w[d * K + k];
   const float bias = a.bias ? a.bias[d] : 0.0f;
+  // inputs at the K-1 steps before the wave: from memory, or the state before step 0
+  float h0[H];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    const int64_t s = w0 - (K - 1) + j;
+    h0[j] = s >= 0 ? ld(xr, s) : (a.st_in ? a.st_in[row * (K - 1) + (K - 1) + s] : 0.0f);
+  }
 
-  float o[kEPT];
 #pragma unroll
-  for (int e = 0; e < kEPT; ++e) {
-    float acc = bias;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int s = e - (K - 1) + k;  // step relative to t0
-      acc = __builtin_fmaf(w[k], s >= 0 ? v[s >= 0 ? s : 0] : hst[s >= 0 ? 0 : K - 1 + s], acc);
-    }
-    o[e] = a.silu ? silu(acc) : acc;
-  }
-  T* orow = (T*)a.out + row * L;
-  if (full) {
-    store8(orow + t0, o);
-  } else {
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e)
-      if (t0 + e < L) st(orow, t0 + e, o[e]);
-  }
-  // the lane holding step L-1 writes the state a following call continues from
-  if (a.st_out && K > 1 && t0 <= L - 1 && L - 1 < t0 + kEPT) {
+  for (int r = 0; r < kRuns; ++r) {
+    const int64_t t0 = w0 + r * kRunSteps + lane * PS;
+    // inputs at steps t0-(K-1) .. t0-1: the previous lane's last K-1 values; lane 0 takes
+    // them from lane 63 of the previous run (or from before the wave)
+    float hst[H];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
-      const int64_t s = L - (K - 1) + j;  // input step; >= t0 - (K-1)
-      const int r = (int)(s - t0);
-      a.st_out[row * (K - 1) + j] = r >= 0 ? v[r >= 0 ? r : 0] : hst[r >= 0 ? 0 : K - 1 + r];
+      const float up = __shfl_up(v[r][PS - (K - 1) + j], 1, 64);
+      const float wrap = r > 0 ? __shfl(v[r > 0 ? r - 1 : 0][PS - (K - 1) + j], 63, 64) : h0[j];
+      hst[j] = lane == 0 ? wrap : up;
+    }
+    float o[PS];
+#pragma unroll
+    for (int e = 0; e < PS; ++e) {
+      float acc = bias;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int s = e - (K - 1) + k;  // step relative to t0
+        acc = __builtin_fmaf(w[k], s >= 0 ? v[r][s >= 0 ? s : 0] : hst[s >= 0 ? 0 : K - 1 + s], acc);
+      }
+      o[e] = a.silu ? silu(acc) : acc;
+    }
+    if constexpr (FULL) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)o[2 * j]);
+          const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)o[2 * j + 1]);
+          w4[j] = lo | (hi << 16);
+        } else {
+          w4[j] = __builtin_bit_cast(uint32_t, o[j]);
+        }
+      }
+      *reinterpret_cast<uint4*>(orow + t0) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < PS; ++e)
+        if (t0 + e < L) st(orow, t0 + e, o[e]);
+    }
+    // the lane holding step L-1 writes the state a following call continues from
+    if (a.st_out && K > 1 && t0 <= L - 1 && L - 1 < t0 + PS) {
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        const int64_t s = L - (K - 1) + j;  // input step; >= t0 - (K-1)
+        const int qq = (int)(s - t0);  // in -(K-1) .. PS-1; selected with constant indices only
+        float val = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PS; ++e) val = qq == e ? v[r][e] : val;
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) val = qq == m - (K - 1) ? hst[m] : val;
+        a.st_out[row * (K - 1) + j] = val;
+      }
     }
   }
+}
+
+template <int K, typename T>
+__global__ __launch_bounds__(256) void conv1d_fwd_kernel(const ConvArgs a) {
+  constexpr int64_t kWaveSteps = kRuns * 64 * kPS<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= a.rows * a.nseg) return;  // uniform per wave
+  const int64_t row = wave / a.nseg;
+  const int64_t w0 = (wave - row * a.nseg) * kWaveSteps;  // first step of the wave
+  if (a.vec && w0 + kWaveSteps <= a.L) conv_wave<K, T, true>(a, row, w0, lane);
+  else conv_wave<K, T, false>(a, row, w0, lane);
 }
 
 // seqlen == 0: the state out is the state in (or zeros)
@@ -172,6 +198,7 @@ __global__ __launch_bounds__(256) void conv1d_update_kernel(const UpdArgs a) {
 
 template <int K, typename T>
 hipError_t run_fwd(const ConvParams& p, hipStream_t stream) {
+  constexpr int64_t kWaveSteps = kRuns * 64 * kPS<T>;
   ConvArgs a{p.x, p.weight, p.bias, p.state_in, p.out, p.state_out, p.batch * p.dim, p.dim, p.seqlen,
              (p.seqlen + kWaveSteps - 1) / kWaveSteps, p.silu, 0};
   const int64_t es = sizeof(T);
