@@ -60,7 +60,8 @@ typedef enum {
   SSM_ERR_NULL_ARG = -1,     /* a required pointer is NULL                         */
   SSM_ERR_BAD_SHAPE = -2,    /* a size is negative / zero where not allowed / too big */
   SSM_ERR_BAD_DTYPE = -3,    /* dtype is not SSM_F32 or SSM_BF16                   */
-  SSM_ERR_MISALIGNED = -4,   /* a pointer is not aligned to its element size       */
+  SSM_ERR_MISALIGNED = -4,   /* a pointer is not aligned to its element size (or to the
+                                vector width an entry point documents)              */
   SSM_ERR_ALIAS = -5,        /* an output overlaps an input or another output      */
   SSM_ERR_UNSUPPORTED = -6,  /* dstate not in the compiled set {1,2,4,8,16,32,64}  */
   SSM_ERR_HIP = -7           /* a HIP runtime call or kernel launch failed         */
@@ -115,6 +116,8 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
  *   B, C        : [batch, dstate] (dtype)
  *   D, dt_bias  : [dim] fp32, NULL = absent / zero
  *   y           : [batch, dim] (dtype) output
+ * With dstate >= 4, state and A must be 16-byte aligned and B, C aligned to 4 elements
+ * (lanes move 4 consecutive entries at once); otherwise SSM_ERR_MISALIGNED.
  * Softplus is always applied to delta + dt_bias.  Required: state, u, delta, A,
  * B, C, y; state and y must not overlap an input or each other.
  */

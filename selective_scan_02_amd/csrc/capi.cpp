@@ -184,15 +184,17 @@ int selective_state_update(float* state, const void* u, const void* delta, const
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
   const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nx = (uint64_t)batch * dim, nbc = (uint64_t)batch * dstate;
+  // with dstate >= 4 a lane moves 4 consecutive states, A, B and C entries as one vector
+  const uint64_t v4 = dstate >= 4 ? 4 : 1;
   const Range ins[] = {{"u", u, nx * es, es},
                        {"delta", delta, nx * es, es},
                        {"z", z, nx * es, es},
-                       {"B", B, nbc * es, es},
-                       {"C", C, nbc * es, es},
-                       {"A", A, (uint64_t)dim * dstate * 4, 4},
+                       {"B", B, nbc * es, v4 * es},
+                       {"C", C, nbc * es, v4 * es},
+                       {"A", A, (uint64_t)dim * dstate * 4, v4 * 4},
                        {"D", D, (uint64_t)dim * 4, 4},
                        {"dt_bias", dt_bias, (uint64_t)dim * 4, 4}};
-  const Range rs{"state", state, nx * dstate * 4, dstate >= 4 ? 16u : 4u}, ry{"y", y, nx * es, es};
+  const Range rs{"state", state, nx * dstate * 4, v4 * 4}, ry{"y", y, nx * es, es};
   for (const Range& r : ins)
     if (int rc = check_aligned(r)) return rc;
   if (int rc = check_aligned(rs)) return rc;

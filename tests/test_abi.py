@@ -111,6 +111,8 @@ def test_misaligned(lib):
     assert lib.selective_scan_fwd(*scan_args(dtype=0, delta=addr(2) + 2)) == MISALIGNED  # fp32 needs 4
     assert lib.selective_scan_fwd(*scan_args(A=addr(3) + 2)) == MISALIGNED
     assert lib.selective_state_update(*step_args(state=addr(1) + 4)) == MISALIGNED   # float4 state rows
+    assert lib.selective_state_update(*step_args(A=addr(4) + 4)) == MISALIGNED       # float4 rows of A
+    assert lib.selective_state_update(*step_args(B=addr(5) + 2)) == MISALIGNED       # 4 bf16 of B at once
 
 
 def test_alias(lib):
