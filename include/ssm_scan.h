@@ -32,9 +32,10 @@
  *    current device), row-major and contiguous (last dimension fastest).
  *  - `dtype` (ssm_dtype_t) is the element type of u, delta, z, B, C and y.  A, D,
  *    dt_bias and the state are always fp32.  Arithmetic is fp32 throughout.
- *  - Ownership: the caller owns every buffer.  The library keeps no pointer after
- *    a call returns.  Scratch memory (scan segment carries) is taken from HIP's
- *    stream-ordered allocator on `stream` and released on `stream`.
+ *  - Ownership: the caller owns every buffer.  The library keeps no pointer to them
+ *    after a call returns.  Scratch memory (scan segment carries and flags) is taken,
+ *    stream-ordered on `stream`, from a memory pool the library creates per device and
+ *    keeps until the process exits, and is returned to that pool on `stream`.
  *  - Calls are asynchronous on `stream` (hipStream_t; NULL = the null stream) and
  *    never synchronise the device.
  *  - Errors: the return value is an ssm_status_t.  Arguments are validated before

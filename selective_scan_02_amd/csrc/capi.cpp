@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/ssm_scan.h"
@@ -56,6 +58,37 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+namespace ssm {
+
+hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream) {
+  static std::mutex mu;
+  static hipMemPool_t pools[256] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  hipMemPool_t pool;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+      hipMemPoolProps props{};
+      props.allocType = hipMemAllocationTypePinned;  // device memory, not migratable
+      props.handleTypes = hipMemHandleTypeNone;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      hipMemPool_t np = nullptr;
+      if ((e = hipMemPoolCreate(&np, &props)) != hipSuccess) return e;
+      uint64_t keep = UINT64_MAX;  // never hand reserved memory back between calls
+      if ((e = hipMemPoolSetAttribute(np, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) return e;
+      pools[dev] = np;
+    }
+    pool = pools[dev];
+  }
+  return hipMallocFromPoolAsync(p, bytes, pool, stream);
+}
+
+}  // namespace ssm
 
 extern "C" {
 

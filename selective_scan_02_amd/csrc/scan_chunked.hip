@@ -700,7 +700,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.wlen = pl.seg_len / kT;
     const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
     const size_t bytes = carry_bytes + ((size_t)a.groups * kS + 64) * sizeof(int);
-    if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
+    if ((err = scratch_alloc(&scratch, bytes, stream)) != hipSuccess) return err;
     a.carry = (float*)scratch;
     a.ticket = (int*)((char*)scratch + carry_bytes);
     a.flags = a.ticket + 64;
@@ -713,7 +713,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     }
   } else if (K > 1) {
     const size_t bytes = (size_t)K * chans * (N + 1) * sizeof(float);
-    if ((err = hipMallocAsync(&scratch, bytes, stream)) != hipSuccess) return err;
+    if ((err = scratch_alloc(&scratch, bytes, stream)) != hipSuccess) return err;
     a.seg_h = (float*)scratch;
     a.seg_dt = a.seg_h + (size_t)K * chans * N;
     Args agg = a;

@@ -179,7 +179,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   if (nseg > 1) {
     const size_t bytes = (size_t)nseg * chans * (N + 1) * sizeof(float);
     void* scratch = nullptr;
-    err = hipMallocAsync(&scratch, bytes, stream);
+    err = scratch_alloc(&scratch, bytes, stream);
     if (err != hipSuccess) return err;
     a.seg_h = (float*)scratch;
     a.seg_dt = a.seg_h + (size_t)nseg * chans * N;

@@ -72,6 +72,11 @@ struct ScanPlan {
 };
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
 
+// Stream-ordered scratch memory from a pool the library owns, one per device.  The pool keeps
+// what it has reserved between calls (no return to the system at synchronisation points), so
+// the carries and flags of one call reuse the memory of the previous one.
+hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream);
+
 bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment
