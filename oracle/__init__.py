@@ -50,6 +50,9 @@ def _load():
         lib.oracle_step.restype = I
         lib.oracle_conv1d.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I, P, P, I]
         lib.oracle_conv1d.restype = I
+        lib.oracle_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P, P, P, P, P, P, P,
+                                         P, P, I]
+        lib.oracle_scan_bwd.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -209,3 +212,45 @@ def conv1d(x, weight, bias=None, silu=True, state=None, threads: int = 0):
     if rc != 0:
         raise ValueError(f"oracle_conv1d failed ({rc})")
     return out.reshape(batch, dim, seqlen), st_out[:, :width - 1].reshape(batch, dim, width - 1)
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None, dy=None,
+             threads: int = 0) -> dict:
+    """Gradients of sum(dy * y) for the forward scan, fp64 (adjoint method; see ssm_oracle.c).
+    Same inputs as scan() plus dy [B,D,L] (dtype of u).  Returns a dict of float64 arrays:
+    du, ddelta, dz [B,D,L] (dz None without z); dB, dC [B,N,L]; dA [D,N]; dD, ddt_bias [D]
+    (None when the input is absent); dh0 [B,D,N]."""
+    keep = []
+    batch, dim, seqlen = (int(s) for s in u.shape)
+    dstate = int(A.shape[1])
+    pu, dtype = _raw(u, keep)
+    pdl, _ = _raw(delta, keep)
+    pB, _ = _raw(B, keep)
+    pC, _ = _raw(C, keep)
+    pz, _ = _raw(z, keep)
+    pdy, dt6 = _raw(dy, keep)
+    if dt6 != dtype:
+        raise TypeError("dy must have the dtype of u")
+    ph0 = None
+    if h0 is not None:
+        h = h0.detach().cpu().double().numpy() if isinstance(h0, torch.Tensor) else np.asarray(h0, np.float64)
+        h = np.ascontiguousarray(h.reshape(batch * dim, dstate), dtype=np.float64)
+        keep.append(h)
+        ph0 = h.ctypes.data
+    out = {k: np.zeros(shape, dtype=np.float64) for k, shape in
+           [("du", (batch, dim, seqlen)), ("ddelta", (batch, dim, seqlen)), ("dz", (batch, dim, seqlen)),
+            ("dA", (dim, dstate)), ("dB", (batch, dstate, seqlen)), ("dC", (batch, dstate, seqlen)),
+            ("dD", (dim,)), ("ddt_bias", (dim,)), ("dh0", (batch, dim, dstate))]}
+    rc = _load().oracle_scan_bwd(pu, pdl, _f32(A, keep), pB, pC, _f32(D, keep), pz, _f32(dt_bias, keep),
+                                 1 if softplus else 0, ph0, pdy, batch, dim, dstate, seqlen, dtype,
+                                 *(out[k].ctypes.data for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD",
+                                                                "ddt_bias", "dh0")), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd failed ({rc})")
+    if z is None:
+        out["dz"] = None
+    if D is None:
+        out["dD"] = None
+    if dt_bias is None:
+        out["ddt_bias"] = None
+    return out

@@ -42,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -208,4 +209,162 @@ int oracle_conv1d(const void* x, const float* w, const float* bias, const double
     }
   }
   return 0;
+}
+
+/*
+ * Backward of the forward scan: the gradients of L = sum dy * y with respect to every
+ * input, by the adjoint method ("Mamba close reading" (jsqmd.com), gradient analysis: dL/dA
+ * as a sum over t of (dh_t/dA)^T dL/dh_t, computed with the adjoint; the Mamba summary,
+ * 方法 second step: the backward pass recomputes the states instead of storing them).
+ * Per channel (b, d) and state n, with g_t = silu(z_t) (1 without z) and
+ * s_t = sum_n C_t[n] h_t[n] + D u_t (y_t = s_t g_t):
+ *
+ *   ds_t      = dy_t g_t                       dz_t = dy_t s_t silu'(z_t)
+ *   lam_t[n]  = ds_t C_t[n] + Abar_{t+1}[n] lam_{t+1}[n]     (lam after the last step = 0)
+ *   du_t      = ds_t D + sum_n lam_t[n] Delta_t B_t[n]
+ *   dDelta_t  = sum_n lam_t[n] (h_{t-1}[n] Abar_t[n] A[n] + B_t[n] u_t)
+ *   ddelta_t  = dDelta_t * (softplus ? sigmoid(delta_t + dt_bias) : 1)
+ *   dA[d,n]  += lam_t[n] h_{t-1}[n] Abar_t[n] Delta_t       dD[d] += ds_t u_t
+ *   ddt_bias[d] += ddelta_t                                  dh0[n] = Abar_0[n] lam_0[n]
+ *   dB[b,n,t] += lam_t[n] Delta_t u_t            dC[b,n,t] += ds_t h_t[n]   (sums over d)
+ *
+ * Inputs as oracle_scan plus dy [B,D,L] (dtype).  Outputs (double, any may be NULL except
+ * du and ddelta): du, ddelta, dz [B,D,L]; dB, dC [B,N,L]; dA [D,N]; dD, ddt_bias [D];
+ * dh0 [B,D,N].  Sums over b and d are taken in index order, so the result does not
+ * depend on the thread count.  Sequences up to 2^22 steps.
+ */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, int softplus_on, const double* h0,
+                    const void* dy, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                    double* du, double* ddelta, double* dz, double* dA, double* dB, double* dC, double* dD,
+                    double* ddt_bias, double* dh0, int nthreads) {
+  if (batch < 0 || dim < 0 || dstate <= 0 || seqlen < 0 || dstate > 1024 || seqlen > (1 << 22)) return -2;
+  if (!du || !ddelta) return -2;
+  set_threads(nthreads);
+  const int64_t L = seqlen, N = dstate, rows = batch * dim;
+  int fail = 0;
+  /* per channel: du, ddelta, dz, dh0 and the channel's share of dA, dD, ddt_bias */
+  double* pA = (double*)calloc((size_t)(rows * N > 0 ? rows * N : 1), sizeof(double));
+  double* pD = (double*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(double));
+  double* pb = (double*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(double));
+  if (!pA || !pD || !pb) fail = 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    if (fail) continue;
+    const int64_t b = r / dim, d = r % dim;
+    double* H = (double*)malloc((size_t)((L + 1) * N > 0 ? (L + 1) * N : 1) * sizeof(double)); /* h_{t-1} at row t */
+    double* DT = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+    double* lam = (double*)malloc((size_t)N * sizeof(double));
+    if (!H || !DT || !lam) { fail = 1; free(H); free(DT); free(lam); continue; }
+    for (int64_t n = 0; n < N; ++n) H[n] = h0 ? h0[r * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) { /* forward, keeping every state */
+      const int64_t i = r * L + t;
+      const double x = elem(delta, i, dtype) + (dt_bias ? (double)dt_bias[d] : 0.0);
+      const double dt = softplus_on ? softplus(x) : x;
+      DT[t] = dt;
+      const double ut = elem(u, i, dtype);
+      for (int64_t n = 0; n < N; ++n)
+        H[(t + 1) * N + n] = exp(dt * (double)A[d * N + n]) * H[t * N + n] + dt * elem(B, (b * N + n) * L + t, dtype) * ut;
+    }
+    for (int64_t n = 0; n < N; ++n) lam[n] = 0.0;
+    double aD = 0.0, ab = 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) { /* adjoint, last step first */
+      const int64_t i = r * L + t;
+      const double ut = elem(u, i, dtype), dyt = elem(dy, i, dtype), dt = DT[t];
+      double s = D ? (double)D[d] * ut : 0.0;
+      for (int64_t n = 0; n < N; ++n) s += elem(C, (b * N + n) * L + t, dtype) * H[(t + 1) * N + n];
+      double g = 1.0, gp = 0.0;
+      if (z) {
+        const double zz = elem(z, i, dtype), sg = sigmoid(zz);
+        g = zz * sg;
+        gp = sg * (1.0 + zz * (1.0 - sg));
+      }
+      const double ds = dyt * g;
+      if (dz) dz[i] = z ? dyt * s * gp : 0.0;
+      double dut = D ? ds * (double)D[d] : 0.0, dDt = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const int64_t j = (b * N + n) * L + t;
+        const double an = (double)A[d * N + n], abar = exp(dt * an), bt = elem(B, j, dtype);
+        /* lam[n] holds Abar_{t+1} lam_{t+1} here */
+        lam[n] = ds * elem(C, j, dtype) + lam[n];
+        dut += lam[n] * dt * bt;
+        dDt += lam[n] * (H[t * N + n] * abar * an + bt * ut);
+        pA[r * N + n] += lam[n] * H[t * N + n] * abar * dt;
+        lam[n] *= abar; /* -> Abar_t lam_t for the step before */
+      }
+      const double x = elem(delta, i, dtype) + (dt_bias ? (double)dt_bias[d] : 0.0);
+      const double dx = dDt * (softplus_on ? sigmoid(x) : 1.0);
+      du[i] = dut;
+      ddelta[i] = dx;
+      aD += ds * ut;
+      ab += dx;
+    }
+    if (dh0)
+      for (int64_t n = 0; n < N; ++n) dh0[r * N + n] = lam[n];
+    pD[r] = aD;
+    pb[r] = ab;
+    free(H);
+    free(DT);
+    free(lam);
+  }
+  if (!fail) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double sD = 0.0, sb = 0.0;
+      for (int64_t b = 0; b < batch; ++b) { sD += pD[b * dim + d]; sb += pb[b * dim + d]; }
+      if (dD) dD[d] = sD;
+      if (ddt_bias) ddt_bias[d] = sb;
+      for (int64_t n = 0; n < N; ++n) {
+        double sa = 0.0;
+        for (int64_t b = 0; b < batch; ++b) sa += pA[(b * dim + d) * N + n];
+        if (dA) dA[d * N + n] = sa;
+      }
+    }
+  }
+  free(pA);
+  free(pD);
+  free(pb);
+  if (fail) return -3;
+  if (!dB && !dC) return 0;
+  /* dB, dC: one task per (b, n); state n alone is a scalar recurrence, summed over d in order */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bn = 0; bn < batch * N; ++bn) {
+    if (fail) continue;
+    const int64_t b = bn / N, n = bn % N;
+    double* hs = (double*)malloc((size_t)((L + 1) > 0 ? (L + 1) : 1) * sizeof(double));
+    double* DT = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+    if (!hs || !DT) { fail = 1; free(hs); free(DT); continue; }
+    for (int64_t t = 0; t < L; ++t) {
+      if (dB) dB[(b * N + n) * L + t] = 0.0;
+      if (dC) dC[(b * N + n) * L + t] = 0.0;
+    }
+    for (int64_t d = 0; d < dim; ++d) {
+      const int64_t r = b * dim + d;
+      const double an = (double)A[d * N + n];
+      hs[0] = h0 ? h0[r * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = r * L + t;
+        const double x = elem(delta, i, dtype) + (dt_bias ? (double)dt_bias[d] : 0.0);
+        const double dt = softplus_on ? softplus(x) : x;
+        DT[t] = dt;
+        hs[t + 1] = exp(dt * an) * hs[t] + dt * elem(B, (b * N + n) * L + t, dtype) * elem(u, i, dtype);
+      }
+      double lam = 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i = r * L + t, j = (b * N + n) * L + t;
+        const double dyt = elem(dy, i, dtype);
+        double g = 1.0;
+        if (z) { const double zz = elem(z, i, dtype); g = zz * sigmoid(zz); }
+        const double ds = dyt * g;
+        lam = ds * elem(C, j, dtype) + lam;
+        if (dB) dB[j] += lam * DT[t] * elem(u, i, dtype);
+        if (dC) dC[j] += ds * hs[t + 1];
+        lam *= exp(DT[t] * an);
+      }
+    }
+    free(hs);
+    free(DT);
+  }
+  return fail ? -3 : 0;
 }
