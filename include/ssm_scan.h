@@ -1,8 +1,8 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
  *
- * Two operations of the Mamba selective SSM ("S6"), as described on the pages
- * this library follows:
+ * Operations of the Mamba selective SSM ("S6"), as described on the pages this
+ * library follows (plus the convolution ahead of it, below):
  *
  *   selective_scan_fwd      the whole-sequence forward scan (training / prefill):
  *                           "Selective Scan 如何兼顾训练与 Decode" in "AI inference
@@ -11,10 +11,11 @@
  *                           hardware-aware chunked scan of the Mamba summary
  *                           (junchaoiu.github.io, 方法 step 2) and of the mlqm.cn
  *                           tutorial §6.
+ *   selective_scan_bwd      gradients of the forward scan (training), states recomputed.
  *   selective_state_update  one autoregressive decode step: a single-step
  *                           recurrent update of a fixed-size per-request state,
  *                           updated in place (same wiblog.cn page, table of the
- *                           two execution forms and "推理框架需要管理完全不同的请求状态";
+ *                           two execution forms and the part on managing per-request state;
  *                           mlqm.cn tutorial §9.2, the single-step update).
  *
  * Per channel d, state n and step t (h_{-1} = 0 for the scan unless resumed from a state):
@@ -109,6 +110,47 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
 
 /*
+ * Backward of the forward scan: the gradients of a scalar loss through y, given
+ * dy = dLoss/dy.  The pages have the fused kernel recompute the intermediate states in
+ * the backward pass rather than store them (Mamba summary (junchaoiu.github.io), 方法
+ * step 2; mlqm.cn tutorial §6); the gradients follow from the recurrence above by the
+ * adjoint method.  With ds_t = dy_t * silu(z_t) (dy_t without a gate) and
+ *   lam_t[n] = ds_t C_t[n] + Abar_{t+1}[n] lam_{t+1}[n],  lam_L = 0,
+ *   du_t      = ds_t D[d] + Delta_t sum_n lam_t[n] B_t[n]
+ *   ddelta_t  = sigmoid(delta_t + dt_bias[d]) * sum_n lam_t[n] (Abar_t[n] h_{t-1}[n] A[d,n] + B_t[n] u_t)
+ *               (without the sigmoid factor when softplus is off)
+ *   dz_t      = dy_t * (sum_n C_t[n] h_t[n] + D[d] u_t) * silu'(z_t)
+ *   dA[d,n]   = sum over b, t of lam_t[n] Abar_t[n] h_{t-1}[n] Delta_t
+ *   dB_t[n]   = sum over d of lam_t[n] Delta_t u_t      dC_t[n] = sum over d of ds_t h_t[n]
+ *   dD[d]     = sum over b, t of ds_t u_t               ddt_bias[d] = sum over b, t of ddelta_t
+ *   dinitial_state = Abar_0 lam_0
+ *
+ *   u, delta, A, B, C, D, z, dt_bias, softplus, initial_state : the forward call's inputs,
+ *                 as for selective_scan_fwd_resume (initial_state NULL = zeros)
+ *   dy          : [batch, dim, seqlen] (dtype)
+ *   du, ddelta  : [batch, dim, seqlen] (dtype) outputs
+ *   dz          : [batch, dim, seqlen] (dtype) output, required when z is given; not written
+ *                 (and may be NULL) without z
+ *   dB, dC      : [batch, dstate, seqlen] (dtype) outputs
+ *   dA          : [dim, dstate] fp32 output
+ *   dD, ddt_bias: [dim] fp32 outputs; NULL = not computed (they are computed whether or not
+ *                 D / dt_bias is given: the gradient at zero)
+ *   dinitial_state : [batch, dim, dstate] fp32 output; NULL = not computed
+ * Sums over channels, batch rows and time are reduced in a fixed order: the result is
+ * deterministic.  Every output must not overlap an input or another output.  seqlen == 0
+ * writes zeros to dA, dD, ddt_bias and dinitial_state.  Required: u, delta, A, B, C, dy,
+ * du, ddelta, dA, dB, dC (all but A and dA may be NULL when seqlen == 0).  Scratch memory
+ * from the library's pool: about (4 * dstate / T + 1) * 4 bytes per (batch, dim, step),
+ * T = 16, 8, 2, 1 steps per chunk for dstate <= 8, 16, 32, 64, plus the per-channel-group
+ * partials of dB and dC.  Errors as for selective_scan_fwd.
+ */
+int selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus,
+                       const float* initial_state, const void* dy, void* du, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, void* dz, float* ddt_bias, float* dinitial_state, int64_t batch,
+                       int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
+
+/*
  * One decode step for `batch` independent requests, state updated IN PLACE.
  *
  *   state       : [batch, dim, dstate] fp32, read as h_{t-1} and overwritten with h_t
@@ -186,7 +228,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -17,8 +17,8 @@ import os
 
 import torch
 
-__all__ = ["load", "lib_path", "scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
-           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+__all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
+           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,7 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
 
 
@@ -54,6 +54,9 @@ def load():
         lib.selective_scan_fwd.restype = I
         lib.selective_scan_fwd_resume.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I, P]
         lib.selective_scan_fwd_resume.restype = I
+        lib.selective_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I64, I64,
+                                           I64, I64, I, P]
+        lib.selective_scan_bwd.restype = I
         lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.selective_state_update.restype = I
         lib.causal_conv1d_fwd.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
@@ -130,6 +133,10 @@ def selective_scan_fwd_resume(*args) -> int:
     return int(load().selective_scan_fwd_resume(*args))
 
 
+def selective_scan_bwd(*args) -> int:
+    return int(load().selective_scan_bwd(*args))
+
+
 def selective_state_update(*args) -> int:
     return int(load().selective_state_update(*args))
 
@@ -181,6 +188,43 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
                                     L, _dtype_code(u), _stream(dev))
     _check(rc)
     return y, last_state
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, dy=None,
+             initial_state=None, need_dD: bool = True, need_ddt_bias: bool = True,
+             need_dinitial_state: bool = True) -> dict:
+    """Gradients of sum(dy * y) for the forward scan with the same inputs (states are
+    recomputed).  Returns a dict: du, ddelta, dz (None without z) [batch, dim, L] and dB, dC
+    [batch, N, L] in the dtype of u; dA [dim, N], dD, ddt_bias [dim] and dinitial_state
+    [batch, dim, N] in fp32 (None when not requested)."""
+    lib = load()
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    dev = u.device
+    dt = u.dtype
+    for t, name, shape in ((u, "u", (batch, dim, L)), (delta, "delta", (batch, dim, L)), (z, "z", (batch, dim, L)),
+                           (dy, "dy", (batch, dim, L)), (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+        _require(t, name, shape, dt, dev)
+    if dy is None:
+        raise ValueError("dy is required")
+    _require(A, "A", (dim, N), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (dim,), torch.float32, dev)
+    _require(initial_state, "initial_state", (batch, dim, N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dz": torch.empty_like(u) if z is not None else None,
+         "dA": torch.empty((dim, N), **f32), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+         "dD": torch.empty((dim,), **f32) if need_dD else None,
+         "ddt_bias": torch.empty((dim,), **f32) if need_ddt_bias else None,
+         "dinitial_state": torch.empty((batch, dim, N), **f32) if need_dinitial_state else None}
+    _check(lib.selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                  1 if softplus else 0, _ptr(initial_state), _ptr(dy), _ptr(g["du"]),
+                                  _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                                  _ptr(g["dz"]), _ptr(g["ddt_bias"]), _ptr(g["dinitial_state"]), batch, dim, N, L,
+                                  _dtype_code(u), _stream(dev)))
+    return g
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, y=None):

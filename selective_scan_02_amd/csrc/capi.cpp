@@ -197,6 +197,78 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                    y, last_state, batch, dim, dstate, seqlen, dtype, stream);
 }
 
+int selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, int softplus,
+                       const float* initial_state, const void* dy, void* du, void* ddelta, float* dA, void* dB,
+                       void* dC, float* dD, void* dz, float* ddt_bias, float* dinitial_state, int64_t batch,
+                       int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream) {
+  g_last_error.clear();
+  if (seqlen != 0) {
+    if (!u) return fail(SSM_ERR_NULL_ARG, "u is NULL");
+    if (!delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
+    if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
+    if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
+    if (!dy) return fail(SSM_ERR_NULL_ARG, "dy is NULL");
+    if (!du) return fail(SSM_ERR_NULL_ARG, "du is NULL");
+    if (!ddelta) return fail(SSM_ERR_NULL_ARG, "ddelta is NULL");
+    if (!dB) return fail(SSM_ERR_NULL_ARG, "dB is NULL");
+    if (!dC) return fail(SSM_ERR_NULL_ARG, "dC is NULL");
+    if (z && !dz) return fail(SSM_ERR_NULL_ARG, "dz is NULL while z is given");
+  }
+  if (!A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+  if (!dA) return fail(SSM_ERR_NULL_ARG, "dA is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld dstate=%lld seqlen=%lld", (long long)batch,
+                (long long)dim, (long long)dstate, (long long)seqlen);
+  if (too_big(batch, dim, seqlen) || too_big(batch, dstate, seqlen) || too_big(batch, dim, dstate) ||
+      batch * ((dim + 63) / 64) > 0x7fffffffLL)
+    return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (!ssm::dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
+  if (!z) dz = nullptr;  // not written without a gate
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim * seqlen, nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
+  const Range ins[] = {{"u", u, nx * es, es},
+                       {"delta", delta, nx * es, es},
+                       {"z", z, nx * es, es},
+                       {"dy", dy, nx * es, es},
+                       {"B", B, nbc * es, es},
+                       {"C", C, nbc * es, es},
+                       {"A", A, (uint64_t)dim * dstate * 4, 4},
+                       {"D", D, (uint64_t)dim * 4, 4},
+                       {"dt_bias", dt_bias, (uint64_t)dim * 4, 4},
+                       {"initial_state", initial_state, nst, 4}};
+  const Range outs[] = {{"du", du, nx * es, es},
+                        {"ddelta", ddelta, nx * es, es},
+                        {"dz", dz, nx * es, es},
+                        {"dB", dB, nbc * es, es},
+                        {"dC", dC, nbc * es, es},
+                        {"dA", dA, (uint64_t)dim * dstate * 4, 4},
+                        {"dD", dD, (uint64_t)dim * 4, 4},
+                        {"ddt_bias", ddt_bias, (uint64_t)dim * 4, 4},
+                        {"dinitial_state", dinitial_state, nst, 4}};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  for (const Range& r : outs)
+    if (int rc = check_aligned(r)) return rc;
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, r.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  ssm::BwdParams p{};
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
+  p.softplus = softplus; p.h0 = initial_state; p.dy = dy;
+  p.du = du; p.ddelta = ddelta; p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.dz = dz; p.ddt_bias = ddt_bias;
+  p.dh0 = dinitial_state;
+  p.batch = batch; p.dim = dim; p.dstate = dstate; p.seqlen = seqlen; p.dtype = dtype;
+  return hip_status(ssm::launch_scan_bwd(p, (hipStream_t)stream), "selective_scan_bwd launch");
+}
+
 int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
                            const void* C, const float* D, const void* z, const float* dt_bias, void* y,
                            int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream) {

@@ -1,0 +1,527 @@
+// scan_bwd.hip -- backward of the selective scan on gfx950: the gradients of a scalar
+// loss through y, given dy = dLoss/dy.
+//
+// The pages describe the forward scan and note that the fused kernel recomputes the
+// intermediate states in the backward pass instead of storing them (Mamba summary
+// (junchaoiu.github.io), 方法 step 2: hardware-aware algorithm, recomputation; mlqm.cn
+// tutorial §6).  The gradients themselves follow from the recurrence by the adjoint
+// (reverse-mode) method; with ds_t = dy_t * silu(z_t) and the adjoint
+//   lam_t[n] = ds_t C_t[n] + Abar_{t+1}[n] lam_{t+1}[n]          (lam_L = 0)
+// they are
+//   du_t     = ds_t D + Delta_t sum_n lam_t[n] B_t[n]
+//   dDelta_t = sum_n lam_t[n] (Abar_t[n] h_{t-1}[n] A[n] + B_t[n] u_t)
+//   ddelta_t = dDelta_t * sigmoid(delta_t + dt_bias)  (softplus on; else dDelta_t)
+//   dz_t     = dy_t s_t silu'(z_t),  s_t = sum_n C_t[n] h_t[n] + D u_t
+//   dA[n]   += lam_t[n] Abar_t[n] h_{t-1}[n] Delta_t   dD += ds_t u_t   ddt_bias += ddelta_t
+//   dB_t[n]  = sum over channels of lam_t[n] Delta_t u_t
+//   dC_t[n]  = sum over channels of ds_t h_t[n]
+//   dh_{-1}  = Abar_0 lam_0.
+//
+// Work decomposition (one wave = 64 consecutive channels of one batch row, one channel
+// per lane, all dstate states in registers, as in the generic forward kernels):
+//   1. checkpoint pass: each sequence segment runs the forward recurrence from h = 0 and
+//      stores its state (and running sum of Delta) at the start of every chunk of T
+//      steps, plus the segment's end state and total sum of Delta;
+//   2. carry pass: the segment end states become each segment's incoming state (the
+//      same combination as the forward's segment carry);
+//   3. adjoint aggregate pass and reverse carry (only with several segments): each
+//      segment but the first runs the adjoint from zero, right to left; a reverse carry
+//      turns these into the adjoint entering each segment from its right.  The adjoint
+//      recurrence is linear, so a segment's contribution combines as
+//      Abar-product * incoming + local, the product being exp(A * sum Delta);
+//   4. main pass: each segment walks its chunks right to left.  A chunk's starting state
+//      is local checkpoint + exp(A * local sum Delta) * segment incoming state; the chunk
+//      reruns the forward over its T steps keeping every h_{t-1} in registers, then runs
+//      the adjoint back over them.  Per-channel gradients are written directly; the
+//      sums over channels (dB, dC) are reduced across the wave's 64 lanes through LDS
+//      and written as one partial per (channel group, batch row, n, t); the sums over
+//      time and batch (dA, dD, ddt_bias) are kept per (segment, channel);
+//   5. reduction passes: partials are summed in a fixed order (deterministic).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kWave = 64;
+
+// Steps per chunk: the chunk's h_{t-1} for every state stays in registers (T * N of them).
+template <int N>
+struct Chunk {
+  static constexpr int T = N <= 8 ? 16 : N == 16 ? 8 : N == 32 ? 2 : 1;
+};
+
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  const void* dy;
+  void* du;
+  void* ddelta;
+  void* dz;
+  float* dh0;
+  float* ck_h;    // [chunks, chans, N]  local state at each chunk start (segment-relative)
+  float* ck_dt;   // [chunks, chans]     local sum of Delta before each chunk
+  float* seg_h;   // [S, chans, N]       segment end state from 0, then incoming state
+  float* seg_dt;  // [S, chans]          sum of Delta over the segment
+  float* seg_l;   // [S, chans, N]       adjoint aggregate, then adjoint entering from the right
+  float* pB;      // [groups, batch, N, L]  dB summed over one channel group
+  float* pC;      // [groups, batch, N, L]
+  float* pA;      // [S, chans, N]
+  float* pD;      // [S, chans]
+  float* pbias;   // [S, chans]
+  int64_t batch, dim, seqlen, seg_len, chans;
+  int groups, nseg, softplus;
+};
+
+struct Lane {
+  int lane;
+  int64_t b, d, dd, ch;
+  bool active;
+};
+
+__device__ __forceinline__ Lane lane_of(const BwdArgs& a) {
+  Lane l;
+  l.lane = threadIdx.x;
+  l.b = blockIdx.x / a.groups;
+  l.d = (int64_t)(blockIdx.x % a.groups) * kWave + l.lane;
+  l.active = l.d < a.dim;
+  l.dd = l.active ? l.d : a.dim - 1;
+  l.ch = l.b * a.dim + l.dd;
+  return l;
+}
+
+__device__ __forceinline__ float step_size(float x, int sp) { return sp ? softplus(x) : x; }
+
+// sigmoid(x) = 1 / (1 + e^-x); e^-x = inf for x << 0 gives 0.
+__device__ __forceinline__ float sigmoid(float x) { return rcp(1.0f + ex2(-x * kLog2e)); }
+
+// 1. Checkpoint pass.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void bwd_checkpoint_kernel(BwdArgs a) {
+  constexpr int CT = Chunk<N>::T;
+  const Lane l = lane_of(a);
+  const int seg = blockIdx.y;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const T* __restrict__ u = (const T*)a.u + l.ch * L;
+  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
+  const T* __restrict__ Bp = (const T*)a.B + l.b * N * L;
+  float A2[N], h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    A2[n] = a.A[l.dd * N + n] * kLog2e;
+    h[n] = 0.0f;
+  }
+  const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  float cum = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t > t0 && (t - t0) % CT == 0 && l.active) {
+      const int64_t kg = t / CT;
+#pragma unroll
+      for (int n = 0; n < N; ++n) a.ck_h[(kg * a.chans + l.ch) * N + n] = h[n];
+      a.ck_dt[kg * a.chans + l.ch] = cum;
+    }
+    const float dt = step_size(ld(dl, t) + bias, a.softplus);
+    const float du = dt * ld(u, t);
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(ex2(dt * A2[n]), h[n], du * ld(Bp, (int64_t)n * L + t));
+    cum += dt;
+  }
+  if (!l.active) return;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.seg_h[((int64_t)seg * a.chans + l.ch) * N + n] = h[n];
+  a.seg_dt[(int64_t)seg * a.chans + l.ch] = cum;
+}
+
+// 2. Forward carry, one thread per (channel, n), in place over seg_h.
+__global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* seg_h, const float* seg_dt, const float* A,
+                                                            const float* h0, int64_t chans, int64_t dim, int N,
+                                                            int nseg) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= chans * N) return;
+  const int64_t ch = i / N;
+  const float A2 = A[(ch % dim) * N + (i % N)] * kLog2e;
+  float h = h0 ? h0[i] : 0.0f;
+  for (int s = 0; s < nseg; ++s) {
+    const int64_t k = (int64_t)s * chans * N + i;
+    const float agg = seg_h[k];
+    seg_h[k] = h;
+    h = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + ch]), h, agg);
+  }
+}
+
+// 3a. Adjoint aggregate of segments 1 .. S-1 (blockIdx.y + 1): the adjoint from zero at the
+// segment's right end, carried through the segment's first transition, Abar_{t0} lam_{t0}.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void bwd_adjoint_aggregate_kernel(BwdArgs a) {
+  const Lane l = lane_of(a);
+  const int seg = blockIdx.y + 1;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
+  const T* __restrict__ dy = (const T*)a.dy + l.ch * L;
+  const T* __restrict__ zz = a.z ? (const T*)a.z + l.ch * L : nullptr;
+  const T* __restrict__ Cp = (const T*)a.C + l.b * N * L;
+  float A2[N], lam[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    A2[n] = a.A[l.dd * N + n] * kLog2e;
+    lam[n] = 0.0f;
+  }
+  const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    const float dt = step_size(ld(dl, t) + bias, a.softplus);
+    float ds = ld(dy, t);
+    if (zz) ds *= silu(ld(zz, t));
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      lam[n] = ex2(dt * A2[n]) * __builtin_fmaf(ds, ld(Cp, (int64_t)n * L + t), lam[n]);
+  }
+  if (!l.active) return;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.seg_l[((int64_t)seg * a.chans + l.ch) * N + n] = lam[n];
+}
+
+// 3b. Reverse carry, one thread per (channel, n): seg_l[s] becomes the adjoint term that
+// enters segment s from the right (zero for the last segment).
+__global__ __launch_bounds__(256) void bwd_adjoint_carry_kernel(float* seg_l, const float* seg_dt, const float* A,
+                                                                int64_t chans, int64_t dim, int N, int nseg) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= chans * N) return;
+  const int64_t ch = i / N;
+  const float A2 = A[(ch % dim) * N + (i % N)] * kLog2e;
+  float mu = 0.0f;
+  for (int s = nseg - 1; s >= 0; --s) {
+    const int64_t k = (int64_t)s * chans * N + i;
+    const float local = s > 0 ? seg_l[k] : 0.0f;
+    seg_l[k] = mu;
+    mu = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + ch]), mu, local);
+  }
+}
+
+// Sum of v[n] over the wave's 64 lanes, for every n.  Each lane writes its N values into
+// red[n][lane]; lane (n = lane / P, part q = lane % P), P = 64 / N lanes per value, then
+// adds N consecutive entries of row n and the P parts are combined across lanes.  Every
+// lane of value n's group returns its sum.
+template <int N>
+__device__ __forceinline__ float wave_sum(const float (&v)[N], float* red) {
+  constexpr int P = kWave / N;
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int n = 0; n < N; ++n) red[n * kWave + lane] = v[n];
+  __syncthreads();
+  const float* row = red + (lane / P) * kWave + (lane % P) * N;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) s += row[i];
+#pragma unroll
+  for (int m = 1; m < P; m <<= 1) s += __shfl_xor(s, m);
+  __syncthreads();
+  return s;
+}
+
+// 4. Main pass: one wave per (channel group, batch row) and segment.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void bwd_main_kernel(BwdArgs a) {
+  constexpr int CT = Chunk<N>::T;
+  constexpr int P = kWave / N;
+  __shared__ float red[N * kWave];
+  const Lane l = lane_of(a);
+  const int seg = blockIdx.y;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const int64_t grp = blockIdx.x % a.groups;
+  const T* __restrict__ u = (const T*)a.u + l.ch * L;
+  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
+  const T* __restrict__ dy = (const T*)a.dy + l.ch * L;
+  const T* __restrict__ zz = a.z ? (const T*)a.z + l.ch * L : nullptr;
+  const T* __restrict__ Bp = (const T*)a.B + l.b * N * L;
+  const T* __restrict__ Cp = (const T*)a.C + l.b * N * L;
+  T* __restrict__ du_o = (T*)a.du + l.ch * L;
+  T* __restrict__ dl_o = (T*)a.ddelta + l.ch * L;
+  T* __restrict__ dz_o = a.z ? (T*)a.dz + l.ch * L : nullptr;
+  // this lane's slot in the reduced sums: value n_red, stored by the group's first lane
+  const int n_red = l.lane / P;
+  const bool red_store = (l.lane % P) == 0;
+  float* __restrict__ pB = a.pB + ((grp * a.batch + l.b) * N + n_red) * L;
+  float* __restrict__ pC = a.pC + ((grp * a.batch + l.b) * N + n_red) * L;
+
+  float A2[N], hin[N], lam[N], dA[N];
+  const bool multi = a.nseg > 1;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    A2[n] = a.A[l.dd * N + n] * kLog2e;
+    const int64_t k = ((int64_t)seg * a.chans + l.ch) * N + n;
+    hin[n] = multi ? a.seg_h[k] : (a.h0 ? a.h0[l.ch * N + n] : 0.0f);
+    lam[n] = (multi && l.active) ? a.seg_l[k] : 0.0f;
+    dA[n] = 0.0f;
+  }
+  const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  const float Dd = a.D ? a.D[l.dd] : 0.0f;
+  float accD = 0.0f, accbias = 0.0f;
+
+  const int nck = (int)((t1 - t0 + CT - 1) / CT);
+  for (int k = nck - 1; k >= 0; --k) {
+    const int64_t tc = t0 + (int64_t)k * CT;
+    const int tl = (int)std::min<int64_t>(CT, t1 - tc);
+    float h[N];
+    if (k == 0) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = hin[n];
+    } else {
+      const int64_t kg = tc / CT;
+      const float c = a.ck_dt[kg * a.chans + l.ch];
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        h[n] = __builtin_fmaf(ex2(A2[n] * c), hin[n], a.ck_h[(kg * a.chans + l.ch) * N + n]);
+    }
+    float hp[CT][N], dts[CT], us[CT], dss[CT], sgx[CT];
+    // forward over the chunk: states, readout, gate gradient, dC partials
+#pragma unroll
+    for (int i = 0; i < CT; ++i) {
+      if (i < tl) {
+        const int64_t t = tc + i;
+        const float x = ld(dl, t) + bias;
+        const float dt = step_size(x, a.softplus);
+        const float ut = ld(u, t);
+        const float dut = dt * ut;
+        float s = 0.0f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          hp[i][n] = h[n];
+          h[n] = __builtin_fmaf(ex2(dt * A2[n]), h[n], dut * ld(Bp, (int64_t)n * L + t));
+          s = __builtin_fmaf(ld(Cp, (int64_t)n * L + t), h[n], s);
+        }
+        s = __builtin_fmaf(Dd, ut, s);
+        const float g = ld(dy, t);
+        float ds = g;
+        if (zz) {
+          const float zv = ld(zz, t);
+          const float sg = sigmoid(zv);
+          ds = g * zv * sg;
+          if (l.active) st(dz_o, t, g * s * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f));
+        }
+        if (!l.active) ds = 0.0f;
+        dts[i] = dt;
+        us[i] = ut;
+        dss[i] = ds;
+        sgx[i] = a.softplus ? sigmoid(x) : 1.0f;
+        float v[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) v[n] = ds * h[n];
+        const float r = wave_sum<N>(v, red);
+        if (red_store) pC[t] = r;
+      }
+    }
+    // adjoint back over the chunk
+#pragma unroll
+    for (int i = CT - 1; i >= 0; --i) {
+      if (i < tl) {
+        const int64_t t = tc + i;
+        const float dt = dts[i], ut = us[i], ds = dss[i];
+        const float dut = dt * ut;
+        float accB = 0.0f, accQ = 0.0f, v[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const float lt = __builtin_fmaf(ds, ld(Cp, (int64_t)n * L + t), lam[n]);
+          accB = __builtin_fmaf(lt, ld(Bp, (int64_t)n * L + t), accB);
+          v[n] = lt * dut;
+          const float lp = ex2(dt * A2[n]) * lt;  // Abar_t lam_t, carried to step t-1
+          const float q = lp * hp[i][n];
+          accQ = __builtin_fmaf(q, A2[n], accQ);
+          dA[n] = __builtin_fmaf(q, dt, dA[n]);
+          lam[n] = lp;
+        }
+        const float r = wave_sum<N>(v, red);
+        if (red_store) pB[t] = r;
+        const float dDelta = __builtin_fmaf(accQ, kLn2, ut * accB);
+        const float ddl = dDelta * sgx[i];
+        if (l.active) {
+          st(du_o, t, __builtin_fmaf(dt, accB, ds * Dd));
+          st(dl_o, t, ddl);
+        }
+        accD = __builtin_fmaf(ds, ut, accD);
+        accbias += ddl;
+      }
+    }
+  }
+  if (!l.active) return;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.pA[((int64_t)seg * a.chans + l.ch) * N + n] = dA[n];
+  a.pD[(int64_t)seg * a.chans + l.ch] = accD;
+  a.pbias[(int64_t)seg * a.chans + l.ch] = accbias;
+  if (seg == 0 && a.dh0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) a.dh0[l.ch * N + n] = lam[n];
+  }
+}
+
+// 5a. dB, dC: sum of the channel-group partials, one thread per (batch row, n, t).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(const float* pB, const float* pC, T* dB, T* dC,
+                                                            int64_t count, int groups) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float sb = 0.0f, sc = 0.0f;
+  for (int g = 0; g < groups; ++g) {
+    sb += pB[(int64_t)g * count + i];
+    sc += pC[(int64_t)g * count + i];
+  }
+  st(dB, i, sb);
+  st(dC, i, sc);
+}
+
+// 5b. dA, dD, ddt_bias: sum over segments and batch rows, one thread per (d, n).
+__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(const float* pA, const float* pD, const float* pbias,
+                                                               float* dA, float* dD, float* dbias, int64_t batch,
+                                                               int64_t dim, int N, int nseg) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= dim * N) return;
+  const int64_t d = i / N;
+  const int n = (int)(i % N);
+  const int64_t chans = batch * dim;
+  float sa = 0.0f, sd = 0.0f, sb = 0.0f;
+  for (int s = 0; s < nseg; ++s)
+    for (int64_t b = 0; b < batch; ++b) {
+      const int64_t ch = (int64_t)s * chans + b * dim + d;
+      sa += pA[ch * N + n];
+      if (n == 0) {
+        sd += pD[ch];
+        sb += pbias[ch];
+      }
+    }
+  dA[i] = sa;
+  if (n == 0) {
+    if (dD) dD[d] = sd;
+    if (dbias) dbias[d] = sb;
+  }
+}
+
+// Zero-length sequence: every gradient is zero.  A fill kernel rather than a memset node.
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t s) {
+  if (!p || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+template <int N, typename T>
+hipError_t run(const BwdParams& p, hipStream_t stream) {
+  constexpr int CT = Chunk<N>::T;
+  BwdArgs a{};
+  a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
+  a.h0 = p.h0; a.dy = p.dy; a.du = p.du; a.ddelta = p.ddelta; a.dz = p.dz; a.dh0 = p.dh0;
+  a.batch = p.batch; a.dim = p.dim; a.seqlen = p.seqlen; a.softplus = p.softplus;
+  a.chans = p.batch * p.dim;
+  a.groups = (int)((p.dim + kWave - 1) / kWave);
+  const int64_t L = p.seqlen, chans = a.chans;
+  const int64_t waves = p.batch * a.groups;
+  // segments: enough waves for every SIMD twice over, each segment at least 4 chunks long
+  int64_t nseg = std::max<int64_t>(1, (4096 + waves - 1) / waves);
+  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, L / (4 * CT)));
+  int64_t seg_len = (L + nseg - 1) / nseg;
+  seg_len = (seg_len + CT - 1) / CT * CT;
+  nseg = (L + seg_len - 1) / seg_len;
+  a.seg_len = seg_len;
+  a.nseg = (int)nseg;
+  const int64_t nchunks = (L + CT - 1) / CT;
+  const size_t fl[] = {(size_t)(nchunks * chans * N), (size_t)(nchunks * chans), (size_t)(nseg * chans * N),
+                       (size_t)(nseg * chans), (size_t)(nseg * chans * N), (size_t)(a.groups * p.batch * N * L),
+                       (size_t)(a.groups * p.batch * N * L), (size_t)(nseg * chans * N), (size_t)(nseg * chans),
+                       (size_t)(nseg * chans)};
+  size_t total = 0;
+  for (size_t f : fl) total += (f + 63) / 64 * 64;  // 256-byte aligned pieces
+  void* scratch = nullptr;
+  hipError_t err = scratch_alloc(&scratch, total * sizeof(float), stream);
+  if (err != hipSuccess) return err;
+  float* q = (float*)scratch;
+  float** dst[] = {&a.ck_h, &a.ck_dt, &a.seg_h, &a.seg_dt, &a.seg_l, &a.pB, &a.pC, &a.pA, &a.pD, &a.pbias};
+  for (int i = 0; i < 10; ++i) {
+    *dst[i] = q;
+    q += (fl[i] + 63) / 64 * 64;
+  }
+  const dim3 grid((unsigned)waves, (unsigned)nseg);
+  hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+  err = hipGetLastError();
+  if (err == hipSuccess && nseg > 1) {
+    hipLaunchKernelGGL(bwd_fwd_carry_kernel, dim3(blocks_of(chans * N)), dim3(256), 0, stream, a.seg_h, a.seg_dt,
+                       p.A, p.h0, chans, p.dim, N, (int)nseg);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), dim3((unsigned)waves, (unsigned)(nseg - 1)),
+                         dim3(kWave), 0, stream, a);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL(bwd_adjoint_carry_kernel, dim3(blocks_of(chans * N)), dim3(256), 0, stream, a.seg_l,
+                         a.seg_dt, p.A, chans, p.dim, N, (int)nseg);
+      err = hipGetLastError();
+    }
+  }
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL((bwd_main_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess) {
+    const int64_t count = p.batch * N * L;
+    hipLaunchKernelGGL((bwd_bc_reduce_kernel<T>), dim3(blocks_of(count)), dim3(256), 0, stream, a.pB, a.pC,
+                       (T*)p.dB, (T*)p.dC, count, a.groups);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(blocks_of(p.dim * N)), dim3(256), 0, stream, a.pA, a.pD,
+                       a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)nseg);
+    err = hipGetLastError();
+  }
+  const hipError_t ferr = hipFreeAsync(scratch, stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+template <typename T>
+hipError_t dispatch_n(const BwdParams& p, hipStream_t s) {
+  switch (p.dstate) {
+    case 1: return run<1, T>(p, s);
+    case 2: return run<2, T>(p, s);
+    case 4: return run<4, T>(p, s);
+    case 8: return run<8, T>(p, s);
+    case 16: return run<16, T>(p, s);
+    case 32: return run<32, T>(p, s);
+    case 64: return run<64, T>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.seqlen == 0) {
+    hipError_t e = zero(p.dA, p.dim * p.dstate, stream);
+    if (e == hipSuccess) e = zero(p.dD, p.dim, stream);
+    if (e == hipSuccess) e = zero(p.ddt_bias, p.dim, stream);
+    if (e == hipSuccess) e = zero(p.dh0, p.batch * p.dim * p.dstate, stream);
+    return e;
+  }
+  return p.dtype == kBF16 ? dispatch_n<__bf16>(p, stream) : dispatch_n<float>(p, stream);
+}
+
+}  // namespace ssm

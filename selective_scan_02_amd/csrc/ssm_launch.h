@@ -63,6 +63,31 @@ struct ConvStepParams {
   int dtype;
 };
 
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* dt_bias;  // nullable
+  int softplus;
+  const float* h0;       // nullable initial state [batch, dim, dstate]
+  const void* dy;
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;             // nullable
+  void* dz;              // written when z is given
+  float* ddt_bias;       // nullable
+  float* dh0;            // nullable
+  int64_t batch, dim, dstate, seqlen;
+  int dtype;
+};
+
 struct ScanPlan {
   int mode;          // 0 intervals, 1 one pass, 2 aggregate/carry/output
   int64_t groups;    // channel groups of 64
@@ -82,6 +107,7 @@ hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dis
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment
 bool chunked_supported(const ScanParams& p);
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
+hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream);

@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_state_update", "causal_conv1d_fwd",
+    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update",
+                 "causal_conv1d_fwd",
                  "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
 
 
 def scan_args(**over):
@@ -236,3 +237,37 @@ def test_conv_validation(lib):
     assert u(*conv_step_args(width=7)) == UNSUPPORTED
     assert u(*conv_step_args(out=addr(1) + 4)) == ALIAS             # out inside the state
     assert u(*conv_step_args(state=addr(3))) == ALIAS               # state overlapping the weights
+
+
+BWD_FIELDS = ("u", "delta", "A", "B", "C", "D", "z", "dt_bias", "softplus", "h0", "dy", "du", "ddelta", "dA", "dB",
+              "dC", "dD", "dz", "ddt_bias", "dh0", "batch", "dim", "dstate", "seqlen", "dtype", "stream")
+
+
+def bwd_args(**over):
+    a = dict(zip(BWD_FIELDS[:8], [addr(i) for i in range(1, 9)]))
+    a.update(softplus=1, h0=addr(9), dy=addr(10), du=addr(11), ddelta=addr(12), dA=addr(13), dB=addr(14),
+             dC=addr(15), dD=addr(16), dz=addr(17), ddt_bias=addr(18), dh0=addr(19), batch=2, dim=64, dstate=16,
+             seqlen=128, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in BWD_FIELDS]
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "dy", "du", "ddelta", "dA", "dB", "dC", "dz"])
+def test_bwd_null_required(lib, field):
+    assert lib.selective_scan_bwd(*bwd_args(**{field: None})) == NULL_ARG
+    assert field in ssm.last_error()
+
+
+def test_bwd_validation(lib):
+    assert lib.selective_scan_bwd(*bwd_args(dtype=3)) == BAD_DTYPE
+    assert lib.selective_scan_bwd(*bwd_args(dstate=12)) == UNSUPPORTED
+    assert lib.selective_scan_bwd(*bwd_args(batch=0)) == BAD_SHAPE
+    assert lib.selective_scan_bwd(*bwd_args(softplus=5)) == BAD_SHAPE
+    assert lib.selective_scan_bwd(*bwd_args(dy=addr(10) + 1)) == MISALIGNED
+    assert lib.selective_scan_bwd(*bwd_args(dA=addr(13) + 2)) == MISALIGNED
+    # outputs may overlap neither an input nor each other
+    assert lib.selective_scan_bwd(*bwd_args(du=addr(10) + 64)) == ALIAS
+    assert lib.selective_scan_bwd(*bwd_args(dC=addr(14) + 64)) == ALIAS
+    assert lib.selective_scan_bwd(*bwd_args(dh0=addr(9))) == ALIAS
+    assert lib.selective_scan_bwd(*bwd_args(dD=addr(13) + 4)) == ALIAS
+    assert "overlaps" in ssm.last_error()
