@@ -417,6 +417,392 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
   if (i < n) p[i] = 0.0f;
 }
 
+// ---------------------------------------------------------------- fast path
+// Rows that are whole 16-byte pieces (seqlen a multiple of 8, 16-byte aligned tensors) and
+// dstate in {8, 16, 32, 64}.  Each lane moves the 8 steps of its channel's chunk with one or
+// two 16-byte loads and stores; B and C are staged per chunk in LDS and read back as
+// broadcasts.  The main pass splits the states over N/8 waves of 8 states each (a workgroup
+// per channel group), which halves the registers a lane needs for the chunk's states; the
+// per-channel sums over n are combined across the waves through LDS.
+#ifndef SSM_BWD_WAVES_PER_SIMD
+#define SSM_BWD_WAVES_PER_SIMD 1
+#endif
+constexpr int kCT = 8;   // steps per chunk
+constexpr int kSPW = 8;  // states per wave in the main pass
+
+template <typename T>
+struct Row8;
+template <>
+struct Row8<__bf16> {
+  static __device__ __forceinline__ void load(const __bf16* p, float (&v)[8]) {
+    const uint4 r = *(const uint4*)p;
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(__bf16* p, const float (&v)[8]) {
+    __bf16 t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = (__bf16)v[i];
+    uint4 r;
+    __builtin_memcpy(&r, t, sizeof r);
+    *(uint4*)p = r;
+  }
+};
+template <>
+struct Row8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
+    ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// Cross-lane sums without LDS.  v_permlane32_swap exchanges lanes 32..63 of its first operand
+// with lanes 0..31 of its second, v_permlane16_swap the odd 16-lane rows of the first with the
+// even rows of the second; adding the two swapped registers halves the lanes a sum spans.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of v[j] over the 64 lanes for j = 0..7, as a reduce-scatter: two swaps fold the halves
+// and the rows, a select plus a row rotation by 8 folds the half-rows, and three DPP adds
+// (half-row mirror, quad swaps by 2 and by 1) finish inside groups of 8 lanes.  Lane l ends
+// with the sum of v[j], j = 4 * bit3(l) + 2 * bit4(l) + bit5(l).
+__device__ __forceinline__ int reduce8_index(int lane) {
+  return ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1);
+}
+__device__ __forceinline__ float reduce8(const float (&v)[8], bool hi8) {
+  const float x0 = swap_sum32(v[0], v[1]), x1 = swap_sum32(v[2], v[3]);
+  const float x2 = swap_sum32(v[4], v[5]), x3 = swap_sum32(v[6], v[7]);
+  const float y0 = swap_sum16(x0, x1), y1 = swap_sum16(x2, x3);
+  const float keep = hi8 ? y1 : y0, send = hi8 ? y0 : y1;
+  float z = keep + dpp<0x128>(send);  // row_ror:8
+  z += dpp<0x141>(z);                 // row_half_mirror
+  z += dpp<0x4E>(z);                  // quad_perm [2,3,0,1]
+  z += dpp<0xB1>(z);                  // quad_perm [1,0,3,2]
+  return z;
+}
+
+// 1'. Checkpoint pass, 16-byte rows.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
+  __shared__ __align__(16) float sB[kCT][N];
+  const Lane l = lane_of(a);
+  const int seg = blockIdx.y;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const T* __restrict__ u = (const T*)a.u + l.ch * L;
+  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
+  const T* __restrict__ Bp = (const T*)a.B + l.b * N * L;
+  float A2[N], h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    A2[n] = a.A[l.dd * N + n] * kLog2e;
+    h[n] = 0.0f;
+  }
+  const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  float cum = 0.0f;
+  for (int64_t tc = t0; tc < t1; tc += kCT) {
+    if (tc > t0 && l.active) {
+      const int64_t kg = tc / kCT;
+      float4* ck = (float4*)(a.ck_h + (kg * a.chans + l.ch) * N);
+#pragma unroll
+      for (int n = 0; n < N; n += 4) ck[n / 4] = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+      a.ck_dt[kg * a.chans + l.ch] = cum;
+    }
+    float uv[kCT], dv[kCT];
+    Row8<T>::load(u + tc, uv);
+    Row8<T>::load(dl + tc, dv);
+    if (l.lane < N) {
+      float bv[kCT];
+      Row8<T>::load(Bp + (int64_t)l.lane * L + tc, bv);
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) sB[i][l.lane] = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      const float dt = step_size(dv[i] + bias, a.softplus);
+      const float du = dt * uv[i];
+      const float4* br = (const float4*)sB[i];
+#pragma unroll
+      for (int n = 0; n < N; n += 4) {
+        const float4 bq = br[n / 4];
+        h[n] = __builtin_fmaf(ex2(dt * A2[n]), h[n], du * bq.x);
+        h[n + 1] = __builtin_fmaf(ex2(dt * A2[n + 1]), h[n + 1], du * bq.y);
+        h[n + 2] = __builtin_fmaf(ex2(dt * A2[n + 2]), h[n + 2], du * bq.z);
+        h[n + 3] = __builtin_fmaf(ex2(dt * A2[n + 3]), h[n + 3], du * bq.w);
+      }
+      cum += dt;
+    }
+    __syncthreads();
+  }
+  if (!l.active) return;
+  float4* sh = (float4*)(a.seg_h + ((int64_t)seg * a.chans + l.ch) * N);
+#pragma unroll
+  for (int n = 0; n < N; n += 4) sh[n / 4] = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
+  a.seg_dt[(int64_t)seg * a.chans + l.ch] = cum;
+}
+
+// 3a'. Adjoint aggregate, 16-byte rows.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a) {
+  __shared__ __align__(16) float sC[kCT][N];
+  const Lane l = lane_of(a);
+  const int seg = blockIdx.y + 1;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
+  const T* __restrict__ dy = (const T*)a.dy + l.ch * L;
+  const T* __restrict__ zz = a.z ? (const T*)a.z + l.ch * L : nullptr;
+  const T* __restrict__ Cp = (const T*)a.C + l.b * N * L;
+  float A2[N], lam[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    A2[n] = a.A[l.dd * N + n] * kLog2e;
+    lam[n] = 0.0f;
+  }
+  const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
+    float dv[kCT], gv[kCT], zv[kCT];
+    Row8<T>::load(dl + tc, dv);
+    Row8<T>::load(dy + tc, gv);
+    if (zz) Row8<T>::load(zz + tc, zv);
+    if (l.lane < N) {
+      float cv[kCT];
+      Row8<T>::load(Cp + (int64_t)l.lane * L + tc, cv);
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) sC[i][l.lane] = cv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = kCT - 1; i >= 0; --i) {
+      const float dt = step_size(dv[i] + bias, a.softplus);
+      const float ds = zz ? gv[i] * silu(zv[i]) : gv[i];
+      const float4* cr = (const float4*)sC[i];
+#pragma unroll
+      for (int n = 0; n < N; n += 4) {
+        const float4 cq = cr[n / 4];
+        lam[n] = ex2(dt * A2[n]) * __builtin_fmaf(ds, cq.x, lam[n]);
+        lam[n + 1] = ex2(dt * A2[n + 1]) * __builtin_fmaf(ds, cq.y, lam[n + 1]);
+        lam[n + 2] = ex2(dt * A2[n + 2]) * __builtin_fmaf(ds, cq.z, lam[n + 2]);
+        lam[n + 3] = ex2(dt * A2[n + 3]) * __builtin_fmaf(ds, cq.w, lam[n + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  if (!l.active) return;
+  float4* sl = (float4*)(a.seg_l + ((int64_t)seg * a.chans + l.ch) * N);
+#pragma unroll
+  for (int n = 0; n < N; n += 4) sl[n / 4] = make_float4(lam[n], lam[n + 1], lam[n + 2], lam[n + 3]);
+}
+
+// 4'. Main pass, 16-byte rows: a workgroup of N/8 waves per (channel group, batch row) and
+// segment; wave w holds states 8w .. 8w+7 of the group's 64 channels.  Per chunk: stage B and
+// C; rerun the forward keeping h_{t-1} (readout partials to LDS, dC partials reduced across
+// lanes); wave 0 writes dz; run the adjoint back (partials of sum lam B and sum q A to LDS,
+// dB partials); the last wave writes du and ddelta.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fbwd_main_kernel(BwdArgs a) {
+  constexpr int W = N / kSPW;
+  __shared__ __align__(16) float sBC[W][2][kCT][kSPW];
+  __shared__ float sS[W][kCT][kWave];
+  __shared__ float sP[W][2][kCT][kWave];
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t b = blockIdx.x / a.groups;
+  const int64_t grp = blockIdx.x % a.groups;
+  const int64_t d = grp * kWave + lane;
+  const bool active = d < a.dim;
+  const int64_t dd = active ? d : a.dim - 1;
+  const int64_t ch = b * a.dim + dd;
+  const int seg = blockIdx.y;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const int n0 = w * kSPW;
+  const T* __restrict__ u = (const T*)a.u + ch * L;
+  const T* __restrict__ dl = (const T*)a.delta + ch * L;
+  const T* __restrict__ dy = (const T*)a.dy + ch * L;
+  const T* __restrict__ zz = a.z ? (const T*)a.z + ch * L : nullptr;
+  const T* __restrict__ Bp = (const T*)a.B + b * N * L;
+  const T* __restrict__ Cp = (const T*)a.C + b * N * L;
+  const int jr = reduce8_index(lane);
+  const bool hi8 = (lane & 8) != 0;
+  float* __restrict__ pB = a.pB + ((grp * a.batch + b) * N + n0 + jr) * L + (lane & 7);
+  float* __restrict__ pC = a.pC + ((grp * a.batch + b) * N + n0 + jr) * L + (lane & 7);
+
+  float A2[kSPW], hin[kSPW], lam[kSPW], dA[kSPW];
+  const bool multi = a.nseg > 1;
+  {
+    const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+#pragma unroll
+    for (int j = 0; j < kSPW; ++j) {
+      A2[j] = a.A[dd * N + n0 + j] * kLog2e;
+      hin[j] = multi ? a.seg_h[k + j] : (a.h0 ? a.h0[ch * N + n0 + j] : 0.0f);
+      lam[j] = (multi && active) ? a.seg_l[k + j] : 0.0f;
+      dA[j] = 0.0f;
+    }
+  }
+  const float bias = a.dt_bias ? a.dt_bias[dd] : 0.0f;
+  const float Dd = a.D ? a.D[dd] : 0.0f;
+  float accD = 0.0f, accbias = 0.0f;
+
+  for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
+    float h[kSPW];
+    if (tc == t0) {
+#pragma unroll
+      for (int j = 0; j < kSPW; ++j) h[j] = hin[j];
+    } else {
+      const int64_t kg = tc / kCT;
+      const float c = a.ck_dt[kg * a.chans + ch];
+      const float4* ck = (const float4*)(a.ck_h + (kg * a.chans + ch) * N + n0);
+      const float4 c0 = ck[0], c1 = ck[1];
+      const float cv[kSPW] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int j = 0; j < kSPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * c), hin[j], cv[j]);
+    }
+    float uv[kCT], dv[kCT], gv[kCT], zv[kCT];
+    Row8<T>::load(u + tc, uv);
+    Row8<T>::load(dl + tc, dv);
+    Row8<T>::load(dy + tc, gv);
+    if (zz) Row8<T>::load(zz + tc, zv);
+    if (lane < 2 * kSPW) {
+      const T* src = (lane < kSPW ? Bp : Cp) + (int64_t)(n0 + (lane & 7)) * L + tc;
+      float bv[kCT];
+      Row8<T>::load(src, bv);
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) sBC[w][lane >> 3][i][lane & 7] = bv[i];
+    }
+    float dt[kCT], dut[kCT], ds[kCT];
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      dt[i] = step_size(dv[i] + bias, a.softplus);
+      dut[i] = dt[i] * uv[i];
+      ds[i] = zz ? gv[i] * silu(zv[i]) : gv[i];
+      if (!active) ds[i] = 0.0f;
+    }
+    __syncthreads();
+    // forward over the chunk
+    float hp[kCT][kSPW];
+    float keepC = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      const float4* br = (const float4*)sBC[w][0][i];
+      const float4* cr = (const float4*)sBC[w][1][i];
+      const float4 b0 = br[0], b1 = br[1], c0 = cr[0], c1 = cr[1];
+      const float Bv[kSPW] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float Cv[kSPW] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float s = 0.0f, v[kSPW];
+#pragma unroll
+      for (int j = 0; j < kSPW; ++j) {
+        hp[i][j] = h[j];
+        h[j] = __builtin_fmaf(ex2(dt[i] * A2[j]), h[j], dut[i] * Bv[j]);
+        s = __builtin_fmaf(Cv[j], h[j], s);
+        v[j] = ds[i] * h[j];
+      }
+      sS[w][i][lane] = s;
+      const float r = reduce8(v, hi8);
+      if ((lane & 7) == i) keepC = r;
+    }
+    pC[tc] = keepC;
+    __syncthreads();
+    if (w == 0 && zz) {
+      float out[kCT];
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) {
+        float s = Dd * uv[i];
+#pragma unroll
+        for (int q = 0; q < W; ++q) s += sS[q][i][lane];
+        const float sg = sigmoid(zv[i]);
+        out[i] = gv[i] * s * sg * __builtin_fmaf(zv[i], 1.0f - sg, 1.0f);
+      }
+      if (active) Row8<T>::store((T*)a.dz + ch * L + tc, out);
+    }
+    // adjoint back over the chunk
+    float keepB = 0.0f;
+#pragma unroll
+    for (int i = kCT - 1; i >= 0; --i) {
+      const float4* br = (const float4*)sBC[w][0][i];
+      const float4* cr = (const float4*)sBC[w][1][i];
+      const float4 b0 = br[0], b1 = br[1], c0 = cr[0], c1 = cr[1];
+      const float Bv[kSPW] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const float Cv[kSPW] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float accB = 0.0f, accQ = 0.0f, v[kSPW];
+#pragma unroll
+      for (int j = 0; j < kSPW; ++j) {
+        const float lt = __builtin_fmaf(ds[i], Cv[j], lam[j]);
+        accB = __builtin_fmaf(lt, Bv[j], accB);
+        v[j] = lt * dut[i];
+        const float lp = ex2(dt[i] * A2[j]) * lt;
+        const float q = lp * hp[i][j];
+        accQ = __builtin_fmaf(q, A2[j], accQ);
+        dA[j] = __builtin_fmaf(q, dt[i], dA[j]);
+        lam[j] = lp;
+      }
+      sP[w][0][i][lane] = accB;
+      sP[w][1][i][lane] = accQ;
+      const float r = reduce8(v, hi8);
+      if ((lane & 7) == i) keepB = r;
+    }
+    pB[tc] = keepB;
+    __syncthreads();
+    if (w == W - 1) {
+      float o_du[kCT], o_dl[kCT];
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) {
+        float sb = 0.0f, sq = 0.0f;
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          sb += sP[q][0][i][lane];
+          sq += sP[q][1][i][lane];
+        }
+        o_du[i] = __builtin_fmaf(dt[i], sb, ds[i] * Dd);
+        const float dDelta = __builtin_fmaf(sq, kLn2, uv[i] * sb);
+        o_dl[i] = a.softplus ? dDelta * sigmoid(dv[i] + bias) : dDelta;
+        accD = __builtin_fmaf(ds[i], uv[i], accD);
+        accbias += o_dl[i];
+      }
+      if (active) {
+        Row8<T>::store((T*)a.du + ch * L + tc, o_du);
+        Row8<T>::store((T*)a.ddelta + ch * L + tc, o_dl);
+      }
+    }
+  }
+  if (!active) return;
+  {
+    const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+#pragma unroll
+    for (int j = 0; j < kSPW; ++j) a.pA[k + j] = dA[j];
+    if (seg == 0 && a.dh0) {
+#pragma unroll
+      for (int j = 0; j < kSPW; ++j) a.dh0[ch * N + n0 + j] = lam[j];
+    }
+  }
+  if (w == W - 1) {
+    a.pD[(int64_t)seg * a.chans + ch] = accD;
+    a.pbias[(int64_t)seg * a.chans + ch] = accbias;
+  }
+}
+
 hipError_t zero(float* p, int64_t n, hipStream_t s) {
   if (!p || n == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
@@ -425,9 +811,21 @@ hipError_t zero(float* p, int64_t n, hipStream_t s) {
 
 unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-template <int N, typename T>
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The fast kernels need whole chunks of 8 steps in 16-byte pieces and at least 8 states.
+bool fast_ok(const BwdParams& p) {
+  if (p.dstate < kSPW || p.seqlen % kCT != 0) return false;
+  const void* ptrs[] = {p.u, p.delta, p.z, p.dy, p.du, p.ddelta, p.dz, p.B, p.C};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return false;
+  return true;
+}
+
+template <int N, typename T, bool FAST>
 hipError_t run(const BwdParams& p, hipStream_t stream) {
-  constexpr int CT = Chunk<N>::T;
+  constexpr int CT = FAST ? kCT : Chunk<N>::T;
+  constexpr int W = FAST ? N / kSPW : 1;  // waves per workgroup of the main pass
   BwdArgs a{};
   a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
   a.h0 = p.h0; a.dy = p.dy; a.du = p.du; a.ddelta = p.ddelta; a.dz = p.dz; a.dh0 = p.dh0;
@@ -435,9 +833,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   a.chans = p.batch * p.dim;
   a.groups = (int)((p.dim + kWave - 1) / kWave);
   const int64_t L = p.seqlen, chans = a.chans;
-  const int64_t waves = p.batch * a.groups;
-  // segments: enough waves for every SIMD twice over, each segment at least 4 chunks long
-  int64_t nseg = std::max<int64_t>(1, (4096 + waves - 1) / waves);
+  const int64_t units = p.batch * a.groups;  // workgroups per segment
+  // segments: enough main-pass waves for every SIMD about four times over, each segment at
+  // least 4 chunks long
+  int64_t nseg = std::max<int64_t>(1, (4096 + units * W - 1) / (units * W));
   nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, L / (4 * CT)));
   int64_t seg_len = (L + nseg - 1) / nseg;
   seg_len = (seg_len + CT - 1) / CT * CT;
@@ -460,16 +859,22 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     *dst[i] = q;
     q += (fl[i] + 63) / 64 * 64;
   }
-  const dim3 grid((unsigned)waves, (unsigned)nseg);
-  hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+  const dim3 grid((unsigned)units, (unsigned)nseg);
+  if constexpr (FAST)
+    hipLaunchKernelGGL((fbwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
   err = hipGetLastError();
   if (err == hipSuccess && nseg > 1) {
     hipLaunchKernelGGL(bwd_fwd_carry_kernel, dim3(blocks_of(chans * N)), dim3(256), 0, stream, a.seg_h, a.seg_dt,
                        p.A, p.h0, chans, p.dim, N, (int)nseg);
     err = hipGetLastError();
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), dim3((unsigned)waves, (unsigned)(nseg - 1)),
-                         dim3(kWave), 0, stream, a);
+      const dim3 g1((unsigned)units, (unsigned)(nseg - 1));
+      if constexpr (FAST)
+        hipLaunchKernelGGL((fbwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
@@ -479,7 +884,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     }
   }
   if (err == hipSuccess) {
-    hipLaunchKernelGGL((bwd_main_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+    if constexpr (FAST)
+      hipLaunchKernelGGL((fbwd_main_kernel<N, T>), grid, dim3(kWave * W), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
     err = hipGetLastError();
   }
   if (err == hipSuccess) {
@@ -499,14 +907,15 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
 
 template <typename T>
 hipError_t dispatch_n(const BwdParams& p, hipStream_t s) {
+  const bool fast = fast_ok(p);
   switch (p.dstate) {
-    case 1: return run<1, T>(p, s);
-    case 2: return run<2, T>(p, s);
-    case 4: return run<4, T>(p, s);
-    case 8: return run<8, T>(p, s);
-    case 16: return run<16, T>(p, s);
-    case 32: return run<32, T>(p, s);
-    case 64: return run<64, T>(p, s);
+    case 1: return run<1, T, false>(p, s);
+    case 2: return run<2, T, false>(p, s);
+    case 4: return run<4, T, false>(p, s);
+    case 8: return fast ? run<8, T, true>(p, s) : run<8, T, false>(p, s);
+    case 16: return fast ? run<16, T, true>(p, s) : run<16, T, false>(p, s);
+    case 32: return fast ? run<32, T, true>(p, s) : run<32, T, false>(p, s);
+    case 64: return fast ? run<64, T, true>(p, s) : run<64, T, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
