@@ -427,6 +427,9 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
 #ifndef SSM_BWD_WAVES_PER_SIMD
 #define SSM_BWD_WAVES_PER_SIMD 1
 #endif
+#ifndef SSM_BWD_RECOMPUTE_ABAR
+#define SSM_BWD_RECOMPUTE_ABAR 1
+#endif
 constexpr int kCT = 8;   // steps per chunk
 constexpr int kSPW = 8;  // states per wave in the main pass
 
@@ -434,9 +437,12 @@ template <typename T>
 struct Row8;
 template <>
 struct Row8<__bf16> {
-  static __device__ __forceinline__ void load(const __bf16* p, float (&v)[8]) {
-    const uint4 r = *(const uint4*)p;
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  struct Raw {
+    uint4 v;
+  };
+  static __device__ __forceinline__ Raw fetch(const __bf16* p) { return Raw{*(const uint4*)p}; }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&v)[8]) {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
@@ -454,9 +460,14 @@ struct Row8<__bf16> {
 };
 template <>
 struct Row8<float> {
-  static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
-    const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  struct Raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ Raw fetch(const float* p) {
+    return Raw{((const float4*)p)[0], ((const float4*)p)[1]};
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, float (&v)[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
   }
   static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
     ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -519,7 +530,20 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
   }
   const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
   float cum = 0.0f;
+  // the next chunk's rows are fetched while the current one is computed
+  using Raw = typename Row8<T>::Raw;
+  Raw nu, nd, nb{};
+  const T* brow = Bp + (int64_t)(l.lane < N ? l.lane : 0) * L;
+  nu = Row8<T>::fetch(u + t0);
+  nd = Row8<T>::fetch(dl + t0);
+  if (l.lane < N) nb = Row8<T>::fetch(brow + t0);
   for (int64_t tc = t0; tc < t1; tc += kCT) {
+    const Raw ru = nu, rd = nd, rb = nb;
+    if (tc + kCT < t1) {
+      nu = Row8<T>::fetch(u + tc + kCT);
+      nd = Row8<T>::fetch(dl + tc + kCT);
+      if (l.lane < N) nb = Row8<T>::fetch(brow + tc + kCT);
+    }
     if (tc > t0 && l.active) {
       const int64_t kg = tc / kCT;
       float4* ck = (float4*)(a.ck_h + (kg * a.chans + l.ch) * N);
@@ -528,11 +552,11 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
       a.ck_dt[kg * a.chans + l.ch] = cum;
     }
     float uv[kCT], dv[kCT];
-    Row8<T>::load(u + tc, uv);
-    Row8<T>::load(dl + tc, dv);
+    Row8<T>::unpack(ru, uv);
+    Row8<T>::unpack(rd, dv);
     if (l.lane < N) {
       float bv[kCT];
-      Row8<T>::load(Bp + (int64_t)l.lane * L + tc, bv);
+      Row8<T>::unpack(rb, bv);
 #pragma unroll
       for (int i = 0; i < kCT; ++i) sB[i][l.lane] = bv[i];
     }
@@ -581,14 +605,31 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
     lam[n] = 0.0f;
   }
   const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
+  using Raw = typename Row8<T>::Raw;
+  Raw nd, ng, nz{}, nc{};
+  const T* crow = Cp + (int64_t)(l.lane < N ? l.lane : 0) * L;
+  {
+    const int64_t tc = t1 - kCT;
+    nd = Row8<T>::fetch(dl + tc);
+    ng = Row8<T>::fetch(dy + tc);
+    if (zz) nz = Row8<T>::fetch(zz + tc);
+    if (l.lane < N) nc = Row8<T>::fetch(crow + tc);
+  }
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
+    const Raw rd = nd, rg = ng, rz = nz, rc = nc;
+    if (tc - kCT >= t0) {
+      nd = Row8<T>::fetch(dl + tc - kCT);
+      ng = Row8<T>::fetch(dy + tc - kCT);
+      if (zz) nz = Row8<T>::fetch(zz + tc - kCT);
+      if (l.lane < N) nc = Row8<T>::fetch(crow + tc - kCT);
+    }
     float dv[kCT], gv[kCT], zv[kCT];
-    Row8<T>::load(dl + tc, dv);
-    Row8<T>::load(dy + tc, gv);
-    if (zz) Row8<T>::load(zz + tc, zv);
+    Row8<T>::unpack(rd, dv);
+    Row8<T>::unpack(rg, gv);
+    if (zz) Row8<T>::unpack(rz, zv);
     if (l.lane < N) {
       float cv[kCT];
-      Row8<T>::load(Cp + (int64_t)l.lane * L + tc, cv);
+      Row8<T>::unpack(rc, cv);
 #pragma unroll
       for (int i = 0; i < kCT; ++i) sC[i][l.lane] = cv[i];
     }
@@ -666,29 +707,49 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   const float Dd = a.D ? a.D[dd] : 0.0f;
   float accD = 0.0f, accbias = 0.0f;
 
+  // the next chunk's rows and checkpoint are fetched while the current one is computed
+  using Raw = typename Row8<T>::Raw;
+  const T* bcrow = (lane < kSPW ? Bp : Cp) + (int64_t)(n0 + (lane & 7)) * L;
+  Raw nu, nd, ng, nz{}, nbc{};
+  float4 nk0 = make_float4(0.f, 0.f, 0.f, 0.f), nk1 = nk0;
+  float nkd = 0.0f;
+  auto fetch = [&](int64_t tc) {
+    nu = Row8<T>::fetch(u + tc);
+    nd = Row8<T>::fetch(dl + tc);
+    ng = Row8<T>::fetch(dy + tc);
+    if (zz) nz = Row8<T>::fetch(zz + tc);
+    if (lane < 2 * kSPW) nbc = Row8<T>::fetch(bcrow + tc);
+    if (tc > t0) {
+      const int64_t kg = tc / kCT;
+      const float4* ck = (const float4*)(a.ck_h + (kg * a.chans + ch) * N + n0);
+      nk0 = ck[0];
+      nk1 = ck[1];
+      nkd = a.ck_dt[kg * a.chans + ch];
+    }
+  };
+  fetch(t1 - kCT);
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
+    const Raw ru = nu, rd = nd, rg = ng, rz = nz, rbc = nbc;
+    const float4 k0 = nk0, k1 = nk1;
+    const float kd = nkd;
+    if (tc - kCT >= t0) fetch(tc - kCT);
     float h[kSPW];
     if (tc == t0) {
 #pragma unroll
       for (int j = 0; j < kSPW; ++j) h[j] = hin[j];
     } else {
-      const int64_t kg = tc / kCT;
-      const float c = a.ck_dt[kg * a.chans + ch];
-      const float4* ck = (const float4*)(a.ck_h + (kg * a.chans + ch) * N + n0);
-      const float4 c0 = ck[0], c1 = ck[1];
-      const float cv[kSPW] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float cv[kSPW] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-      for (int j = 0; j < kSPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * c), hin[j], cv[j]);
+      for (int j = 0; j < kSPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * kd), hin[j], cv[j]);
     }
     float uv[kCT], dv[kCT], gv[kCT], zv[kCT];
-    Row8<T>::load(u + tc, uv);
-    Row8<T>::load(dl + tc, dv);
-    Row8<T>::load(dy + tc, gv);
-    if (zz) Row8<T>::load(zz + tc, zv);
+    Row8<T>::unpack(ru, uv);
+    Row8<T>::unpack(rd, dv);
+    Row8<T>::unpack(rg, gv);
+    if (zz) Row8<T>::unpack(rz, zv);
     if (lane < 2 * kSPW) {
-      const T* src = (lane < kSPW ? Bp : Cp) + (int64_t)(n0 + (lane & 7)) * L + tc;
       float bv[kCT];
-      Row8<T>::load(src, bv);
+      Row8<T>::unpack(rbc, bv);
 #pragma unroll
       for (int i = 0; i < kCT; ++i) sBC[w][lane >> 3][i][lane & 7] = bv[i];
     }
@@ -747,12 +808,20 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
       const float Bv[kSPW] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       const float Cv[kSPW] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       float accB = 0.0f, accQ = 0.0f, v[kSPW];
+#if SSM_BWD_RECOMPUTE_ABAR
+      // an opaque copy of the step keeps the compiler from holding the forward's Abar values
+      // in registers across the chunk; they are recomputed instead
+      float dtb = dt[i];
+      asm volatile("" : "+v"(dtb));
+#else
+      const float dtb = dt[i];
+#endif
 #pragma unroll
       for (int j = 0; j < kSPW; ++j) {
         const float lt = __builtin_fmaf(ds[i], Cv[j], lam[j]);
         accB = __builtin_fmaf(lt, Bv[j], accB);
         v[j] = lt * dut[i];
-        const float lp = ex2(dt[i] * A2[j]) * lt;
+        const float lp = ex2(dtb * A2[j]) * lt;
         const float q = lp * hp[i][j];
         accQ = __builtin_fmaf(q, A2[j], accQ);
         dA[j] = __builtin_fmaf(q, dt[i], dA[j]);
