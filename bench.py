@@ -14,7 +14,9 @@ as baseline.  Also reported: the long-sequence scan (B=1, D=256, N=16,
 L=2^20, fp32) under "long", the same layer prefilled as four scans resumed
 from each other's state under "resume", the decode step (B=256, D=5120,
 N=16, 128 steps) under "decode", flushed and back to back, and the causal
-conv1d + SiLU ahead of the scan (sequence and decode step) under "conv1d".
+conv1d + SiLU ahead of the scan (sequence and decode step) under "conv1d",
+and the backward scan (selective_scan_bwd, all gradients) of the same layer
+under "backward".
 """
 from __future__ import annotations
 
@@ -53,7 +55,19 @@ def algo_slots(N: int, gate: bool = True, skip: bool = True, softplus: bool = Tr
 
 # HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, per launch, scaled by
 # the same counters' reading for plain copies of known size; null until measured for the current kernel.
-TRAFFIC = {}
+TRAFFIC = {2: 356.5e6}
+
+
+def algo_slots_bwd(N: int) -> int:
+    """VALU issue slots per element of the plain adjoint-method backward (exp/log/rcp = 2), with
+    the forward states recomputed once and Abar kept from the forward half:
+      per n, forward:  Delta*A, exp, du*B, fma(h), fma(C*h) for dz, ds*h and its channel sum  -> 8 + 2
+      per n, adjoint:  fma(ds*C + lam), fma(lam*B), lam*du and its channel sum, Abar*lam,
+                       q = (Abar lam) h, fma(q*A), fma(q*Delta)                               -> 8
+      per element:     softplus 6, du = Delta*u 1, sigmoid(z) and silu 7, ds 1, dz 3, du 2,
+                       dDelta 2, sigmoid(x) 5, ddelta 1, dD and ddt_bias sums 2                -> 30
+    """
+    return 18 * N + 30
 
 
 def algo_bytes(B, D, N, L, es, gate=True, last_state=True):
@@ -75,6 +89,7 @@ def parse():
     p.add_argument("--no-long", action="store_true", help="skip the long-sequence (L=2^20) scan figure")
     p.add_argument("--no-resume", action="store_true", help="skip the prefill-in-pieces figure")
     p.add_argument("--no-conv", action="store_true", help="skip the causal conv1d figures")
+    p.add_argument("--no-bwd", action="store_true", help="skip the backward-scan figure")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the scan, run 5 plain device copies of MIB MiB each (reference dispatches for "
@@ -186,6 +201,8 @@ def main():
         out["decode"] = bench_decode(torch, gen, ssm, args)
     if not args.no_conv:
         out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
+    if not args.no_bwd and args.workload == 2:
+        out["backward"] = bench_bwd(torch, ssm, w, x, max(5, args.steps // 5), r["ms"])
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(torch, args.copy_calibration)
     if not args.no_cpu_baseline:
@@ -225,6 +242,35 @@ def bench_resume(torch, gen, ssm, w, x, steps, pieces=4):
             "ms_per_step": ms, "value": el / (ms * 1e-3), "unit": "elements/s",
             "alu_frac": el * algo_slots(N) / (ms * 1e-3) / 1e12 / PEAK_VALU_TOPS,
             "note": "inputs resident (no rotation): the pieces' 337 MB exceed the last-level cache"}
+
+
+def bench_bwd(torch, ssm, w, x, steps, fwd_ms):
+    """Backward of the layer's scan: every gradient (du, ddelta, dz, dA, dB, dC, dD, ddt_bias) for a
+    given dy, states recomputed.  Bound by VALU issue like the forward (algo_slots_bwd per element)."""
+    B, D, N, L = w.batch, w.dim, w.dstate, w.seqlen
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    gen_ = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn(g["u"].shape, device="cuda", generator=gen_).to(g["u"].dtype)
+    args = (g["u"], g["delta"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"])
+    for _ in range(2):
+        ssm.scan_bwd(*args, dy=dy, need_dinitial_state=False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ssm.scan_bwd(*args, dy=dy, need_dinitial_state=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = B * D * L
+    tops = el * algo_slots_bwd(N) / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "steps": steps, "ms_per_step": ms, "value": el / (ms * 1e-3),
+            "unit": "elements/s", "alu": {"achieved": tops, "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+                                           "frac": tops / PEAK_VALU_TOPS, "ops_per_element": algo_slots_bwd(N)},
+            "vs_forward": ms / fwd_ms,
+            "note": "checkpoint, adjoint-aggregate and main passes plus carries and deterministic reductions"}
+
 
 
 def bench_conv(torch, np, ssm, steps, K=4):
