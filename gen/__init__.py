@@ -23,6 +23,13 @@ and rounded to bf16 (round-to-nearest-even, via torch on the CPU) where the
 workload is bf16.  Draw order: dt_bias, D, u (workload 3: P, tokens), delta,
 z, B, C.  Decode: dt_bias, D, state, then per step (own seed stream) u, delta,
 z, B, C.
+
+SSD (Mamba-2 form, scalar decay per head; ``ssd_inputs``): x [B, H*P, L], dt
+[B, H, L], A [H], B, C [B, N, L], D [H*P], dt_bias [H], z [B, H*P, L].  The
+benchmark shape is the 2.8B-shaped layer as 80 heads of 64 channels (B=4,
+d_inner=5120, N=16, L=2048, bf16).  A_h = -U[1, 16]; dt_bias per head as
+above; raw dt ~ 0.1*N(0,1); x, z, B, C ~ N(0,1); D ~ N(1, 0.1).  Draw order:
+A, dt_bias, D, x, dt, z, B, C.
 """
 from __future__ import annotations
 
@@ -33,7 +40,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "scan_inputs", "random_scan_inputs", "decode_params",
-           "decode_state", "decode_step_inputs", "to_dtype"]
+           "decode_state", "decode_step_inputs", "to_dtype", "ssd_inputs", "SSD_LAYER"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -192,3 +199,25 @@ def decode_step_inputs(w: Workload | int, step: int, seed: int | None = None) ->
     C = _normal(rng, (w.batch, w.dstate))
     return dict(u=to_dtype(u, w.dtype), delta=to_dtype(delta, w.dtype), z=to_dtype(z, w.dtype),
                 B=to_dtype(B, w.dtype), C=to_dtype(C, w.dtype))
+
+
+SSD_LAYER = dict(batch=4, heads=80, headdim=64, dstate=16, seqlen=2048, dtype="bf16")
+
+
+def ssd_inputs(batch: int, heads: int, headdim: int, dstate: int, seqlen: int, dtype: str = "bf16",
+               seed: int = 0, with_D: bool = True, with_z: bool = True, with_bias: bool = True,
+               softplus: bool = True) -> dict:
+    """Inputs of the SSD (Mamba-2) layer: per-head scalar decay A [H], step dt [B, H, L]."""
+    rng = _rng(20_000 + seed, batch, heads, headdim, dstate, seqlen)
+    dim = heads * headdim
+    A = torch.from_numpy(-rng.uniform(1.0, 16.0, size=heads).astype(np.float32))
+    dt_bias = _dt_bias(rng, heads) if with_bias else None
+    D = _D(rng, dim, False) if with_D else None
+    x = _normal(rng, (batch, dim, seqlen))
+    dt = _normal(rng, (batch, heads, seqlen), 0.1)
+    z = _normal(rng, (batch, dim, seqlen)) if with_z else None
+    B = _normal(rng, (batch, dstate, seqlen))
+    C = _normal(rng, (batch, dstate, seqlen))
+    return dict(x=to_dtype(x, dtype), dt=to_dtype(dt, dtype), A=A, B=to_dtype(B, dtype), C=to_dtype(C, dtype),
+                D=D, z=None if z is None else to_dtype(z, dtype), dt_bias=dt_bias, softplus=softplus,
+                batch=batch, heads=heads, headdim=headdim, dstate=dstate, seqlen=seqlen, dtype=dtype)

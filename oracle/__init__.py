@@ -254,3 +254,25 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=
     if dt_bias is None:
         out["ddt_bias"] = None
     return out
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, headdim: int = 64, h0=None, chans=None,
+        threads: int = 0):
+    """Mamba-2 SSD forward (state-space duality, scalar A per head), fp64.
+
+    The SSD layer is the selective recurrence of ``scan`` with one decay rate and one step size per
+    head: every channel d of head h = d // headdim uses A[d, n] = A_heads[h] for all n and
+    delta[b, d, t] = dt[b, h, t] (dt_bias likewise per head).  This function is exactly that: it
+    broadcasts the per-head parameters to the channels and runs the sequential oracle.  Shapes: x, z
+    [B, H*P, L]; dt [B, H, L] (dtype of x); A [H] fp32; B, C [B, N, L]; D [H*P] fp32; dt_bias [H]
+    fp32.  Returns (y, last_state) like ``scan``.  Pinned by tests/test_oracle_ssd.py against the
+    explicit semiseparable matrix and a chunked evaluation."""
+    batch, dim, seqlen = (int(s) for s in x.shape)
+    heads = int(A.shape[0])
+    if heads * headdim != dim:
+        raise ValueError("x's channel count must be heads * headdim")
+    dstate = int(B.shape[1])
+    delta = torch.as_tensor(dt).repeat_interleave(headdim, dim=1).contiguous()
+    a = torch.as_tensor(A, dtype=torch.float32).repeat_interleave(headdim)[:, None].expand(dim, dstate).contiguous()
+    bias = None if dt_bias is None else torch.as_tensor(dt_bias, dtype=torch.float32).repeat_interleave(headdim)
+    return scan(x, delta, a, B, C, D, z, bias, softplus, h0=h0, chans=chans, threads=threads)
