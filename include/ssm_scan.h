@@ -12,6 +12,7 @@
  *                           (junchaoiu.github.io, 方法 step 2) and of the mlqm.cn
  *                           tutorial §6.
  *   selective_scan_bwd      gradients of the forward scan (training), states recomputed.
+ *   ssd_scan_fwd            the Mamba-2 SSD form (scalar decay per head) on the matrix cores.
  *   selective_state_update  one autoregressive decode step: a single-step
  *                           recurrent update of a fixed-size per-request state,
  *                           updated in place (same wiblog.cn page, table of the
@@ -151,6 +152,39 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A, const v
                        int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
 
 /*
+ * The Mamba-2 "state space duality" (SSD) form of the scan: one decay rate and one step size
+ * per head of `headdim` channels, evaluated as chunked matrix products on the matrix cores.
+ * The pages describe Mamba-2 as showing that the selective scan is dual to multiplication by
+ * a structured (semiseparable) matrix, so that the work can be reorganised in chunks onto
+ * matrix-multiply units (mlqm.cn tutorial §8; AI inference series (14), the part on
+ * reorganising the SSM into matrix computation).  With head h = d / headdim, it computes the
+ * recurrence above with A[d, n] = A[h] for every n and delta[b, d, t] = dt[b, h, t]
+ * (dt_bias[h] likewise), that is, per head:
+ *   y_t = (sum_{s<=t} (C_t . B_s) exp(A[h] (cs_t - cs_s)) Delta_s x_s + D x_t) * silu(z_t),
+ *   cs_t = Delta_0 + ... + Delta_t.
+ *
+ *   x, z, y       : [batch, heads*headdim, seqlen] bf16; z NULL = no gate
+ *   dt            : [batch, heads, seqlen] bf16, raw step before bias / softplus
+ *   A             : [heads] fp32;  dt_bias : [heads] fp32, NULL = 0
+ *   B, C          : [batch, dstate, seqlen] bf16, shared by all heads
+ *   D             : [heads*headdim] fp32, NULL = no skip
+ *   initial_state : [batch, heads*headdim, dstate] fp32, NULL = zeros; may be the same buffer
+ *                   as last_state (advanced in place)
+ *   last_state    : [batch, heads*headdim, dstate] fp32 output, NULL = not written
+ * Supported: dtype SSM_BF16, headdim 64, dstate in {16, 32, 64}, seqlen a multiple of 8, and
+ * x, dt, z, y, B, C 16-byte aligned; anything else is SSM_ERR_UNSUPPORTED (or
+ * SSM_ERR_MISALIGNED).  The matrix-core products take bf16 operands with fp32 accumulation;
+ * operands computed in fp32 (the decay-weighted matrices, the carried state) enter as hi + lo
+ * bf16 pairs.  Results match the recurrence within the bf16 tolerance; they are not bit-equal
+ * to selective_scan_fwd on the broadcast parameters.  Scratch:
+ * 4 * dstate * 64 bytes per (batch, head, 64-step chunk).  Errors as for selective_scan_fwd.
+ */
+int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* dt_bias, int softplus, const float* initial_state, void* y,
+                 float* last_state, int64_t batch, int64_t heads, int64_t headdim, int64_t dstate, int64_t seqlen,
+                 int dtype, void* stream);
+
+/*
  * One decode step for `batch` independent requests, state updated IN PLACE.
  *
  *   state       : [batch, dim, dstate] fp32, read as h_{t-1} and overwritten with h_t
@@ -228,7 +262,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -17,8 +17,8 @@ import os
 
 import torch
 
-__all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
-           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update", "causal_conv1d_fwd",
+__all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
+           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,8 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update", "causal_conv1d_fwd",
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd",
+           "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
 
 
@@ -57,6 +58,8 @@ def load():
         lib.selective_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I64, I64,
                                            I64, I64, I, P]
         lib.selective_scan_bwd.restype = I
+        lib.ssd_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I64, I, P]
+        lib.ssd_scan_fwd.restype = I
         lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.selective_state_update.restype = I
         lib.causal_conv1d_fwd.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I, P]
@@ -135,6 +138,10 @@ def selective_scan_fwd_resume(*args) -> int:
 
 def selective_scan_bwd(*args) -> int:
     return int(load().selective_scan_bwd(*args))
+
+
+def ssd_scan_fwd(*args) -> int:
+    return int(load().ssd_scan_fwd(*args))
 
 
 def selective_state_update(*args) -> int:
@@ -225,6 +232,41 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
                                   _ptr(g["dz"]), _ptr(g["ddt_bias"]), _ptr(g["dinitial_state"]), batch, dim, N, L,
                                   _dtype_code(u), _stream(dev)))
     return g
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, initial_state=None,
+            return_last_state: bool = True, y=None, last_state=None, headdim: int = 64):
+    """Mamba-2 SSD scan (scalar decay per head) on the matrix cores.  x, z: [batch, H*P, L];
+    dt: [batch, H, L]; B, C: [batch, N, L] (bf16); A, dt_bias: [H] fp32; D: [H*P] fp32.
+    Returns (y, last_state)."""
+    lib = load()
+    if x.dim() != 3 or A.dim() != 1:
+        raise ValueError("x must be [batch, heads*headdim, seqlen] and A [heads]")
+    batch, dim, L = x.shape
+    H = A.shape[0]
+    if H * headdim != dim:
+        raise ValueError(f"x has {dim} channels, not heads*headdim = {H}*{headdim}")
+    N = B.shape[1]
+    dev, dtp = x.device, x.dtype
+    _require(x, "x", (batch, dim, L), dtp, dev)
+    _require(dt, "dt", (batch, H, L), dtp, dev)
+    _require(z, "z", (batch, dim, L), dtp, dev)
+    _require(B, "B", (batch, N, L), dtp, dev)
+    _require(C, "C", (batch, N, L), dtp, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _require(initial_state, "initial_state", (batch, dim, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _require(y, "y", (batch, dim, L), dtp, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _require(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    _check(lib.ssd_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                            1 if softplus else 0, _ptr(initial_state), _ptr(y), _ptr(last_state), batch, H,
+                            headdim, N, L, _dtype_code(x), _stream(dev)))
+    return y, last_state
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, y=None):

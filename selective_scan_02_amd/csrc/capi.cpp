@@ -269,6 +269,63 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A, const v
   return hip_status(ssm::launch_scan_bwd(p, (hipStream_t)stream), "selective_scan_bwd launch");
 }
 
+int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* dt_bias, int softplus, const float* initial_state, void* y,
+                 float* last_state, int64_t batch, int64_t heads, int64_t headdim, int64_t dstate, int64_t seqlen,
+                 int dtype, void* stream) {
+  g_last_error.clear();
+  if (seqlen != 0) {
+    if (!x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+    if (!dt) return fail(SSM_ERR_NULL_ARG, "dt is NULL");
+    if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
+    if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
+    if (!y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
+  }
+  if (!A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || heads < 1 || headdim < 1 || dstate < 1 || seqlen < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld heads=%lld headdim=%lld dstate=%lld seqlen=%lld",
+                (long long)batch, (long long)heads, (long long)headdim, (long long)dstate, (long long)seqlen);
+  if (too_big(batch, heads * headdim, seqlen) || too_big(batch, dstate, seqlen) || too_big(batch, heads, seqlen) ||
+      too_big(batch, heads * headdim, dstate) || batch * heads > 65535)
+    return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
+  if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD kernels take bf16 inputs only");
+  if (!ssm::ssd_supported(headdim, dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "headdim=%lld dstate=%lld: need headdim 64 and dstate in {16,32,64}",
+                (long long)headdim, (long long)dstate);
+  if (seqlen % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "seqlen=%lld is not a multiple of 8", (long long)seqlen);
+  if ((seqlen + 63) / 64 > 0x7fffffffLL) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  const uint64_t dim = (uint64_t)heads * headdim;
+  const uint64_t nx = (uint64_t)batch * dim * seqlen * 2, nbc = (uint64_t)batch * dstate * seqlen * 2;
+  const uint64_t ndt = (uint64_t)batch * heads * seqlen * 2, nst = (uint64_t)batch * dim * dstate * 4;
+  const Range ins[] = {{"x", x, nx, 16},
+                       {"dt", dt, ndt, 16},
+                       {"z", z, nx, 16},
+                       {"B", B, nbc, 16},
+                       {"C", C, nbc, 16},
+                       {"A", A, (uint64_t)heads * 4, 4},
+                       {"D", D, dim * 4, 4},
+                       {"dt_bias", dt_bias, (uint64_t)heads * 4, 4},
+                       {"initial_state", initial_state, nst, 4}};
+  const Range ry{"y", y, nx, 16}, rl{"last_state", last_state, nst, 4};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(ry)) return rc;
+  if (int rc = check_aligned(rl)) return rc;
+  for (const Range& r : ins) {
+    if (overlap(ry, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+    if (overlap(rl, r) && !(r.p == initial_state && last_state == initial_state))
+      return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
+  }
+  if (overlap(ry, rl)) return fail(SSM_ERR_ALIAS, "y overlaps last_state");
+  ssm::SsdParams p{};
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias; p.softplus = softplus;
+  p.h0 = initial_state; p.y = y; p.last_state = last_state;
+  p.batch = batch; p.heads = heads; p.headdim = headdim; p.dstate = dstate; p.seqlen = seqlen;
+  return hip_status(ssm::launch_ssd_fwd(p, (hipStream_t)stream), "ssd_scan_fwd launch");
+}
+
 int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
                            const void* C, const float* D, const void* z, const float* dt_bias, void* y,
                            int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream) {

@@ -1,0 +1,379 @@
+// ssd.hip -- the Mamba-2 "state space duality" (SSD) form of the scan on gfx950 MFMA.
+//
+// With one decay rate a_h and one step size Delta_t per head (every channel of head h
+// uses A[d, n] = a_h for all n), the recurrence of the S6 scan is a multiplication by a
+// lower-triangular semiseparable matrix (mlqm.cn tutorial §8; AI inference series (14),
+// the part on reorganising the SSM into matrix computation): per head,
+//   y_t = sum_{s <= t} (C_t . B_s) exp(a (cs_t - cs_s)) Delta_s x_s,   cs_t = sum_{r <= t} Delta_r.
+// Cut into chunks of Q = 64 steps, this is three dense products per chunk plus a short
+// recurrence over chunks:
+//   1. chunk state (ssd_chunk_state_kernel): S_c = sum_s B_s w_s x_s^T, w_s = exp(a (cs_end - cs_s)) Delta_s
+//      -- [N x Q] x [Q x P] on MFMA;
+//   2. state passing (ssd_state_pass_kernel): H_c = exp(a cs_end,c) H_{c-1} + S_c, one thread per
+//      (head, n, p), sequential over chunks; H_{c-1} replaces S_c in place;
+//   3. chunk output (ssd_chunk_scan_kernel): Y = (G o decay o Delta) X + diag(exp(a cs_t)) C H_{c-1},
+//      G = C B^T -- [Q x N] x [N x Q], [Q x Q] x [Q x P] and [Q x N] x [N x P] on MFMA; then the
+//      D skip and the SiLU gate.
+// MFMA operands are bf16 with fp32 accumulation.  x, B and C are the bf16 inputs themselves.  The
+// operands computed in fp32 -- the decay-weighted matrices and the carried state -- enter as a
+// pair of bf16 values, v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), and each product is
+// taken twice (hi, then lo): the operand then carries about 16 bits instead of 8, at twice the
+// matrix-core work of those products.  Step sizes, cumulative sums, decays and the state passing
+// are fp32.
+//
+// MFMA lane layout of v_mfma_f32_16x16x16_bf16 (checked on the device with an in-bounds probe):
+// lane l supplies A[l % 16][4 (l / 16) + j] and B[4 (l / 16) + j][l % 16], j = 0..3, and receives
+// D[4 (l / 16) + j][l % 16].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kQ = 64;  // steps per chunk
+constexpr int kP = 64;  // channels per head
+
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct SsdArgs {
+  const __bf16* x;
+  const __bf16* dt;
+  const float* A;        // [H]
+  const __bf16* B;
+  const __bf16* C;
+  const float* D;        // [H*P] or null
+  const __bf16* z;       // or null
+  const float* dt_bias;  // [H] or null
+  const float* h0;       // [batch, H*P, N] or null
+  __bf16* y;
+  float* last;           // [batch, H*P, N] or null
+  float* S;              // [batch*H, chunks, N, P]: chunk states, then incoming states
+  float* csum;           // [batch*H, chunks]: sum of Delta over the chunk
+  int64_t batch, heads, seqlen;
+  int chunks, softplus;
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ short bf16_bits(float v) {
+  const __bf16 h = (__bf16)v;
+  return __builtin_bit_cast(short, h);
+}
+
+// v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+
+// Step sizes of the chunk, one per lane (0 beyond the sequence), and their inclusive prefix sums.
+__device__ __forceinline__ void chunk_steps(const SsdArgs& a, int64_t bh, int64_t t0, int len, int lane, float& dl,
+                                            float& cs) {
+  dl = 0.0f;
+  if (lane < len) {
+    const int h = (int)(bh % a.heads);
+    const float xr = (float)a.dt[bh * a.seqlen + t0 + lane] + (a.dt_bias ? a.dt_bias[h] : 0.0f);
+    dl = a.softplus ? softplus(xr) : xr;
+  }
+  cs = dl;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_up(cs, o);
+    if (lane >= o) cs += v;
+  }
+}
+
+// 1. Chunk states: one wave per (chunk, batch row x head).
+template <int N>
+__global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
+  __shared__ float sw[kQ];
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.heads, h = bh % a.heads;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)c * kQ;
+  const int len = (int)std::min<int64_t>(kQ, L - t0);
+  float dl, cs;
+  chunk_steps(a, bh, t0, len, lane, dl, cs);
+  const float cs_end = __shfl(cs, kQ - 1);
+  const float A2 = a.A[h] * kLog2e;
+  sw[lane] = ex2(A2 * (cs_end - cs)) * dl;
+  if (lane == 0) a.csum[bh * a.chunks + c] = cs_end;
+  __syncthreads();
+  const int r = lane % 16, q = lane / 16;
+  const __bf16* xh = a.x + (b * a.heads * kP + h * kP) * L + t0;
+  const __bf16* Bb = a.B + b * N * L + t0;
+  float* S = a.S + (bh * a.chunks + c) * N * kP;
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt) {
+    f32x4 acc[kP / 16];
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < kQ / 16; ++kt) {
+      if (16 * kt >= len) break;  // the same for the whole wave
+      // lanes past the sequence end (len is a multiple of 8) supply zeros and load nothing
+      const int s = 16 * kt + 4 * q;
+      const bool in = s < len;
+      // A operand: B[n][s..s+3] * w[s..s+3], n = 16 nt + r, as a hi/lo pair
+      bf16x4 ahi, alo;
+      {
+        const uint2 raw = in ? *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + s) : make_uint2(0, 0);
+        const float4 wv = *(const float4*)&sw[s];
+        const float bw[4] = {__uint_as_float(raw.x << 16) * wv.x, __uint_as_float(raw.x & 0xffff0000u) * wv.y,
+                             __uint_as_float(raw.y << 16) * wv.z, __uint_as_float(raw.y & 0xffff0000u) * wv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          __bf16 hi, lo;
+          split_bf16(bw[j], hi, lo);
+          ahi[j] = __builtin_bit_cast(short, hi);
+          alo[j] = __builtin_bit_cast(short, lo);
+        }
+      }
+#pragma unroll
+      for (int pt = 0; pt < kP / 16; ++pt) {
+        // B operand: x[p][s..s+3], p = 16 pt + r
+        const bf16x4 bv = in ? *(const bf16x4*)(xh + (int64_t)(16 * pt + r) * L + s) : bf16x4{0, 0, 0, 0};
+        acc[pt] = mfma16(ahi, bv, acc[pt]);
+        acc[pt] = mfma16(alo, bv, acc[pt]);
+      }
+    }
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; ++pt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[(16 * nt + 4 * q + j) * kP + 16 * pt + r] = acc[pt][j];
+  }
+}
+
+// 2. State passing: one thread per (batch row x head, n, p).
+__global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a, int N) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)N * kP;
+  if (i >= a.batch * a.heads * per) return;
+  const int64_t bh = i / per, rem = i % per;
+  const int n = (int)(rem / kP), p = (int)(rem % kP);
+  const int64_t b = bh / a.heads, h = bh % a.heads;
+  const int64_t state_idx = ((b * a.heads + h) * kP + p) * N + n;  // [batch, H*P, N]
+  const float A2 = a.A[h] * kLog2e;
+  float hs = a.h0 ? a.h0[state_idx] : 0.0f;
+  for (int c = 0; c < a.chunks; ++c) {
+    const int64_t k = (bh * a.chunks + c) * per + rem;
+    const float s = a.S[k];
+    a.S[k] = hs;
+    hs = __builtin_fmaf(ex2(A2 * a.csum[bh * a.chunks + c]), hs, s);
+  }
+  if (a.last) a.last[state_idx] = hs;
+}
+
+// 3. Chunk outputs: four waves per (chunk, batch row x head); wave w owns output rows
+// t = 16 w .. 16 w + 15 (all 64 channels).
+template <int N>
+__global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
+  constexpr int XS = kQ + 8;  // padded row of the x tile (bf16)
+  constexpr int NS = N + 4;   // padded row of the step-major B, C and state tiles
+  __shared__ __align__(16) __bf16 sX[kP][XS];   // x[p][s]
+  __shared__ __align__(16) __bf16 sM[2][kQ][XS];  // decay-weighted C B^T, [t][s], hi and lo parts
+  __shared__ __align__(16) __bf16 sCt[kQ][NS];  // C[t][n]
+  __shared__ __align__(16) __bf16 sBt[kQ][NS];  // B[s][n]
+  __shared__ __align__(16) __bf16 sH[2][kP][NS];  // incoming state, [p][n], hi and lo parts
+  __shared__ float scs[kQ], sdl[kQ];
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  const int c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.heads, h = bh % a.heads;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)c * kQ;
+  const int len = (int)std::min<int64_t>(kQ, L - t0);
+  const float A2 = a.A[h] * kLog2e;
+  const int64_t ch0 = b * a.heads * kP + h * kP;  // first channel of the head
+  const __bf16* xh = a.x + ch0 * L + t0;
+
+  if (w == 0) {
+    float dl, cs;
+    chunk_steps(a, bh, t0, len, lane, dl, cs);
+    scs[lane] = cs;
+    sdl[lane] = dl;
+  }
+  // x tile: 64 rows x 64 steps, 8 steps (16 bytes) per piece, zero beyond the sequence
+  for (int pc = tid; pc < kP * kQ / 8; pc += 256) {
+    const int row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (s8 < len) v = *(const uint4*)(xh + (int64_t)row * L + s8);
+    *(uint2*)&sX[row][s8] = make_uint2(v.x, v.y);
+    *(uint2*)&sX[row][s8 + 4] = make_uint2(v.z, v.w);
+  }
+  // B, C transposed to step-major, 4 steps per piece
+  const __bf16* Bb = a.B + b * N * L + t0;
+  const __bf16* Cb = a.C + b * N * L + t0;
+  for (int pc = tid; pc < N * kQ / 4; pc += 256) {
+    const int n = pc / (kQ / 4), s4 = 4 * (pc % (kQ / 4));
+    uint2 vb = make_uint2(0, 0), vc = make_uint2(0, 0);
+    if (s4 < len) {
+      vb = *(const uint2*)(Bb + (int64_t)n * L + s4);
+      vc = *(const uint2*)(Cb + (int64_t)n * L + s4);
+    }
+    const uint32_t wb[2] = {vb.x, vb.y}, wc[2] = {vc.x, vc.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t bj = (uint16_t)(wb[j / 2] >> (16 * (j % 2))), cj = (uint16_t)(wc[j / 2] >> (16 * (j % 2)));
+      sBt[s4 + j][n] = __builtin_bit_cast(__bf16, bj);
+      sCt[s4 + j][n] = __builtin_bit_cast(__bf16, cj);
+    }
+  }
+  // incoming state, transposed to [p][n], rounded to bf16
+  const float* Hin = a.S + (bh * a.chunks + c) * N * kP;
+  for (int e = tid; e < N * kP; e += 256) {
+    const int n = e / kP, p = e % kP;
+    split_bf16(Hin[e], sH[0][p][n], sH[1][p][n]);
+  }
+  __syncthreads();
+
+  const int r = lane % 16, q = lane / 16;
+  const int trow = 16 * w + r;  // A-operand row of this lane
+  // decay-weighted G = C B^T for the column tiles at or left of the diagonal
+  for (int st = 0; st <= w; ++st) {
+    f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < N / 16; ++kt) {
+      const bf16x4 av = *(const bf16x4*)&sCt[trow][16 * kt + 4 * q];
+      const bf16x4 bv = *(const bf16x4*)&sBt[16 * st + r][16 * kt + 4 * q];
+      g = mfma16(av, bv, g);
+    }
+    const int s = 16 * st + r;
+    const float css = scs[s], dls = sdl[s];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 16 * w + 4 * q + j;
+      const float m = s <= t ? g[j] * ex2(A2 * (scs[t] - css)) * dls : 0.0f;
+      split_bf16(m, sM[0][t][s], sM[1][t][s]);
+    }
+  }
+  __syncthreads();
+  f32x4 acc[kP / 16];
+#pragma unroll
+  for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Y = M x over the causal column tiles
+  for (int kt = 0; kt <= w; ++kt) {
+    const bf16x4 ahi = *(const bf16x4*)&sM[0][trow][16 * kt + 4 * q];
+    const bf16x4 alo = *(const bf16x4*)&sM[1][trow][16 * kt + 4 * q];
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; ++pt) {
+      const bf16x4 bv = *(const bf16x4*)&sX[16 * pt + r][16 * kt + 4 * q];
+      acc[pt] = mfma16(ahi, bv, acc[pt]);
+      acc[pt] = mfma16(alo, bv, acc[pt]);
+    }
+  }
+  // + diag(exp(a cs_t)) C H_in
+  float dec[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dec[j] = ex2(A2 * scs[16 * w + 4 * q + j]);
+#pragma unroll
+  for (int pt = 0; pt < kP / 16; ++pt) {
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < N / 16; ++kt) {
+      const bf16x4 av = *(const bf16x4*)&sCt[trow][16 * kt + 4 * q];
+      o = mfma16(av, *(const bf16x4*)&sH[0][16 * pt + r][16 * kt + 4 * q], o);
+      o = mfma16(av, *(const bf16x4*)&sH[1][16 * pt + r][16 * kt + 4 * q], o);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[pt][j] = __builtin_fmaf(dec[j], o[j], acc[pt][j]);
+  }
+  // skip, gate, store: this lane holds steps t = 16 w + 4 q + j of channel p = 16 pt + r
+  const int tq = 16 * w + 4 * q;
+  if (tq >= len) return;
+#pragma unroll
+  for (int pt = 0; pt < kP / 16; ++pt) {
+    const int p = 16 * pt + r;
+    const int64_t row = (ch0 + p) * L + t0 + tq;
+    float zv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (a.z) {
+      const uint2 zr = *(const uint2*)(a.z + row);
+      zv[0] = __uint_as_float(zr.x << 16);
+      zv[1] = __uint_as_float(zr.x & 0xffff0000u);
+      zv[2] = __uint_as_float(zr.y << 16);
+      zv[3] = __uint_as_float(zr.y & 0xffff0000u);
+    }
+    const float Dp = a.D ? a.D[h * kP + p] : 0.0f;
+    __bf16 out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = __builtin_fmaf(Dp, (float)sX[p][tq + j], acc[pt][j]);
+      if (a.z) v *= silu(zv[j]);
+      out[j] = (__bf16)v;
+    }
+    uint2 o;
+    __builtin_memcpy(&o, out, sizeof o);
+    *(uint2*)(a.y + row) = o;
+  }
+}
+
+template <int N>
+hipError_t run(const SsdParams& p, hipStream_t stream) {
+  SsdArgs a{};
+  a.x = (const __bf16*)p.x; a.dt = (const __bf16*)p.dt; a.A = p.A; a.B = (const __bf16*)p.B;
+  a.C = (const __bf16*)p.C; a.D = p.D; a.z = (const __bf16*)p.z; a.dt_bias = p.dt_bias; a.h0 = p.h0;
+  a.y = (__bf16*)p.y; a.last = p.last_state;
+  a.batch = p.batch; a.heads = p.heads; a.seqlen = p.seqlen; a.softplus = p.softplus;
+  a.chunks = (int)((p.seqlen + kQ - 1) / kQ);
+  const int64_t bh = p.batch * p.heads;
+  const size_t nS = (size_t)bh * a.chunks * N * kP, nc = (size_t)bh * a.chunks;
+  void* scratch = nullptr;
+  hipError_t err = scratch_alloc(&scratch, (nS + (nc + 63) / 64 * 64) * sizeof(float), stream);
+  if (err != hipSuccess) return err;
+  a.S = (float*)scratch;
+  a.csum = a.S + nS;
+  const dim3 grid((unsigned)a.chunks, (unsigned)bh);
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<N>), grid, dim3(64), 0, stream, a);
+  err = hipGetLastError();
+  if (err == hipSuccess) {
+    const int64_t threads = bh * N * kP;
+    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, N);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N>), grid, dim3(256), 0, stream, a);
+    err = hipGetLastError();
+  }
+  const hipError_t ferr = hipFreeAsync(scratch, stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+__global__ __launch_bounds__(256) void ssd_empty_state(float* last, const float* h0, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) last[i] = h0 ? h0[i] : 0.0f;
+}
+
+}  // namespace
+
+bool ssd_supported(int64_t headdim, int64_t dstate) {
+  return headdim == kP && (dstate == 16 || dstate == 32 || dstate == 64);
+}
+
+hipError_t launch_ssd_fwd(const SsdParams& p, hipStream_t stream) {
+  if (p.seqlen == 0) {
+    if (p.last_state && p.last_state != p.h0) {
+      const int64_t n = p.batch * p.heads * kP * p.dstate;
+      hipLaunchKernelGGL(ssd_empty_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.last_state,
+                         p.h0, n);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  switch (p.dstate) {
+    case 16: return run<16>(p, stream);
+    case 32: return run<32>(p, stream);
+    case 64: return run<64>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ssm

@@ -88,6 +88,22 @@ struct BwdParams {
   int dtype;
 };
 
+struct SsdParams {
+  const void* x;         // [batch, heads*headdim, L] bf16
+  const void* dt;        // [batch, heads, L] bf16
+  const float* A;        // [heads]
+  const void* B;         // [batch, dstate, L] bf16
+  const void* C;
+  const float* D;        // [heads*headdim] or null
+  const void* z;         // or null
+  const float* dt_bias;  // [heads] or null
+  int softplus;
+  const float* h0;       // [batch, heads*headdim, dstate] or null
+  void* y;
+  float* last_state;     // or null
+  int64_t batch, heads, headdim, dstate, seqlen;
+};
+
 struct ScanPlan {
   int mode;          // 0 intervals, 1 one pass, 2 aggregate/carry/output
   int64_t groups;    // channel groups of 64
@@ -108,6 +124,8 @@ hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any
 bool chunked_supported(const ScanParams& p);
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
 hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream);
+bool ssd_supported(int64_t headdim, int64_t dstate);
+hipError_t launch_ssd_fwd(const SsdParams& p, hipStream_t stream);
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream);

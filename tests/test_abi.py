@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "selective_state_update",
+    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd",
+                 "selective_state_update",
                  "causal_conv1d_fwd",
                  "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
         assert name in fns
@@ -54,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 4
+    assert lib.ssm_abi_version() == 5
 
 
 def scan_args(**over):
@@ -271,3 +272,28 @@ def test_bwd_validation(lib):
     assert lib.selective_scan_bwd(*bwd_args(dh0=addr(9))) == ALIAS
     assert lib.selective_scan_bwd(*bwd_args(dD=addr(13) + 4)) == ALIAS
     assert "overlaps" in ssm.last_error()
+
+
+SSD_FIELDS = ("x", "dt", "A", "B", "C", "D", "z", "dt_bias", "softplus", "h0", "y", "last", "batch", "heads",
+              "headdim", "dstate", "seqlen", "dtype", "stream")
+
+
+def ssd_args(**over):
+    a = dict(zip(SSD_FIELDS[:8], [addr(i) for i in range(1, 9)]))
+    a.update(softplus=1, h0=addr(9), y=addr(10), last=addr(11), batch=2, heads=4, headdim=64, dstate=16,
+             seqlen=256, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in SSD_FIELDS]
+
+
+def test_ssd_validation(lib):
+    for f in ("x", "dt", "A", "B", "C", "y"):
+        assert lib.ssd_scan_fwd(*ssd_args(**{f: None})) == NULL_ARG, f
+    assert lib.ssd_scan_fwd(*ssd_args(dtype=0)) == UNSUPPORTED          # bf16 only
+    assert lib.ssd_scan_fwd(*ssd_args(headdim=32)) == UNSUPPORTED
+    assert lib.ssd_scan_fwd(*ssd_args(dstate=8)) == UNSUPPORTED
+    assert lib.ssd_scan_fwd(*ssd_args(seqlen=100)) == UNSUPPORTED       # not a multiple of 8
+    assert lib.ssd_scan_fwd(*ssd_args(batch=0)) == BAD_SHAPE
+    assert lib.ssd_scan_fwd(*ssd_args(x=addr(1) + 8)) == MISALIGNED     # 16-byte rows
+    assert lib.ssd_scan_fwd(*ssd_args(y=addr(1) + 64)) == ALIAS
+    assert lib.ssd_scan_fwd(*ssd_args(last=addr(9) + 64)) == ALIAS
