@@ -101,6 +101,25 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
   const int64_t L = a.seqlen;
   const int64_t t0 = (int64_t)c * kQ;
   const int len = (int)std::min<int64_t>(kQ, L - t0);
+  const int r = lane % 16, q = lane / 16;
+  const __bf16* xh = a.x + (b * a.heads * kP + h * kP) * L + t0;
+  const __bf16* Bb = a.B + b * N * L + t0;
+  float* S = a.S + (bh * a.chunks + c) * N * kP;
+  // every global load is issued before the step sizes are needed: x and B do not depend on them
+  bf16x4 xv[kQ / 16][kP / 16];
+  uint2 braw[N / 16][kQ / 16];
+#pragma unroll
+  for (int kt = 0; kt < kQ / 16; ++kt) {
+    // lanes past the sequence end (len is a multiple of 8) supply zeros and load nothing
+    const int s = 16 * kt + 4 * q;
+    const bool in = s < len;
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; ++pt)
+      xv[kt][pt] = in ? *(const bf16x4*)(xh + (int64_t)(16 * pt + r) * L + s) : bf16x4{0, 0, 0, 0};
+#pragma unroll
+    for (int nt = 0; nt < N / 16; ++nt)
+      braw[nt][kt] = in ? *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + s) : make_uint2(0, 0);
+  }
   float dl, cs;
   chunk_steps(a, bh, t0, len, lane, dl, cs);
   const float cs_end = __shfl(cs, kQ - 1);
@@ -108,10 +127,6 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
   sw[lane] = ex2(A2 * (cs_end - cs)) * dl;
   if (lane == 0) a.csum[bh * a.chunks + c] = cs_end;
   __syncthreads();
-  const int r = lane % 16, q = lane / 16;
-  const __bf16* xh = a.x + (b * a.heads * kP + h * kP) * L + t0;
-  const __bf16* Bb = a.B + b * N * L + t0;
-  float* S = a.S + (bh * a.chunks + c) * N * kP;
 #pragma unroll
   for (int nt = 0; nt < N / 16; ++nt) {
     f32x4 acc[kP / 16];
@@ -119,14 +134,11 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
     for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kt = 0; kt < kQ / 16; ++kt) {
-      if (16 * kt >= len) break;  // the same for the whole wave
-      // lanes past the sequence end (len is a multiple of 8) supply zeros and load nothing
       const int s = 16 * kt + 4 * q;
-      const bool in = s < len;
       // A operand: B[n][s..s+3] * w[s..s+3], n = 16 nt + r, as a hi/lo pair
       bf16x4 ahi, alo;
       {
-        const uint2 raw = in ? *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + s) : make_uint2(0, 0);
+        const uint2 raw = braw[nt][kt];
         const float4 wv = *(const float4*)&sw[s];
         const float bw[4] = {__uint_as_float(raw.x << 16) * wv.x, __uint_as_float(raw.x & 0xffff0000u) * wv.y,
                              __uint_as_float(raw.y << 16) * wv.z, __uint_as_float(raw.y & 0xffff0000u) * wv.w};
@@ -140,10 +152,8 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
       }
 #pragma unroll
       for (int pt = 0; pt < kP / 16; ++pt) {
-        // B operand: x[p][s..s+3], p = 16 pt + r
-        const bf16x4 bv = in ? *(const bf16x4*)(xh + (int64_t)(16 * pt + r) * L + s) : bf16x4{0, 0, 0, 0};
-        acc[pt] = mfma16(ahi, bv, acc[pt]);
-        acc[pt] = mfma16(alo, bv, acc[pt]);
+        acc[pt] = mfma16(ahi, xv[kt][pt], acc[pt]);
+        acc[pt] = mfma16(alo, xv[kt][pt], acc[pt]);
       }
     }
 #pragma unroll
@@ -164,27 +174,40 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a, int N) {
   const int64_t state_idx = ((b * a.heads + h) * kP + p) * N + n;  // [batch, H*P, N]
   const float A2 = a.A[h] * kLog2e;
   float hs = a.h0 ? a.h0[state_idx] : 0.0f;
-  for (int c = 0; c < a.chunks; ++c) {
-    const int64_t k = (bh * a.chunks + c) * per + rem;
-    const float s = a.S[k];
-    a.S[k] = hs;
-    hs = __builtin_fmaf(ex2(A2 * a.csum[bh * a.chunks + c]), hs, s);
+  // 16 chunks at a time: their loads are all in flight before the first is used
+  constexpr int kBatch = 16;
+  for (int c0 = 0; c0 < a.chunks; c0 += kBatch) {
+    const int nb = std::min(kBatch, a.chunks - c0);
+    float sv[kBatch], ev[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (k < nb) {
+        sv[k] = a.S[(bh * a.chunks + c0 + k) * per + rem];
+        ev[k] = a.csum[bh * a.chunks + c0 + k];
+      }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (k < nb) {
+        a.S[(bh * a.chunks + c0 + k) * per + rem] = hs;
+        hs = __builtin_fmaf(ex2(A2 * ev[k]), hs, sv[k]);
+      }
   }
   if (a.last) a.last[state_idx] = hs;
 }
 
 // 3. Chunk outputs: four waves per (chunk, batch row x head); wave w owns output rows
-// t = 16 w .. 16 w + 15 (all 64 channels).
+// t = 16 w .. 16 w + 15 (all 64 channels).  The decay-weighted matrix is formed transposed,
+// G^T = B C^T, whose accumulator layout (rows s, columns t) is exactly the A-operand layout
+// of the next product M x (rows t, reduction index s): it never leaves the registers.
 template <int N>
 __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   constexpr int XS = kQ + 8;  // padded row of the x tile (bf16)
-  constexpr int NS = N + 4;   // padded row of the step-major B, C and state tiles
+  constexpr int NS = N + 4;   // padded row of the step-major B and C tiles
   __shared__ __align__(16) __bf16 sX[kP][XS];   // x[p][s]
-  __shared__ __align__(16) __bf16 sM[2][kQ][XS];  // decay-weighted C B^T, [t][s], hi and lo parts
   __shared__ __align__(16) __bf16 sCt[kQ][NS];  // C[t][n]
   __shared__ __align__(16) __bf16 sBt[kQ][NS];  // B[s][n]
-  __shared__ __align__(16) __bf16 sH[2][kP][NS];  // incoming state, [p][n], hi and lo parts
   __shared__ float scs[kQ], sdl[kQ];
+  __shared__ __align__(16) float sY[kP][kQ + 4];  // y before the gate, [p][t]
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
   const int c = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -195,7 +218,29 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   const float A2 = a.A[h] * kLog2e;
   const int64_t ch0 = b * a.heads * kP + h * kP;  // first channel of the head
   const __bf16* xh = a.x + ch0 * L + t0;
-
+  const int r = lane % 16, q = lane / 16;
+  const int tq = 16 * w + 4 * q;  // first output step of this lane's accumulators
+  // the gate inputs of this thread's two output pieces (8 steps of one channel each), the skip
+  // weights and the incoming state are fetched before anything waits
+  constexpr int kPieces = kP * kQ / 8 / 256;
+  uint4 zraw[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int pc = tid + 256 * i, row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
+    zraw[i] = (a.z && s8 < len) ? *(const uint4*)(a.z + (ch0 + row) * L + t0 + s8) : make_uint4(0, 0, 0, 0);
+  }
+  float Dv[kP / 16];
+#pragma unroll
+  for (int pt = 0; pt < kP / 16; ++pt) Dv[pt] = a.D ? a.D[h * kP + 16 * pt + r] : 0.0f;
+  // B operand of C H_in: H[n][p] for n = 16 kt + 4 q + j, p = 16 pt + r
+  const float* Hin = a.S + (bh * a.chunks + c) * N * kP;
+  float hv[N / 16][kP / 16][4];
+#pragma unroll
+  for (int kt = 0; kt < N / 16; ++kt)
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; ++pt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) hv[kt][pt][jj] = Hin[(16 * kt + 4 * q + jj) * kP + 16 * pt + r];
   if (w == 0) {
     float dl, cs;
     chunk_steps(a, bh, t0, len, lane, dl, cs);
@@ -222,97 +267,104 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
     }
     const uint32_t wb[2] = {vb.x, vb.y}, wc[2] = {vc.x, vc.y};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint16_t bj = (uint16_t)(wb[j / 2] >> (16 * (j % 2))), cj = (uint16_t)(wc[j / 2] >> (16 * (j % 2)));
-      sBt[s4 + j][n] = __builtin_bit_cast(__bf16, bj);
-      sCt[s4 + j][n] = __builtin_bit_cast(__bf16, cj);
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint16_t bj = (uint16_t)(wb[jj / 2] >> (16 * (jj % 2))), cj = (uint16_t)(wc[jj / 2] >> (16 * (jj % 2)));
+      sBt[s4 + jj][n] = __builtin_bit_cast(__bf16, bj);
+      sCt[s4 + jj][n] = __builtin_bit_cast(__bf16, cj);
     }
-  }
-  // incoming state, transposed to [p][n], rounded to bf16
-  const float* Hin = a.S + (bh * a.chunks + c) * N * kP;
-  for (int e = tid; e < N * kP; e += 256) {
-    const int n = e / kP, p = e % kP;
-    split_bf16(Hin[e], sH[0][p][n], sH[1][p][n]);
   }
   __syncthreads();
 
-  const int r = lane % 16, q = lane / 16;
-  const int trow = 16 * w + r;  // A-operand row of this lane
-  // decay-weighted G = C B^T for the column tiles at or left of the diagonal
-  for (int st = 0; st <= w; ++st) {
-    f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kt = 0; kt < N / 16; ++kt) {
-      const bf16x4 av = *(const bf16x4*)&sCt[trow][16 * kt + 4 * q];
-      const bf16x4 bv = *(const bf16x4*)&sBt[16 * st + r][16 * kt + 4 * q];
-      g = mfma16(av, bv, g);
-    }
-    const int s = 16 * st + r;
-    const float css = scs[s], dls = sdl[s];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * q + j;
-      const float m = s <= t ? g[j] * ex2(A2 * (scs[t] - css)) * dls : 0.0f;
-      split_bf16(m, sM[0][t][s], sM[1][t][s]);
-    }
-  }
-  __syncthreads();
+  const int t = 16 * w + r;  // the step of this lane's A-operand row
+  const float cst = scs[t];
   f32x4 acc[kP / 16];
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // Y = M x over the causal column tiles
-  for (int kt = 0; kt <= w; ++kt) {
-    const bf16x4 ahi = *(const bf16x4*)&sM[0][trow][16 * kt + 4 * q];
-    const bf16x4 alo = *(const bf16x4*)&sM[1][trow][16 * kt + 4 * q];
+  for (int st = 0; st <= w; ++st) {
+    // G^T[s][t] = sum_n B[s][n] C[t][n]: lane holds s = 16 st + 4 q + j, t = 16 w + r
+    f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < N / 16; ++kt) {
+      const bf16x4 av = *(const bf16x4*)&sBt[16 * st + r][16 * kt + 4 * q];
+      const bf16x4 bv = *(const bf16x4*)&sCt[t][16 * kt + 4 * q];
+      g = mfma16(av, bv, g);
+    }
+    // M[t][s] = G[t][s] exp(a (cs_t - cs_s)) Delta_s for s <= t, as hi/lo bf16 A operands
+    bf16x4 mhi, mlo;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int sj = 16 * st + 4 * q + jj;
+      const float m = sj <= t ? g[jj] * ex2(A2 * (cst - scs[sj])) * sdl[sj] : 0.0f;
+      __bf16 hi, lo;
+      split_bf16(m, hi, lo);
+      mhi[jj] = __builtin_bit_cast(short, hi);
+      mlo[jj] = __builtin_bit_cast(short, lo);
+    }
 #pragma unroll
     for (int pt = 0; pt < kP / 16; ++pt) {
-      const bf16x4 bv = *(const bf16x4*)&sX[16 * pt + r][16 * kt + 4 * q];
-      acc[pt] = mfma16(ahi, bv, acc[pt]);
-      acc[pt] = mfma16(alo, bv, acc[pt]);
+      const bf16x4 bv = *(const bf16x4*)&sX[16 * pt + r][16 * st + 4 * q];
+      acc[pt] = mfma16(mhi, bv, acc[pt]);
+      acc[pt] = mfma16(mlo, bv, acc[pt]);
     }
   }
-  // + diag(exp(a cs_t)) C H_in
+  // + diag(exp(a cs_t)) C H_in (accumulator rows are t = 16 w + 4 q + j)
   float dec[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dec[j] = ex2(A2 * scs[16 * w + 4 * q + j]);
+  for (int jj = 0; jj < 4; ++jj) dec[jj] = ex2(A2 * scs[tq + jj]);
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) {
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kt = 0; kt < N / 16; ++kt) {
-      const bf16x4 av = *(const bf16x4*)&sCt[trow][16 * kt + 4 * q];
-      o = mfma16(av, *(const bf16x4*)&sH[0][16 * pt + r][16 * kt + 4 * q], o);
-      o = mfma16(av, *(const bf16x4*)&sH[1][16 * pt + r][16 * kt + 4 * q], o);
+      const bf16x4 av = *(const bf16x4*)&sCt[t][16 * kt + 4 * q];
+      bf16x4 hhi, hlo;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        __bf16 hi, lo;
+        split_bf16(hv[kt][pt][jj], hi, lo);
+        hhi[jj] = __builtin_bit_cast(short, hi);
+        hlo[jj] = __builtin_bit_cast(short, lo);
+      }
+      o = mfma16(av, hhi, o);
+      o = mfma16(av, hlo, o);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[pt][j] = __builtin_fmaf(dec[j], o[j], acc[pt][j]);
+    for (int jj = 0; jj < 4; ++jj) acc[pt][jj] = __builtin_fmaf(dec[jj], o[jj], acc[pt][jj]);
   }
-  // skip, gate, store: this lane holds steps t = 16 w + 4 q + j of channel p = 16 pt + r
-  const int tq = 16 * w + 4 * q;
-  if (tq >= len) return;
+  // skip: this lane holds steps t = 16 w + 4 q + j of channel p = 16 pt + r; y before the gate
+  // goes through LDS so that the gate and the store run on whole 16-byte row pieces
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) {
     const int p = 16 * pt + r;
-    const int64_t row = (ch0 + p) * L + t0 + tq;
-    float zv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (a.z) {
-      const uint2 zr = *(const uint2*)(a.z + row);
-      zv[0] = __uint_as_float(zr.x << 16);
-      zv[1] = __uint_as_float(zr.x & 0xffff0000u);
-      zv[2] = __uint_as_float(zr.y << 16);
-      zv[3] = __uint_as_float(zr.y & 0xffff0000u);
-    }
-    const float Dp = a.D ? a.D[h * kP + p] : 0.0f;
-    __bf16 out[4];
+    float4 v;
+    v.x = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 0], acc[pt][0]);
+    v.y = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 1], acc[pt][1]);
+    v.z = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 2], acc[pt][2]);
+    v.w = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 3], acc[pt][3]);
+    *(float4*)&sY[p][tq] = v;
+  }
+  __syncthreads();
+  // gate and store, 8 steps of one channel per piece
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = __builtin_fmaf(Dp, (float)sX[p][tq + j], acc[pt][j]);
-      if (a.z) v *= silu(zv[j]);
-      out[j] = (__bf16)v;
+  for (int i = 0; i < kPieces; ++i) {
+    const int pc = tid + 256 * i, row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
+    if (s8 >= len) continue;
+    const float4 v0 = *(const float4*)&sY[row][s8], v1 = *(const float4*)&sY[row][s8 + 4];
+    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (a.z) {
+      const uint32_t zw[4] = {zraw[i].x, zraw[i].y, zraw[i].z, zraw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] *= silu(__uint_as_float(zw[k] << 16));
+        v[2 * k + 1] *= silu(__uint_as_float(zw[k] & 0xffff0000u));
+      }
     }
-    uint2 o;
+    __bf16 out[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = (__bf16)v[k];
+    uint4 o;
     __builtin_memcpy(&o, out, sizeof o);
-    *(uint2*)(a.y + row) = o;
+    *(uint4*)(a.y + (ch0 + row) * L + t0 + s8) = o;
   }
 }
 
