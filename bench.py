@@ -15,8 +15,9 @@ L=2^20, fp32) under "long", the same layer prefilled as four scans resumed
 from each other's state under "resume", the decode step (B=256, D=5120,
 N=16, 128 steps) under "decode", flushed and back to back, and the causal
 conv1d + SiLU ahead of the scan (sequence and decode step) under "conv1d",
-and the backward scan (selective_scan_bwd, all gradients) of the same layer
-under "backward".
+the backward scan (selective_scan_bwd, all gradients) of the same layer
+under "backward", and the same layer in the Mamba-2 SSD form (80 heads of
+64 channels, ssd_scan_fwd on the matrix cores) under "ssd".
 """
 from __future__ import annotations
 
@@ -90,6 +91,7 @@ def parse():
     p.add_argument("--no-resume", action="store_true", help="skip the prefill-in-pieces figure")
     p.add_argument("--no-conv", action="store_true", help="skip the causal conv1d figures")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward-scan figure")
+    p.add_argument("--no-ssd", action="store_true", help="skip the SSD (Mamba-2 form) figure")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the scan, run 5 plain device copies of MIB MiB each (reference dispatches for "
@@ -203,6 +205,8 @@ def main():
         out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
     if not args.no_bwd and args.workload == 2:
         out["backward"] = bench_bwd(torch, ssm, w, x, max(5, args.steps // 5), r["ms"])
+    if not args.no_ssd and args.workload == 2:
+        out["ssd"] = bench_ssd(torch, gen, ssm, max(10, args.steps // 2), r["ms"])
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(torch, args.copy_calibration)
     if not args.no_cpu_baseline:
@@ -271,6 +275,55 @@ def bench_bwd(torch, ssm, w, x, steps, fwd_ms):
             "vs_forward": ms / fwd_ms,
             "note": "checkpoint, adjoint-aggregate and main passes plus carries and deterministic reductions"}
 
+
+
+def ssd_flops_per_element(N: int, Q: int = 64, P: int = 64) -> float:
+    """Algorithmic flops per element of the chunked SSD form (chunk Q, head size P, state N): per
+    chunk and head, the causal half of C B^T (Q(Q+1)/2 N MACs) and of M x (Q(Q+1)/2 P), C H_in
+    (Q N P) and the chunk state B^T x (N Q P), over Q*P elements."""
+    macs = Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P
+    return 2.0 * macs / (Q * P)
+
+
+def bench_ssd(torch, gen, ssm, steps, fwd_ms):
+    """The 2.8B-shaped layer in the SSD form: 80 heads of 64 channels with one decay rate and step
+    size per head, N = 16, bf16; three kernels (chunk states, state passing, chunk outputs)."""
+    sp = gen.SSD_LAYER
+    Bt, H, P, N, L = sp["batch"], sp["heads"], sp["headdim"], sp["dstate"], sp["seqlen"]
+    x = gen.ssd_inputs(Bt, H, P, N, L, sp["dtype"], seed=2)
+    copies = 3
+    ins = [{k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()} for _ in range(copies)]
+    y = torch.empty_like(ins[0]["x"])
+    last = torch.empty((Bt, H * P, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        g = ins[i % copies]
+        ssm.ssd_fwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"], True, y=y,
+                    last_state=last)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = Bt * H * P * L
+    by = el * 2 * 3 + Bt * H * L * 2 + 2 * Bt * N * L * 2 + H * P * 4 + 2 * H * 4 + Bt * H * P * N * 4
+    gbs = by / (ms * 1e-3) / 1e9
+    tf = el * ssd_flops_per_element(N) / (ms * 1e-3) / 1e12
+    return {"workload": f"2.8B-shaped layer as SSD: B={Bt}, {H} heads x {P} channels, N={N}, L={L}, bf16",
+            "steps": steps, "ms_per_step": ms, "value": el / (ms * 1e-3), "unit": "elements/s",
+            "hbm": {"achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                    "bytes_per_step": by},
+            "mfma": {"achieved": tf, "peak": 2500.0, "unit": "TFLOP/s", "frac": tf / 2500.0,
+                     "flops_per_element": ssd_flops_per_element(N), "dtype": "bf16"},
+            "vs_selective_scan": fwd_ms / ms, "inputs_rotated": copies,
+            "note": "bound by HBM (about 6 bytes against 145 matrix-core flops per element)"}
 
 
 def bench_conv(torch, np, ssm, steps, K=4):
