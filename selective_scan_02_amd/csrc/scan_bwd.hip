@@ -882,6 +882,27 @@ unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+int bwd_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Workgroups of `threads` threads of `kernel` resident per CU (at least 1).
+template <typename K>
+int resident_blocks(K kernel, int threads) {
+  int b = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, threads, 0) != hipSuccess || b < 1) b = 1;
+  return b;
+}
+
 // The fast kernels need whole chunks of 8 steps in 16-byte pieces and at least 8 states.
 bool fast_ok(const BwdParams& p) {
   if (p.dstate < kSPW || p.seqlen % kCT != 0) return false;
@@ -903,13 +924,49 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   a.groups = (int)((p.dim + kWave - 1) / kWave);
   const int64_t L = p.seqlen, chans = a.chans;
   const int64_t units = p.batch * a.groups;  // workgroups per segment
-  // segments: enough main-pass waves for every SIMD about four times over, each segment at
-  // least 4 chunks long
-  int64_t nseg = std::max<int64_t>(1, (4096 + units * W - 1) / (units * W));
-  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, L / (4 * CT)));
-  int64_t seg_len = (L + nseg - 1) / nseg;
-  seg_len = (seg_len + CT - 1) / CT * CT;
-  nseg = (L + seg_len - 1) / seg_len;
+  // Segment count from a cost model: each pass takes (rounds of resident workgroups) x (steps
+  // per segment + a start-up cost), with the resident count from the kernels' occupancy on this
+  // device; the main pass weighs twice a pre-pass.  Segments are at least 4 chunks long.
+  struct Slots {
+    int64_t main, ck, adj;
+  };
+  static const Slots sl = [] {
+    const int64_t cus = bwd_cu_count();
+    if constexpr (FAST)
+      return Slots{cus * resident_blocks(fbwd_main_kernel<N, T>, kWave * W),
+                   cus * resident_blocks(fbwd_checkpoint_kernel<N, T>, kWave),
+                   cus * resident_blocks(fbwd_adjoint_aggregate_kernel<N, T>, kWave)};
+    else
+      return Slots{cus * resident_blocks(bwd_main_kernel<N, T>, kWave),
+                   cus * resident_blocks(bwd_checkpoint_kernel<N, T>, kWave),
+                   cus * resident_blocks(bwd_adjoint_aggregate_kernel<N, T>, kWave)};
+  }();
+  const int64_t slots_main = sl.main, slots_ck = sl.ck, slots_adj = sl.adj;
+  int64_t nseg = 1, seg_len = (L + CT - 1) / CT * CT;
+  {
+    const int64_t max_seg = std::max<int64_t>(1, std::min<int64_t>(8192, L / (4 * CT)));
+    int64_t best = -1;
+    const auto rounds = [](int64_t wgs, int64_t slots) { return (wgs + slots - 1) / slots; };
+    const auto consider = [&](int64_t k) {
+      if (k < 1 || k > max_seg) return;
+      const int64_t len = ((L + k - 1) / k + CT - 1) / CT * CT;
+      const int64_t real = (L + len - 1) / len;
+      // a workgroup's start (first loads, checkpoint, carries) costs about 4 chunks
+      const int64_t cost = (len + 4 * CT) * (2 * rounds(units * real, slots_main) + rounds(units * real, slots_ck) +
+                                             (real > 1 ? rounds(units * (real - 1), slots_adj) : 0));
+      if (best < 0 || cost < best || (cost == best && real < nseg)) {
+        best = cost;
+        nseg = real;
+        seg_len = len;
+      }
+    };
+    // every count up to 64, and the counts that fill whole rounds of the main pass or the checkpoint pass
+    for (int64_t k = 1; k <= 64; ++k) consider(k);
+    for (int64_t m = 1; m <= 64; ++m) {
+      consider(m * slots_main / units);
+      consider(m * slots_ck / units);
+    }
+  }
   a.seg_len = seg_len;
   a.nseg = (int)nseg;
   const int64_t nchunks = (L + CT - 1) / CT;
