@@ -475,6 +475,35 @@ struct Row8<float> {
   }
 };
 
+// Per-channel input rows are staged through LDS in tiles of kSC steps for the 64 channels of a
+// group: consecutive threads take consecutive 16-byte pieces along a row, so every row segment
+// is read once and whole (a lane reading only its own row, 16 bytes at a time, leaves most of
+// each cache line to be fetched again by later chunks once other rows have evicted it).
+constexpr int kSC = 32;  // steps per staged tile (4 chunks)
+template <typename T>
+struct Tile {
+  static constexpr int kPiece = 16 / (int)sizeof(T);              // elements per 16-byte piece
+  static constexpr int kRow = kSC + kPiece;                       // padded row (elements)
+  static constexpr int kPieces = kSC / kPiece;                    // pieces per row
+};
+
+// Stage steps [ts0, ts1) (a multiple of 8, at most kSC) of `nt` tensors: rows of the 64 channels
+// of group `grp` of batch row `b` (channels past the end repeat the last one).
+template <typename T>
+__device__ __forceinline__ void stage_rows(T (*tile)[kWave][Tile<T>::kRow], const T* const* bases, int nt,
+                                           const BwdArgs& a, int64_t b, int64_t grp, int64_t ts0, int64_t ts1,
+                                           int tid, int nthreads) {
+  constexpr int P = Tile<T>::kPieces, E = Tile<T>::kPiece;
+  for (int pc = tid; pc < nt * kWave * P; pc += nthreads) {
+    const int k = pc / (kWave * P), r = (pc / P) % kWave, pi = pc % P;
+    const int64_t ts = ts0 + (int64_t)pi * E;
+    if (ts < ts1) {
+      const int64_t ch = b * a.dim + std::min<int64_t>(grp * kWave + r, a.dim - 1);
+      *(uint4*)&tile[k][r][pi * E] = *(const uint4*)(bases[k] + ch * a.seqlen + ts);
+    }
+  }
+}
+
 // Cross-lane sums without LDS.  v_permlane32_swap exchanges lanes 32..63 of its first operand
 // with lanes 0..31 of its second, v_permlane16_swap the odd 16-lane rows of the first with the
 // even rows of the second; adding the two swapped registers halves the lanes a sum spans.
@@ -513,15 +542,17 @@ __device__ __forceinline__ float reduce8(const float (&v)[8], bool hi8) {
 // 1'. Checkpoint pass, 16-byte rows.
 template <int N, typename T>
 __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
+  using TL = Tile<T>;
   __shared__ __align__(16) float sB[kCT][N];
+  __shared__ __align__(16) T sIn[2][kWave][TL::kRow];  // u, delta
   const Lane l = lane_of(a);
+  const int64_t grp = blockIdx.x % a.groups;
   const int seg = blockIdx.y;
   const int64_t L = a.seqlen;
   const int64_t t0 = (int64_t)seg * a.seg_len;
   const int64_t t1 = std::min(t0 + a.seg_len, L);
-  const T* __restrict__ u = (const T*)a.u + l.ch * L;
-  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
   const T* __restrict__ Bp = (const T*)a.B + l.b * N * L;
+  const T* const bases[2] = {(const T*)a.u, (const T*)a.delta};
   float A2[N], h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
@@ -530,20 +561,15 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
   }
   const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
   float cum = 0.0f;
-  // the next chunk's rows are fetched while the current one is computed
+  // the next chunk's B rows are fetched while the current one is computed
   using Raw = typename Row8<T>::Raw;
-  Raw nu, nd, nb{};
+  Raw nb{};
   const T* brow = Bp + (int64_t)(l.lane < N ? l.lane : 0) * L;
-  nu = Row8<T>::fetch(u + t0);
-  nd = Row8<T>::fetch(dl + t0);
   if (l.lane < N) nb = Row8<T>::fetch(brow + t0);
   for (int64_t tc = t0; tc < t1; tc += kCT) {
-    const Raw ru = nu, rd = nd, rb = nb;
-    if (tc + kCT < t1) {
-      nu = Row8<T>::fetch(u + tc + kCT);
-      nd = Row8<T>::fetch(dl + tc + kCT);
-      if (l.lane < N) nb = Row8<T>::fetch(brow + tc + kCT);
-    }
+    if ((tc - t0) % kSC == 0) stage_rows<T>(sIn, bases, 2, a, l.b, grp, tc, std::min(tc + kSC, t1), l.lane, kWave);
+    const Raw rb = nb;
+    if (tc + kCT < t1 && l.lane < N) nb = Row8<T>::fetch(brow + tc + kCT);
     if (tc > t0 && l.active) {
       const int64_t kg = tc / kCT;
       float4* ck = (float4*)(a.ck_h + (kg * a.chans + l.ch) * N);
@@ -551,9 +577,6 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
       for (int n = 0; n < N; n += 4) ck[n / 4] = make_float4(h[n], h[n + 1], h[n + 2], h[n + 3]);
       a.ck_dt[kg * a.chans + l.ch] = cum;
     }
-    float uv[kCT], dv[kCT];
-    Row8<T>::unpack(ru, uv);
-    Row8<T>::unpack(rd, dv);
     if (l.lane < N) {
       float bv[kCT];
       Row8<T>::unpack(rb, bv);
@@ -561,6 +584,10 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
       for (int i = 0; i < kCT; ++i) sB[i][l.lane] = bv[i];
     }
     __syncthreads();
+    const int off = (int)((tc - t0) % kSC);
+    float uv[kCT], dv[kCT];
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[0][l.lane][off]), uv);
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[1][l.lane][off]), dv);
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
       const float dt = step_size(dv[i] + bias, a.softplus);
@@ -588,16 +615,18 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
 // 3a'. Adjoint aggregate, 16-byte rows.
 template <int N, typename T>
 __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a) {
+  using TL = Tile<T>;
   __shared__ __align__(16) float sC[kCT][N];
+  __shared__ __align__(16) T sIn[3][kWave][TL::kRow];  // delta, dy, z
   const Lane l = lane_of(a);
+  const int64_t grp = blockIdx.x % a.groups;
   const int seg = blockIdx.y + 1;
   const int64_t L = a.seqlen;
   const int64_t t0 = (int64_t)seg * a.seg_len;
   const int64_t t1 = std::min(t0 + a.seg_len, L);
-  const T* __restrict__ dl = (const T*)a.delta + l.ch * L;
-  const T* __restrict__ dy = (const T*)a.dy + l.ch * L;
-  const T* __restrict__ zz = a.z ? (const T*)a.z + l.ch * L : nullptr;
+  const bool gated = a.z != nullptr;
   const T* __restrict__ Cp = (const T*)a.C + l.b * N * L;
+  const T* const bases[3] = {(const T*)a.delta, (const T*)a.dy, (const T*)a.z};
   float A2[N], lam[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
@@ -606,27 +635,15 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
   }
   const float bias = a.dt_bias ? a.dt_bias[l.dd] : 0.0f;
   using Raw = typename Row8<T>::Raw;
-  Raw nd, ng, nz{}, nc{};
+  Raw nc{};
   const T* crow = Cp + (int64_t)(l.lane < N ? l.lane : 0) * L;
-  {
-    const int64_t tc = t1 - kCT;
-    nd = Row8<T>::fetch(dl + tc);
-    ng = Row8<T>::fetch(dy + tc);
-    if (zz) nz = Row8<T>::fetch(zz + tc);
-    if (l.lane < N) nc = Row8<T>::fetch(crow + tc);
-  }
+  if (l.lane < N) nc = Row8<T>::fetch(crow + t1 - kCT);
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
-    const Raw rd = nd, rg = ng, rz = nz, rc = nc;
-    if (tc - kCT >= t0) {
-      nd = Row8<T>::fetch(dl + tc - kCT);
-      ng = Row8<T>::fetch(dy + tc - kCT);
-      if (zz) nz = Row8<T>::fetch(zz + tc - kCT);
-      if (l.lane < N) nc = Row8<T>::fetch(crow + tc - kCT);
-    }
-    float dv[kCT], gv[kCT], zv[kCT];
-    Row8<T>::unpack(rd, dv);
-    Row8<T>::unpack(rg, gv);
-    if (zz) Row8<T>::unpack(rz, zv);
+    const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
+    if (tc == t1 - kCT || tc + kCT == j0 + kSC)
+      stage_rows<T>(sIn, bases, gated ? 3 : 2, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane, kWave);
+    const Raw rc = nc;
+    if (tc - kCT >= t0 && l.lane < N) nc = Row8<T>::fetch(crow + tc - kCT);
     if (l.lane < N) {
       float cv[kCT];
       Row8<T>::unpack(rc, cv);
@@ -634,10 +651,15 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
       for (int i = 0; i < kCT; ++i) sC[i][l.lane] = cv[i];
     }
     __syncthreads();
+    const int off = (int)(tc - j0);
+    float dv[kCT], gv[kCT], zv[kCT];
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[0][l.lane][off]), dv);
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[1][l.lane][off]), gv);
+    if (gated) Row8<T>::unpack(Row8<T>::fetch(&sIn[2][l.lane][off]), zv);
 #pragma unroll
     for (int i = kCT - 1; i >= 0; --i) {
       const float dt = step_size(dv[i] + bias, a.softplus);
-      const float ds = zz ? gv[i] * silu(zv[i]) : gv[i];
+      const float ds = gated ? gv[i] * silu(zv[i]) : gv[i];
       const float4* cr = (const float4*)sC[i];
 #pragma unroll
       for (int n = 0; n < N; n += 4) {
@@ -667,6 +689,7 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   __shared__ __align__(16) float sBC[W][2][kCT][kSPW];
   __shared__ float sS[W][kCT][kWave];
   __shared__ float sP[W][2][kCT][kWave];
+  __shared__ __align__(16) T sIn[4][kWave][Tile<T>::kRow];  // u, delta, dy, z
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int64_t b = blockIdx.x / a.groups;
@@ -680,10 +703,7 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   const int64_t t0 = (int64_t)seg * a.seg_len;
   const int64_t t1 = std::min(t0 + a.seg_len, L);
   const int n0 = w * kSPW;
-  const T* __restrict__ u = (const T*)a.u + ch * L;
-  const T* __restrict__ dl = (const T*)a.delta + ch * L;
-  const T* __restrict__ dy = (const T*)a.dy + ch * L;
-  const T* __restrict__ zz = a.z ? (const T*)a.z + ch * L : nullptr;
+  const bool zz = a.z != nullptr;  // gated
   const T* __restrict__ Bp = (const T*)a.B + b * N * L;
   const T* __restrict__ Cp = (const T*)a.C + b * N * L;
   const int jr = reduce8_index(lane);
@@ -710,14 +730,11 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   // the next chunk's rows and checkpoint are fetched while the current one is computed
   using Raw = typename Row8<T>::Raw;
   const T* bcrow = (lane < kSPW ? Bp : Cp) + (int64_t)(n0 + (lane & 7)) * L;
-  Raw nu, nd, ng, nz{}, nbc{};
+  Raw nbc{};
+  const T* const bases[4] = {(const T*)a.u, (const T*)a.delta, (const T*)a.dy, (const T*)a.z};
   float4 nk0 = make_float4(0.f, 0.f, 0.f, 0.f), nk1 = nk0;
   float nkd = 0.0f;
   auto fetch = [&](int64_t tc) {
-    nu = Row8<T>::fetch(u + tc);
-    nd = Row8<T>::fetch(dl + tc);
-    ng = Row8<T>::fetch(dy + tc);
-    if (zz) nz = Row8<T>::fetch(zz + tc);
     if (lane < 2 * kSPW) nbc = Row8<T>::fetch(bcrow + tc);
     if (tc > t0) {
       const int64_t kg = tc / kCT;
@@ -729,7 +746,10 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   };
   fetch(t1 - kCT);
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
-    const Raw ru = nu, rd = nd, rg = ng, rz = nz, rbc = nbc;
+    const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
+    if (tc == t1 - kCT || tc + kCT == j0 + kSC)
+      stage_rows<T>(sIn, bases, zz ? 4 : 3, a, b, grp, j0, std::min(j0 + kSC, t1), threadIdx.x, kWave * W);
+    const Raw rbc = nbc;
     const float4 k0 = nk0, k1 = nk1;
     const float kd = nkd;
     if (tc - kCT >= t0) fetch(tc - kCT);
@@ -742,17 +762,19 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
 #pragma unroll
       for (int j = 0; j < kSPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * kd), hin[j], cv[j]);
     }
-    float uv[kCT], dv[kCT], gv[kCT], zv[kCT];
-    Row8<T>::unpack(ru, uv);
-    Row8<T>::unpack(rd, dv);
-    Row8<T>::unpack(rg, gv);
-    if (zz) Row8<T>::unpack(rz, zv);
     if (lane < 2 * kSPW) {
       float bv[kCT];
       Row8<T>::unpack(rbc, bv);
 #pragma unroll
       for (int i = 0; i < kCT; ++i) sBC[w][lane >> 3][i][lane & 7] = bv[i];
     }
+    __syncthreads();
+    const int off = (int)(tc - j0);
+    float uv[kCT], dv[kCT], gv[kCT], zv[kCT];
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[0][lane][off]), uv);
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[1][lane][off]), dv);
+    Row8<T>::unpack(Row8<T>::fetch(&sIn[2][lane][off]), gv);
+    if (zz) Row8<T>::unpack(Row8<T>::fetch(&sIn[3][lane][off]), zv);
     float dt[kCT], dut[kCT], ds[kCT];
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
@@ -761,7 +783,6 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
       ds[i] = zz ? gv[i] * silu(zv[i]) : gv[i];
       if (!active) ds[i] = 0.0f;
     }
-    __syncthreads();
     // forward over the chunk
     float hp[kCT][kSPW];
     float keepC = 0.0f;
@@ -915,6 +936,7 @@ bool fast_ok(const BwdParams& p) {
 template <int N, typename T, bool FAST>
 hipError_t run(const BwdParams& p, hipStream_t stream) {
   constexpr int CT = FAST ? kCT : Chunk<N>::T;
+  constexpr int GR = FAST ? kSC : CT;     // segment lengths are multiples of this (whole staged tiles)
   constexpr int W = FAST ? N / kSPW : 1;  // waves per workgroup of the main pass
   BwdArgs a{};
   a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
@@ -942,14 +964,14 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
                    cus * resident_blocks(bwd_adjoint_aggregate_kernel<N, T>, kWave)};
   }();
   const int64_t slots_main = sl.main, slots_ck = sl.ck, slots_adj = sl.adj;
-  int64_t nseg = 1, seg_len = (L + CT - 1) / CT * CT;
+  int64_t nseg = 1, seg_len = (L + GR - 1) / GR * GR;
   {
     const int64_t max_seg = std::max<int64_t>(1, std::min<int64_t>(8192, L / (4 * CT)));
     int64_t best = -1;
     const auto rounds = [](int64_t wgs, int64_t slots) { return (wgs + slots - 1) / slots; };
     const auto consider = [&](int64_t k) {
       if (k < 1 || k > max_seg) return;
-      const int64_t len = ((L + k - 1) / k + CT - 1) / CT * CT;
+      const int64_t len = ((L + k - 1) / k + GR - 1) / GR * GR;
       const int64_t real = (L + len - 1) / len;
       // a workgroup's start (first loads, checkpoint, carries) costs about 4 chunks
       const int64_t cost = (len + 4 * CT) * (2 * rounds(units * real, slots_main) + rounds(units * real, slots_ck) +

@@ -90,6 +90,11 @@ SMALL = [
     (1, 20, 64, 77, "f32", {"h0": True}),
     (1, 5, 16, 1, "f32", {"h0": True}),
     (1, 192, 16, 2048, "bf16", {}),
+    # 16-byte rows (fast path): partial staged tiles, one to eight waves per channel group
+    (2, 130, 16, 520, "bf16", {"h0": True}),
+    (1, 64, 8, 264, "f32", {"with_z": False}),
+    (2, 100, 64, 136, "bf16", {}),
+    (1, 70, 32, 4104, "f32", {"h0": True}),
 ]
 
 
