@@ -121,6 +121,15 @@ def test_bwd_full_2p8b_layer():
     compare(x, got, ref, TOL["bf16"])
 
 
+def test_bwd_full_130m_layer():
+    x = gen.scan_inputs(1)
+    note("bwd 130M-shaped layer (B=8, D=1536, N=16, L=2048, bf16), every output against the oracle")
+    dy = upstream(x, 1)
+    got = gpu_bwd(x, dy)
+    ref = ref_bwd(x, dy)
+    compare(x, got, ref, TOL["bf16"])
+
+
 def test_bwd_is_deterministic():
     x = gen.random_scan_inputs(2, 300, 16, 1500, "f32", seed=4)
     note("bwd run twice, bitwise")
