@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kWave) void bwd_checkpoint_kernel(BwdArgs a) {
   a.seg_dt[(int64_t)seg * a.chans + l.ch] = cum;
 }
 
+constexpr int kCarryBatch = 16;
+
 // 2. Forward carry, one thread per (channel, n), in place over seg_h.
 __global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* seg_h, const float* seg_dt, const float* A,
                                                             const float* h0, int64_t chans, int64_t dim, int N,
@@ -154,11 +156,22 @@ __global__ __launch_bounds__(256) void bwd_fwd_carry_kernel(float* seg_h, const 
   const int64_t ch = i / N;
   const float A2 = A[(ch % dim) * N + (i % N)] * kLog2e;
   float h = h0 ? h0[i] : 0.0f;
-  for (int s = 0; s < nseg; ++s) {
-    const int64_t k = (int64_t)s * chans * N + i;
-    const float agg = seg_h[k];
-    seg_h[k] = h;
-    h = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + ch]), h, agg);
+  // 16 segments at a time, their loads all in flight before the first is used
+  for (int s0 = 0; s0 < nseg; s0 += kCarryBatch) {
+    const int nb = nseg - s0 < kCarryBatch ? nseg - s0 : kCarryBatch;
+    float agg[kCarryBatch], sdt[kCarryBatch];
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k)
+      if (k < nb) {
+        agg[k] = seg_h[(int64_t)(s0 + k) * chans * N + i];
+        sdt[k] = seg_dt[(int64_t)(s0 + k) * chans + ch];
+      }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k)
+      if (k < nb) {
+        seg_h[(int64_t)(s0 + k) * chans * N + i] = h;
+        h = __builtin_fmaf(ex2(A2 * sdt[k]), h, agg[k]);
+      }
   }
 }
 
@@ -204,11 +217,23 @@ __global__ __launch_bounds__(256) void bwd_adjoint_carry_kernel(float* seg_l, co
   const int64_t ch = i / N;
   const float A2 = A[(ch % dim) * N + (i % N)] * kLog2e;
   float mu = 0.0f;
-  for (int s = nseg - 1; s >= 0; --s) {
-    const int64_t k = (int64_t)s * chans * N + i;
-    const float local = s > 0 ? seg_l[k] : 0.0f;
-    seg_l[k] = mu;
-    mu = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + ch]), mu, local);
+  // 16 segments at a time (last first), their loads all in flight before the first is used
+  for (int s0 = nseg - 1; s0 >= 0; s0 -= kCarryBatch) {
+    const int nb = s0 + 1 < kCarryBatch ? s0 + 1 : kCarryBatch;
+    float loc[kCarryBatch], sdt[kCarryBatch];
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k)
+      if (k < nb) {
+        const int s = s0 - k;
+        loc[k] = s > 0 ? seg_l[(int64_t)s * chans * N + i] : 0.0f;
+        sdt[k] = seg_dt[(int64_t)s * chans + ch];
+      }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k)
+      if (k < nb) {
+        seg_l[(int64_t)(s0 - k) * chans * N + i] = mu;
+        mu = __builtin_fmaf(ex2(A2 * sdt[k]), mu, loc[k]);
+      }
   }
 }
 

@@ -619,11 +619,24 @@ __global__ __launch_bounds__(256) void carry_kernel(float* seg_h, const float* s
   const int n = (int)(i % N);
   const float A2 = A[(chn % dim) * N + n] * kLog2e;
   float h = h0 ? h0[i] : 0.0f;
-  for (int s = 0; s < nseg; ++s) {
-    const int64_t kk = (int64_t)s * chans * N + i;
-    const float agg = seg_h[kk];
-    seg_h[kk] = h;
-    h = __builtin_fmaf(ex2(A2 * seg_dt[(int64_t)s * chans + chn]), h, agg);
+  // 16 segments at a time: their loads are all in flight before the first is used (few threads
+  // run this loop, so it is bound by load latency, not bandwidth)
+  constexpr int kBatch = 16;
+  for (int s0 = 0; s0 < nseg; s0 += kBatch) {
+    const int nb = nseg - s0 < kBatch ? nseg - s0 : kBatch;
+    float agg[kBatch], sdt[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (k < nb) {
+        agg[k] = seg_h[(int64_t)(s0 + k) * chans * N + i];
+        sdt[k] = seg_dt[(int64_t)(s0 + k) * chans + chn];
+      }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (k < nb) {
+        seg_h[(int64_t)(s0 + k) * chans * N + i] = h;
+        h = __builtin_fmaf(ex2(A2 * sdt[k]), h, agg[k]);
+      }
   }
 }
 
