@@ -6,12 +6,12 @@
 // the part on reorganising the SSM into matrix computation): per head,
 //   y_t = sum_{s <= t} (C_t . B_s) exp(a (cs_t - cs_s)) Delta_s x_s,   cs_t = sum_{r <= t} Delta_r.
 // Cut into chunks of Q = 64 steps, this is three dense products per chunk plus a short
-// recurrence over chunks:
-//   1. chunk state (ssd_chunk_state_kernel): S_c = sum_s B_s w_s x_s^T, w_s = exp(a (cs_end - cs_s)) Delta_s
-//      -- [N x Q] x [Q x P] on MFMA;
-//   2. state passing (ssd_state_pass_kernel): H_c = exp(a cs_end,c) H_{c-1} + S_c, one thread per
-//      (head, n, p), sequential over chunks; H_{c-1} replaces S_c in place;
-//   3. chunk output (ssd_chunk_scan_kernel): Y = (G o decay o Delta) X + diag(exp(a cs_t)) C H_{c-1},
+// recurrence over chunks, in two kernels:
+//   1. chunk states and state passing (ssd_state_kernel): S_c = sum_s B_s w_s x_s^T,
+//      w_s = exp(a (cs_end - cs_s)) Delta_s -- [N x Q] x [Q x 16] on MFMA per 16-column tile -- and
+//      H_c = exp(a cs_end,c) H_{c-1} + S_c, the chunks of a head walked in order, H in registers;
+//      the state entering each chunk is written out;
+//   2. chunk output (ssd_chunk_scan_kernel): Y = (G o decay o Delta) X + diag(exp(a cs_t)) C H_{c-1},
 //      G = C B^T -- [Q x N] x [N x Q], [Q x Q] x [Q x P] and [Q x N] x [N x P] on MFMA; then the
 //      D skip and the SiLU gate.
 // MFMA operands are bf16 with fp32 accumulation.  x, B and C are the bf16 inputs themselves.  The
@@ -52,8 +52,7 @@ struct SsdArgs {
   const float* h0;       // [batch, H*P, N] or null
   __bf16* y;
   float* last;           // [batch, H*P, N] or null
-  float* S;              // [batch*H, chunks, N, P]: chunk states, then incoming states
-  float* csum;           // [batch*H, chunks]: sum of Delta over the chunk
+  float* S;              // [batch*H, chunks, N, P]: the state entering each chunk
   int64_t batch, heads, seqlen;
   int chunks, softplus;
 };
@@ -62,15 +61,26 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ short bf16_bits(float v) {
-  const __bf16 h = (__bf16)v;
-  return __builtin_bit_cast(short, h);
-}
-
 // v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi).
 __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
   hi = (__bf16)v;
   lo = (__bf16)(v - (float)hi);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP (the gfx9 wave scan): four row shifts scan each
+// 16-lane row, then row broadcasts of lanes 15 and 31 carry the row totals forward.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_src(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_src<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_src<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_src<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_src<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_src<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_src<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 // Step sizes of the chunk, one per lane (0 beyond the sequence), and their inclusive prefix sums.
@@ -82,66 +92,85 @@ __device__ __forceinline__ void chunk_steps(const SsdArgs& a, int64_t bh, int64_
     const float xr = (float)a.dt[bh * a.seqlen + t0 + lane] + (a.dt_bias ? a.dt_bias[h] : 0.0f);
     dl = a.softplus ? softplus(xr) : xr;
   }
-  cs = dl;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float v = __shfl_up(cs, o);
-    if (lane >= o) cs += v;
-  }
+  cs = wave_prefix_sum(dl);
 }
 
-// 1. Chunk states: one wave per (chunk, batch row x head).
+// 1+2. Chunk states and state passing: one wave per (batch row x head, 16-channel column tile),
+// walking the chunks in order with the running state H[n][p] of its 16 columns in registers --
+// in the accumulator layout of the chunk-state product, lane (q, r) holding n = 4 q + j (+ 16 nt)
+// of column p = 16 tile + r.  Per chunk: S_c = sum_s B_s w_s x_s^T on MFMA, the incoming state is
+// written out for the output kernel, then H <- exp(a cs_end) H + S_c.  The next two chunks' B, x
+// and steps are in flight while the current one is combined.
 template <int N>
-__global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
+__global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
   __shared__ float sw[kQ];
   const int lane = threadIdx.x;
-  const int c = blockIdx.x;
+  const int pt = blockIdx.x;  // column tile
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / a.heads, h = bh % a.heads;
   const int64_t L = a.seqlen;
-  const int64_t t0 = (int64_t)c * kQ;
-  const int len = (int)std::min<int64_t>(kQ, L - t0);
   const int r = lane % 16, q = lane / 16;
-  const __bf16* xh = a.x + (b * a.heads * kP + h * kP) * L + t0;
-  const __bf16* Bb = a.B + b * N * L + t0;
-  float* S = a.S + (bh * a.chunks + c) * N * kP;
-  // every global load is issued before the step sizes are needed: x and B do not depend on them
-  bf16x4 xv[kQ / 16][kP / 16];
-  uint2 braw[N / 16][kQ / 16];
-#pragma unroll
-  for (int kt = 0; kt < kQ / 16; ++kt) {
-    // lanes past the sequence end (len is a multiple of 8) supply zeros and load nothing
-    const int s = 16 * kt + 4 * q;
-    const bool in = s < len;
-#pragma unroll
-    for (int pt = 0; pt < kP / 16; ++pt)
-      xv[kt][pt] = in ? *(const bf16x4*)(xh + (int64_t)(16 * pt + r) * L + s) : bf16x4{0, 0, 0, 0};
-#pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
-      braw[nt][kt] = in ? *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + s) : make_uint2(0, 0);
-  }
-  float dl, cs;
-  chunk_steps(a, bh, t0, len, lane, dl, cs);
-  const float cs_end = __shfl(cs, kQ - 1);
+  const int p = 16 * pt + r;
   const float A2 = a.A[h] * kLog2e;
-  sw[lane] = ex2(A2 * (cs_end - cs)) * dl;
-  if (lane == 0) a.csum[bh * a.chunks + c] = cs_end;
-  __syncthreads();
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const __bf16* xrow = a.x + (b * a.heads * kP + h * kP + p) * L;  // this lane's B-operand column
+  const __bf16* Bb = a.B + b * N * L;
+  const __bf16* dtr = a.dt + bh * L;
+  const int64_t sidx0 = ((b * a.heads + h) * kP + p) * N;  // [batch, H*P, N] row of column p
+  float H[N / 16][4];
 #pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt) {
-    f32x4 acc[kP / 16];
+  for (int nt = 0; nt < N / 16; ++nt)
 #pragma unroll
-    for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 4; ++j) H[nt][j] = a.h0 ? a.h0[sidx0 + 16 * nt + 4 * q + j] : 0.0f;
+
+  // loads of one chunk: x[p][s..s+3] and B[n][s..s+3] for s = 16 kt + 4 q, n = 16 nt + r, and the step
+  // of lane s.  Two register sets alternate, so two chunks' loads are in flight ahead of the one
+  // being combined.
+  // The loads are unconditional (lanes past the sequence end read step t0 of the chunk instead) and
+  // their values are masked where they are used, so no load sits in a branch that must wait for it.
+  struct Loads {
+    bf16x4 x[kQ / 16];
+    uint2 b[N / 16][kQ / 16];
+    unsigned short dt;
+  };
+  const auto fetch = [&](int c, Loads& ld) {
+    const int64_t t0 = (int64_t)c * kQ;
+    const int len = (int)std::min<int64_t>(kQ, L - t0);
 #pragma unroll
     for (int kt = 0; kt < kQ / 16; ++kt) {
       const int s = 16 * kt + 4 * q;
-      // A operand: B[n][s..s+3] * w[s..s+3], n = 16 nt + r, as a hi/lo pair
-      bf16x4 ahi, alo;
-      {
-        const uint2 raw = braw[nt][kt];
-        const float4 wv = *(const float4*)&sw[s];
-        const float bw[4] = {__uint_as_float(raw.x << 16) * wv.x, __uint_as_float(raw.x & 0xffff0000u) * wv.y,
-                             __uint_as_float(raw.y << 16) * wv.z, __uint_as_float(raw.y & 0xffff0000u) * wv.w};
+      const int sv = s < len ? s : 0;  // len is a multiple of 8: a lane's 4 steps are all in or all out
+      ld.x[kt] = *(const bf16x4*)(xrow + t0 + sv);
+#pragma unroll
+      for (int nt = 0; nt < N / 16; ++nt) ld.b[nt][kt] = *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + t0 + sv);
+    }
+    ld.dt = ((const unsigned short*)dtr)[t0 + (lane < len ? lane : 0)];
+  };
+  const auto combine = [&](int c, const Loads& ld) {
+    const int64_t t0 = (int64_t)c * kQ;
+    const int len = (int)std::min<int64_t>(kQ, L - t0);
+    // step sizes and their prefix sums (lane = step)
+    const float raw = __uint_as_float((uint32_t)ld.dt << 16) + bias;
+    const float dl = lane < len ? (a.softplus ? softplus(raw) : raw) : 0.0f;
+    const float cs = wave_prefix_sum(dl);
+    const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), kQ - 1));
+    sw[lane] = ex2(A2 * (cs_end - cs)) * dl;
+    __syncthreads();
+    // S_c, with the decay-weighted B as hi/lo bf16 A operands
+    f32x4 sc[N / 16];
+#pragma unroll
+    for (int nt = 0; nt < N / 16; ++nt) {
+      // hi and lo products accumulate separately: two independent MFMA chains
+      f32x4 shi = {0.0f, 0.0f, 0.0f, 0.0f}, slo = shi;
+#pragma unroll
+      for (int kt = 0; kt < kQ / 16; ++kt) {
+        const bool in = 16 * kt + 4 * q < len;
+        const float4 wv = *(const float4*)&sw[16 * kt + 4 * q];  // zero past the sequence end (Delta = 0)
+        const uint2 raw2 = ld.b[nt][kt];
+        const bf16x4 xv = in ? ld.x[kt] : bf16x4{0, 0, 0, 0};
+        const float bw[4] = {__uint_as_float(raw2.x << 16) * wv.x, __uint_as_float(raw2.x & 0xffff0000u) * wv.y,
+                             __uint_as_float(raw2.y << 16) * wv.z, __uint_as_float(raw2.y & 0xffff0000u) * wv.w};
+        bf16x4 ahi, alo;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           __bf16 hi, lo;
@@ -149,50 +178,40 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_kernel(SsdArgs a) {
           ahi[j] = __builtin_bit_cast(short, hi);
           alo[j] = __builtin_bit_cast(short, lo);
         }
+        shi = mfma16(ahi, xv, shi);
+        slo = mfma16(alo, xv, slo);
       }
-#pragma unroll
-      for (int pt = 0; pt < kP / 16; ++pt) {
-        acc[pt] = mfma16(ahi, xv[kt][pt], acc[pt]);
-        acc[pt] = mfma16(alo, xv[kt][pt], acc[pt]);
-      }
+      sc[nt] = shi + slo;
     }
+    __syncthreads();  // sw is rewritten by the next chunk
+    // hand the incoming state to the output kernel, then advance it over the chunk
+    float* Sin = a.S + (bh * a.chunks + c) * N * kP;
+    const float decay = ex2(A2 * cs_end);
 #pragma unroll
-    for (int pt = 0; pt < kP / 16; ++pt)
+    for (int nt = 0; nt < N / 16; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[(16 * nt + 4 * q + j) * kP + 16 * pt + r] = acc[pt][j];
-  }
-}
-
-// 2. State passing: one thread per (batch row x head, n, p).
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a, int N) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t per = (int64_t)N * kP;
-  if (i >= a.batch * a.heads * per) return;
-  const int64_t bh = i / per, rem = i % per;
-  const int n = (int)(rem / kP), p = (int)(rem % kP);
-  const int64_t b = bh / a.heads, h = bh % a.heads;
-  const int64_t state_idx = ((b * a.heads + h) * kP + p) * N + n;  // [batch, H*P, N]
-  const float A2 = a.A[h] * kLog2e;
-  float hs = a.h0 ? a.h0[state_idx] : 0.0f;
-  // 16 chunks at a time: their loads are all in flight before the first is used
-  constexpr int kBatch = 16;
-  for (int c0 = 0; c0 < a.chunks; c0 += kBatch) {
-    const int nb = std::min(kBatch, a.chunks - c0);
-    float sv[kBatch], ev[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (k < nb) {
-        sv[k] = a.S[(bh * a.chunks + c0 + k) * per + rem];
-        ev[k] = a.csum[bh * a.chunks + c0 + k];
+      for (int j = 0; j < 4; ++j) {
+        Sin[(16 * nt + 4 * q + j) * kP + p] = H[nt][j];
+        H[nt][j] = __builtin_fmaf(decay, H[nt][j], sc[nt][j]);
       }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (k < nb) {
-        a.S[(bh * a.chunks + c0 + k) * per + rem] = hs;
-        hs = __builtin_fmaf(ex2(A2 * ev[k]), hs, sv[k]);
-      }
+  };
+  Loads la, lb;
+  fetch(0, la);
+  if (a.chunks > 1) fetch(1, lb);
+  for (int c = 0; c < a.chunks; c += 2) {
+    combine(c, la);
+    if (c + 2 < a.chunks) fetch(c + 2, la);
+    if (c + 1 < a.chunks) {
+      combine(c + 1, lb);
+      if (c + 3 < a.chunks) fetch(c + 3, lb);
+    }
   }
-  if (a.last) a.last[state_idx] = hs;
+  if (a.last) {
+#pragma unroll
+    for (int nt = 0; nt < N / 16; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.last[sidx0 + 16 * nt + 4 * q + j] = H[nt][j];
+  }
 }
 
 // 3. Chunk outputs: four waves per (chunk, batch row x head); wave w owns output rows
@@ -377,22 +396,15 @@ hipError_t run(const SsdParams& p, hipStream_t stream) {
   a.batch = p.batch; a.heads = p.heads; a.seqlen = p.seqlen; a.softplus = p.softplus;
   a.chunks = (int)((p.seqlen + kQ - 1) / kQ);
   const int64_t bh = p.batch * p.heads;
-  const size_t nS = (size_t)bh * a.chunks * N * kP, nc = (size_t)bh * a.chunks;
+  const size_t nS = (size_t)bh * a.chunks * N * kP;
   void* scratch = nullptr;
-  hipError_t err = scratch_alloc(&scratch, (nS + (nc + 63) / 64 * 64) * sizeof(float), stream);
+  hipError_t err = scratch_alloc(&scratch, nS * sizeof(float), stream);
   if (err != hipSuccess) return err;
   a.S = (float*)scratch;
-  a.csum = a.S + nS;
-  const dim3 grid((unsigned)a.chunks, (unsigned)bh);
-  hipLaunchKernelGGL((ssd_chunk_state_kernel<N>), grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((ssd_state_kernel<N>), dim3(kP / 16, (unsigned)bh), dim3(64), 0, stream, a);
   err = hipGetLastError();
   if (err == hipSuccess) {
-    const int64_t threads = bh * N * kP;
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, N);
-    err = hipGetLastError();
-  }
-  if (err == hipSuccess) {
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N>), dim3((unsigned)a.chunks, (unsigned)bh), dim3(256), 0, stream, a);
     err = hipGetLastError();
   }
   const hipError_t ferr = hipFreeAsync(scratch, stream);
