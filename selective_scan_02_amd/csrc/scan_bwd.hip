@@ -512,19 +512,37 @@ struct Tile {
   static constexpr int kPieces = kSC / kPiece;                    // pieces per row
 };
 
-// Stage steps [ts0, ts1) (a multiple of 8, at most kSC) of `nt` tensors: rows of the 64 channels
-// of group `grp` of batch row `b` (channels past the end repeat the last one).
-template <typename T>
-__device__ __forceinline__ void stage_rows(T (*tile)[kWave][Tile<T>::kRow], const T* const* bases, int nt,
+// Stage steps [ts0, ts1) (a multiple of 8, at most kSC) of the first `nt` of the NT tensors: rows
+// of the 64 channels of group `grp` of batch row `b` (channels past the end repeat the last one).
+// NTH threads take a tensor's pieces in rounds of 4 per thread; a round's loads are all issued
+// before the first is written to LDS.
+template <typename T, int NTH, int NT>
+__device__ __forceinline__ void stage_rows(T (*tile)[kWave][Tile<T>::kRow], const T* const (&bases)[NT], int nt,
                                            const BwdArgs& a, int64_t b, int64_t grp, int64_t ts0, int64_t ts1,
-                                           int tid, int nthreads) {
-  constexpr int P = Tile<T>::kPieces, E = Tile<T>::kPiece;
-  for (int pc = tid; pc < nt * kWave * P; pc += nthreads) {
-    const int k = pc / (kWave * P), r = (pc / P) % kWave, pi = pc % P;
-    const int64_t ts = ts0 + (int64_t)pi * E;
-    if (ts < ts1) {
-      const int64_t ch = b * a.dim + std::min<int64_t>(grp * kWave + r, a.dim - 1);
-      *(uint4*)&tile[k][r][pi * E] = *(const uint4*)(bases[k] + ch * a.seqlen + ts);
+                                           int tid) {
+  constexpr int P = Tile<T>::kPieces, E = Tile<T>::kPiece, R = 4, PER = kWave * P;
+  asm volatile("" : "+v"(tid));  // addresses are recomputed per call, not held across the caller's loop
+#pragma unroll
+  for (int kk = 0; kk < NT; ++kk) {
+    if (kk >= nt) break;
+#pragma unroll 1
+    for (int base = 0; base < PER; base += NTH * R) {
+      uint4 v[R];
+      bool ok[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int pc = base + k * NTH + tid;
+        const int r = (pc / P) % kWave, pi = pc % P;
+        const int64_t ts = ts0 + (int64_t)pi * E;
+        ok[k] = pc < PER && ts < ts1;
+        const int64_t ch = b * a.dim + std::min<int64_t>(grp * kWave + r, a.dim - 1);
+        v[k] = *(const uint4*)(bases[kk] + ch * a.seqlen + (ok[k] ? ts : ts0));
+      }
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int pc = base + k * NTH + tid;
+        if (ok[k]) *(uint4*)&tile[kk][(pc / P) % kWave][(pc % P) * E] = v[k];
+      }
     }
   }
 }
@@ -592,7 +610,7 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
   const T* brow = Bp + (int64_t)(l.lane < N ? l.lane : 0) * L;
   if (l.lane < N) nb = Row8<T>::fetch(brow + t0);
   for (int64_t tc = t0; tc < t1; tc += kCT) {
-    if ((tc - t0) % kSC == 0) stage_rows<T>(sIn, bases, 2, a, l.b, grp, tc, std::min(tc + kSC, t1), l.lane, kWave);
+    if ((tc - t0) % kSC == 0) stage_rows<T, kWave, 2>(sIn, bases, 2, a, l.b, grp, tc, std::min(tc + kSC, t1), l.lane);
     const Raw rb = nb;
     if (tc + kCT < t1 && l.lane < N) nb = Row8<T>::fetch(brow + tc + kCT);
     if (tc > t0 && l.active) {
@@ -666,7 +684,7 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
     const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
     if (tc == t1 - kCT || tc + kCT == j0 + kSC)
-      stage_rows<T>(sIn, bases, gated ? 3 : 2, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane, kWave);
+      stage_rows<T, kWave, 3>(sIn, bases, gated ? 3 : 2, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane);
     const Raw rc = nc;
     if (tc - kCT >= t0 && l.lane < N) nc = Row8<T>::fetch(crow + tc - kCT);
     if (l.lane < N) {
@@ -773,7 +791,7 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
     const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
     if (tc == t1 - kCT || tc + kCT == j0 + kSC)
-      stage_rows<T>(sIn, bases, zz ? 4 : 3, a, b, grp, j0, std::min(j0 + kSC, t1), threadIdx.x, kWave * W);
+      stage_rows<T, kWave * W, 4>(sIn, bases, zz ? 4 : 3, a, b, grp, j0, std::min(j0 + kSC, t1), threadIdx.x);
     const Raw rbc = nbc;
     const float4 k0 = nk0, k1 = nk1;
     const float kd = nkd;
