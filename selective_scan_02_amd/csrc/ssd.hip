@@ -23,7 +23,8 @@
 //
 // MFMA lane layout of v_mfma_f32_16x16x16_bf16 (checked on the device with an in-bounds probe):
 // lane l supplies A[l % 16][4 (l / 16) + j] and B[4 (l / 16) + j][l % 16], j = 0..3, and receives
-// D[4 (l / 16) + j][l % 16].
+// D[4 (l / 16) + j][l % 16].  v_mfma_f32_16x16x32_bf16 is the same with 8 (l / 16) + j, j = 0..7, for
+// the reduction index.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,6 +40,7 @@ constexpr int kP = 64;  // channels per head
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct SsdArgs {
   const __bf16* x;
@@ -52,13 +54,16 @@ struct SsdArgs {
   const float* h0;       // [batch, H*P, N] or null
   __bf16* y;
   float* last;           // [batch, H*P, N] or null
-  float* S;              // [batch*H, chunks, N, P]: the state entering each chunk
+  float* S;              // the state entering each chunk: [batch*H, chunks, P/16, N/16, 64 lanes, 4]
   int64_t batch, heads, seqlen;
   int chunks, softplus;
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi).
@@ -83,18 +88,6 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
   return x;
 }
 
-// Step sizes of the chunk, one per lane (0 beyond the sequence), and their inclusive prefix sums.
-__device__ __forceinline__ void chunk_steps(const SsdArgs& a, int64_t bh, int64_t t0, int len, int lane, float& dl,
-                                            float& cs) {
-  dl = 0.0f;
-  if (lane < len) {
-    const int h = (int)(bh % a.heads);
-    const float xr = (float)a.dt[bh * a.seqlen + t0 + lane] + (a.dt_bias ? a.dt_bias[h] : 0.0f);
-    dl = a.softplus ? softplus(xr) : xr;
-  }
-  cs = wave_prefix_sum(dl);
-}
-
 // 1+2. Chunk states and state passing: one wave per (batch row x head, 16-channel column tile),
 // walking the chunks in order with the running state H[n][p] of its 16 columns in registers --
 // in the accumulator layout of the chunk-state product, lane (q, r) holding n = 4 q + j (+ 16 nt)
@@ -103,6 +96,7 @@ __device__ __forceinline__ void chunk_steps(const SsdArgs& a, int64_t bh, int64_
 // and steps are in flight while the current one is combined.
 template <int N>
 __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
+  constexpr int kDepth = 4;  // chunks whose loads are in flight (2, 4 and 8 measured within 3%)
   __shared__ float sw[kQ];
   const int lane = threadIdx.x;
   const int pt = blockIdx.x;  // column tile
@@ -123,26 +117,26 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) H[nt][j] = a.h0 ? a.h0[sidx0 + 16 * nt + 4 * q + j] : 0.0f;
 
-  // loads of one chunk: x[p][s..s+3] and B[n][s..s+3] for s = 16 kt + 4 q, n = 16 nt + r, and the step
-  // of lane s.  Two register sets alternate, so two chunks' loads are in flight ahead of the one
-  // being combined.
-  // The loads are unconditional (lanes past the sequence end read step t0 of the chunk instead) and
-  // their values are masked where they are used, so no load sits in a branch that must wait for it.
+  // loads of one chunk: x[p][s..s+7] and B[n][s..s+7] for s = 32 kt + 8 q, n = 16 nt + r (16 bytes
+  // each), and the step of lane s.  The loads of the next kDepth - 1 chunks are in flight while one
+  // is combined.  The loads are unconditional (lanes past the sequence end read step t0 of the chunk
+  // instead) and their values are masked where they are used, so no load sits in a branch that must
+  // wait for it.
   struct Loads {
-    bf16x4 x[kQ / 16];
-    uint2 b[N / 16][kQ / 16];
+    uint4 x[kQ / 32];
+    uint4 b[N / 16][kQ / 32];
     unsigned short dt;
   };
   const auto fetch = [&](int c, Loads& ld) {
     const int64_t t0 = (int64_t)c * kQ;
     const int len = (int)std::min<int64_t>(kQ, L - t0);
 #pragma unroll
-    for (int kt = 0; kt < kQ / 16; ++kt) {
-      const int s = 16 * kt + 4 * q;
-      const int sv = s < len ? s : 0;  // len is a multiple of 8: a lane's 4 steps are all in or all out
-      ld.x[kt] = *(const bf16x4*)(xrow + t0 + sv);
+    for (int kt = 0; kt < kQ / 32; ++kt) {
+      const int s = 32 * kt + 8 * q;
+      const int sv = s < len ? s : 0;  // len is a multiple of 8: a lane's 8 steps are all in or all out
+      ld.x[kt] = *(const uint4*)(xrow + t0 + sv);
 #pragma unroll
-      for (int nt = 0; nt < N / 16; ++nt) ld.b[nt][kt] = *(const uint2*)(Bb + (int64_t)(16 * nt + r) * L + t0 + sv);
+      for (int nt = 0; nt < N / 16; ++nt) ld.b[nt][kt] = *(const uint4*)(Bb + (int64_t)(16 * nt + r) * L + t0 + sv);
     }
     ld.dt = ((const unsigned short*)dtr)[t0 + (lane < len ? lane : 0)];
   };
@@ -163,47 +157,54 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
       // hi and lo products accumulate separately: two independent MFMA chains
       f32x4 shi = {0.0f, 0.0f, 0.0f, 0.0f}, slo = shi;
 #pragma unroll
-      for (int kt = 0; kt < kQ / 16; ++kt) {
-        const bool in = 16 * kt + 4 * q < len;
-        const float4 wv = *(const float4*)&sw[16 * kt + 4 * q];  // zero past the sequence end (Delta = 0)
-        const uint2 raw2 = ld.b[nt][kt];
-        const bf16x4 xv = in ? ld.x[kt] : bf16x4{0, 0, 0, 0};
-        const float bw[4] = {__uint_as_float(raw2.x << 16) * wv.x, __uint_as_float(raw2.x & 0xffff0000u) * wv.y,
-                             __uint_as_float(raw2.y << 16) * wv.z, __uint_as_float(raw2.y & 0xffff0000u) * wv.w};
-        bf16x4 ahi, alo;
+      for (int kt = 0; kt < kQ / 32; ++kt) {
+        const bool in = 32 * kt + 8 * q < len;
+        const float4 w0 = *(const float4*)&sw[32 * kt + 8 * q];  // zero past the sequence end (Delta = 0)
+        const float4 w1 = *(const float4*)&sw[32 * kt + 8 * q + 4];
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const uint4 rb = ld.b[nt][kt];
+        const uint32_t bw2[4] = {rb.x, rb.y, rb.z, rb.w};
+        const uint4 rx = in ? ld.x[kt] : make_uint4(0, 0, 0, 0);
+        bf16x8 ahi, alo;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t bits = j % 2 ? bw2[j / 2] & 0xffff0000u : bw2[j / 2] << 16;
           __bf16 hi, lo;
-          split_bf16(bw[j], hi, lo);
-          ahi[j] = __builtin_bit_cast(short, hi);
-          alo[j] = __builtin_bit_cast(short, lo);
+          split_bf16(__uint_as_float(bits) * wv[j], hi, lo);
+          ahi[j] = hi;
+          alo[j] = lo;
         }
-        shi = mfma16(ahi, xv, shi);
-        slo = mfma16(alo, xv, slo);
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, rx);
+        shi = mfma32(ahi, xv, shi);
+        slo = mfma32(alo, xv, slo);
       }
       sc[nt] = shi + slo;
     }
     __syncthreads();  // sw is rewritten by the next chunk
     // hand the incoming state to the output kernel, then advance it over the chunk
-    float* Sin = a.S + (bh * a.chunks + c) * N * kP;
+    float4* Sin = (float4*)a.S + ((bh * a.chunks + c) * (kP / 16) + pt) * (N / 16) * 64 + lane;
     const float decay = ex2(A2 * cs_end);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
+    for (int nt = 0; nt < N / 16; ++nt) {
+      Sin[nt * 64] = make_float4(H[nt][0], H[nt][1], H[nt][2], H[nt][3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Sin[(16 * nt + 4 * q + j) * kP + p] = H[nt][j];
-        H[nt][j] = __builtin_fmaf(decay, H[nt][j], sc[nt][j]);
-      }
+      for (int j = 0; j < 4; ++j) H[nt][j] = __builtin_fmaf(decay, H[nt][j], sc[nt][j]);
+    }
   };
-  Loads la, lb;
-  fetch(0, la);
-  if (a.chunks > 1) fetch(1, lb);
-  for (int c = 0; c < a.chunks; c += 2) {
-    combine(c, la);
-    if (c + 2 < a.chunks) fetch(c + 2, la);
-    if (c + 1 < a.chunks) {
-      combine(c + 1, lb);
-      if (c + 3 < a.chunks) fetch(c + 3, lb);
+  // kDepth register sets in a ring; the loop is unrolled over the ring so that every set has a
+  // fixed register home
+  Loads ld[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k)
+    if (k < a.chunks) fetch(k, ld[k]);
+  for (int c0 = 0; c0 < a.chunks; c0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int c = c0 + k;
+      if (c < a.chunks) {
+        combine(c, ld[k]);
+        if (c + kDepth < a.chunks) fetch(c + kDepth, ld[k]);
+      }
     }
   }
   if (a.last) {
@@ -239,52 +240,69 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   const __bf16* xh = a.x + ch0 * L + t0;
   const int r = lane % 16, q = lane / 16;
   const int tq = 16 * w + 4 * q;  // first output step of this lane's accumulators
-  // the gate inputs of this thread's two output pieces (8 steps of one channel each), the skip
-  // weights and the incoming state are fetched before anything waits
+  // Every global load of the block is issued before the first is waited for.  Pieces past the
+  // sequence end load step 0 of the chunk instead and are masked where they are used.
+  // x tile: 64 rows x 64 steps, 8 steps (16 bytes) per piece
   constexpr int kPieces = kP * kQ / 8 / 256;
-  uint4 zraw[kPieces];
+  uint4 xraw[kPieces], zraw[kPieces];
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
     const int pc = tid + 256 * i, row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
-    zraw[i] = (a.z && s8 < len) ? *(const uint4*)(a.z + (ch0 + row) * L + t0 + s8) : make_uint4(0, 0, 0, 0);
+    xraw[i] = *(const uint4*)(xh + (int64_t)row * L + (s8 < len ? s8 : 0));
+  }
+  // B and C rows, 4 steps per piece
+  constexpr int kBC = N * kQ / 4 / 256;
+  const __bf16* Bb = a.B + b * N * L + t0;
+  const __bf16* Cb = a.C + b * N * L + t0;
+  uint2 braw[kBC], craw[kBC];
+#pragma unroll
+  for (int i = 0; i < kBC; ++i) {
+    const int pc = tid + 256 * i, n = pc / (kQ / 4), s4 = 4 * (pc % (kQ / 4));
+    const int64_t off = (int64_t)n * L + (s4 < len ? s4 : 0);
+    braw[i] = *(const uint2*)(Bb + off);
+    craw[i] = *(const uint2*)(Cb + off);
+  }
+  // the step of lane t (wave 0)
+  const unsigned short dtraw = ((const unsigned short*)a.dt)[bh * L + t0 + (lane < len ? lane : 0)];
+  // gate inputs of this thread's output pieces
+  if (a.z) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int pc = tid + 256 * i, row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
+      zraw[i] = *(const uint4*)(a.z + (ch0 + row) * L + t0 + (s8 < len ? s8 : 0));
+    }
   }
   float Dv[kP / 16];
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) Dv[pt] = a.D ? a.D[h * kP + 16 * pt + r] : 0.0f;
-  // B operand of C H_in: H[n][p] for n = 16 kt + 4 q + j, p = 16 pt + r
-  const float* Hin = a.S + (bh * a.chunks + c) * N * kP;
-  float hv[N / 16][kP / 16][4];
+  // B operand of C H_in: H[n][p] for n = 16 kt + 4 q + j, p = 16 pt + r, one float4 per (pt, kt)
+  const f32x4* Hin = (const f32x4*)a.S + (bh * a.chunks + c) * (kP / 16) * (N / 16) * 64 + lane;
+  f32x4 hv[N / 16][kP / 16];
 #pragma unroll
-  for (int kt = 0; kt < N / 16; ++kt)
+  for (int pt = 0; pt < kP / 16; ++pt)
 #pragma unroll
-    for (int pt = 0; pt < kP / 16; ++pt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) hv[kt][pt][jj] = Hin[(16 * kt + 4 * q + jj) * kP + 16 * pt + r];
+    for (int kt = 0; kt < N / 16; ++kt) hv[kt][pt] = Hin[(pt * (N / 16) + kt) * 64];
+
   if (w == 0) {
-    float dl, cs;
-    chunk_steps(a, bh, t0, len, lane, dl, cs);
-    scs[lane] = cs;
+    const float raw = __uint_as_float((uint32_t)dtraw << 16) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
+    const float dl = lane < len ? (a.softplus ? softplus(raw) : raw) : 0.0f;
+    scs[lane] = wave_prefix_sum(dl);
     sdl[lane] = dl;
   }
-  // x tile: 64 rows x 64 steps, 8 steps (16 bytes) per piece, zero beyond the sequence
-  for (int pc = tid; pc < kP * kQ / 8; pc += 256) {
-    const int row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (s8 < len) v = *(const uint4*)(xh + (int64_t)row * L + s8);
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int pc = tid + 256 * i, row = pc / (kQ / 8), s8 = 8 * (pc % (kQ / 8));
+    const uint4 v = s8 < len ? xraw[i] : make_uint4(0, 0, 0, 0);
     *(uint2*)&sX[row][s8] = make_uint2(v.x, v.y);
     *(uint2*)&sX[row][s8 + 4] = make_uint2(v.z, v.w);
   }
-  // B, C transposed to step-major, 4 steps per piece
-  const __bf16* Bb = a.B + b * N * L + t0;
-  const __bf16* Cb = a.C + b * N * L + t0;
-  for (int pc = tid; pc < N * kQ / 4; pc += 256) {
-    const int n = pc / (kQ / 4), s4 = 4 * (pc % (kQ / 4));
-    uint2 vb = make_uint2(0, 0), vc = make_uint2(0, 0);
-    if (s4 < len) {
-      vb = *(const uint2*)(Bb + (int64_t)n * L + s4);
-      vc = *(const uint2*)(Cb + (int64_t)n * L + s4);
-    }
-    const uint32_t wb[2] = {vb.x, vb.y}, wc[2] = {vc.x, vc.y};
+  // B, C transposed to step-major
+#pragma unroll
+  for (int i = 0; i < kBC; ++i) {
+    const int pc = tid + 256 * i, n = pc / (kQ / 4), s4 = 4 * (pc % (kQ / 4));
+    const bool in = s4 < len;
+    const uint32_t wb[2] = {in ? braw[i].x : 0u, in ? braw[i].y : 0u};
+    const uint32_t wc[2] = {in ? craw[i].x : 0u, in ? craw[i].y : 0u};
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint16_t bj = (uint16_t)(wb[jj / 2] >> (16 * (jj % 2))), cj = (uint16_t)(wc[jj / 2] >> (16 * (jj % 2)));
