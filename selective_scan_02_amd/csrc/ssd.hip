@@ -54,7 +54,8 @@ struct SsdArgs {
   const float* h0;       // [batch, H*P, N] or null
   __bf16* y;
   float* last;           // [batch, H*P, N] or null
-  float* S;              // the state entering each chunk: [batch*H, chunks, P/16, N/16, 64 lanes, 4]
+  float* S;  // the state entering each chunk, 16 bytes per (lane, 16-state tile): bf16 hi x4, lo x4;
+             // [batch*H, chunks, P/16, N/16, 64 lanes]
   int64_t batch, heads, seqlen;
   int chunks, softplus;
 };
@@ -181,14 +182,23 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
       sc[nt] = shi + slo;
     }
     __syncthreads();  // sw is rewritten by the next chunk
-    // hand the incoming state to the output kernel, then advance it over the chunk
-    float4* Sin = (float4*)a.S + ((bh * a.chunks + c) * (kP / 16) + pt) * (N / 16) * 64 + lane;
+    // hand the incoming state to the output kernel, already split into the hi/lo bf16 operands it
+    // takes, then advance it over the chunk
+    uint4* Sin = (uint4*)a.S + ((bh * a.chunks + c) * (kP / 16) + pt) * (N / 16) * 64 + lane;
     const float decay = ex2(A2 * cs_end);
 #pragma unroll
     for (int nt = 0; nt < N / 16; ++nt) {
-      Sin[nt * 64] = make_float4(H[nt][0], H[nt][1], H[nt][2], H[nt][3]);
+      bf16x4 hhi, hlo;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) H[nt][j] = __builtin_fmaf(decay, H[nt][j], sc[nt][j]);
+      for (int j = 0; j < 4; ++j) {
+        __bf16 hi, lo;
+        split_bf16(H[nt][j], hi, lo);
+        hhi[j] = __builtin_bit_cast(short, hi);
+        hlo[j] = __builtin_bit_cast(short, lo);
+        H[nt][j] = __builtin_fmaf(decay, H[nt][j], sc[nt][j]);
+      }
+      const uint2 uh = __builtin_bit_cast(uint2, hhi), ul = __builtin_bit_cast(uint2, hlo);
+      Sin[nt * 64] = make_uint4(uh.x, uh.y, ul.x, ul.y);
     }
   };
   // kDepth register sets in a ring; the loop is unrolled over the ring so that every set has a
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
 // of the next product M x (rows t, reduction index s): it never leaves the registers.
 template <int N>
 __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
-  constexpr int XS = kQ + 8;  // padded row of the x tile (bf16)
+  constexpr int XS = kQ + 4;  // padded row of the x tile (bf16): 34 banks, so 16 rows' 8-byte reads miss each other
   constexpr int NS = N + 4;   // padded row of the step-major B and C tiles
   __shared__ __align__(16) __bf16 sX[kP][XS];   // x[p][s]
   __shared__ __align__(16) __bf16 sCt[kQ][NS];  // C[t][n]
@@ -276,8 +286,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) Dv[pt] = a.D ? a.D[h * kP + 16 * pt + r] : 0.0f;
   // B operand of C H_in: H[n][p] for n = 16 kt + 4 q + j, p = 16 pt + r, one float4 per (pt, kt)
-  const f32x4* Hin = (const f32x4*)a.S + (bh * a.chunks + c) * (kP / 16) * (N / 16) * 64 + lane;
-  f32x4 hv[N / 16][kP / 16];
+  const uint4* Hin = (const uint4*)a.S + (bh * a.chunks + c) * (kP / 16) * (N / 16) * 64 + lane;
+  uint4 hv[N / 16][kP / 16];
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt)
 #pragma unroll
@@ -354,14 +364,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < N / 16; ++kt) {
       const bf16x4 av = *(const bf16x4*)&sCt[t][16 * kt + 4 * q];
-      bf16x4 hhi, hlo;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        __bf16 hi, lo;
-        split_bf16(hv[kt][pt][jj], hi, lo);
-        hhi[jj] = __builtin_bit_cast(short, hi);
-        hlo[jj] = __builtin_bit_cast(short, lo);
-      }
+      const bf16x4 hhi = __builtin_bit_cast(bf16x4, make_uint2(hv[kt][pt].x, hv[kt][pt].y));
+      const bf16x4 hlo = __builtin_bit_cast(bf16x4, make_uint2(hv[kt][pt].z, hv[kt][pt].w));
       o = mfma16(av, hhi, o);
       o = mfma16(av, hlo, o);
     }
@@ -374,10 +378,11 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   for (int pt = 0; pt < kP / 16; ++pt) {
     const int p = 16 * pt + r;
     float4 v;
-    v.x = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 0], acc[pt][0]);
-    v.y = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 1], acc[pt][1]);
-    v.z = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 2], acc[pt][2]);
-    v.w = __builtin_fmaf(Dv[pt], (float)sX[p][tq + 3], acc[pt][3]);
+    const uint2 xw = *(const uint2*)&sX[p][tq];
+    v.x = __builtin_fmaf(Dv[pt], __uint_as_float(xw.x << 16), acc[pt][0]);
+    v.y = __builtin_fmaf(Dv[pt], __uint_as_float(xw.x & 0xffff0000u), acc[pt][1]);
+    v.z = __builtin_fmaf(Dv[pt], __uint_as_float(xw.y << 16), acc[pt][2]);
+    v.w = __builtin_fmaf(Dv[pt], __uint_as_float(xw.y & 0xffff0000u), acc[pt][3]);
     *(float4*)&sY[p][tq] = v;
   }
   __syncthreads();
