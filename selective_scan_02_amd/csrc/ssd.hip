@@ -93,12 +93,15 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // walking the chunks in order with the running state H[n][p] of its 16 columns in registers --
 // in the accumulator layout of the chunk-state product, lane (q, r) holding n = 4 q + j (+ 16 nt)
 // of column p = 16 tile + r.  Per chunk: S_c = sum_s B_s w_s x_s^T on MFMA, the incoming state is
-// written out for the output kernel, then H <- exp(a cs_end) H + S_c.  The next two chunks' B, x
-// and steps are in flight while the current one is combined.
+// written out for the output kernel, then H <- exp(a cs_end) H + S_c.  The following chunks' B, x
+// and steps are in flight while one is combined.
 template <int N>
 __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
   constexpr int kDepth = 4;  // chunks whose loads are in flight (2, 4 and 8 measured within 3%)
-  __shared__ float sw[kQ];
+  // decay weights of the chunks in flight, one row per ring slot.  The block is one wave, whose LDS
+  // accesses execute in order, so no barrier stands between writing a row and reading it: the
+  // combines of consecutive chunks are independent up to the state update and may interleave.
+  __shared__ __align__(16) float sw[kDepth][kQ];
   const int lane = threadIdx.x;
   const int pt = blockIdx.x;  // column tile
   const int64_t bh = blockIdx.y;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
     }
     ld.dt = ((const unsigned short*)dtr)[t0 + (lane < len ? lane : 0)];
   };
-  const auto combine = [&](int c, const Loads& ld) {
+  const auto combine = [&](int c, const Loads& ld, float* swk) {
     const int64_t t0 = (int64_t)c * kQ;
     const int len = (int)std::min<int64_t>(kQ, L - t0);
     // step sizes and their prefix sums (lane = step)
@@ -149,8 +152,7 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
     const float dl = lane < len ? (a.softplus ? softplus(raw) : raw) : 0.0f;
     const float cs = wave_prefix_sum(dl);
     const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), kQ - 1));
-    sw[lane] = ex2(A2 * (cs_end - cs)) * dl;
-    __syncthreads();
+    swk[lane] = ex2(A2 * (cs_end - cs)) * dl;
     // S_c, with the decay-weighted B as hi/lo bf16 A operands
     f32x4 sc[N / 16];
 #pragma unroll
@@ -160,8 +162,8 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
 #pragma unroll
       for (int kt = 0; kt < kQ / 32; ++kt) {
         const bool in = 32 * kt + 8 * q < len;
-        const float4 w0 = *(const float4*)&sw[32 * kt + 8 * q];  // zero past the sequence end (Delta = 0)
-        const float4 w1 = *(const float4*)&sw[32 * kt + 8 * q + 4];
+        const float4 w0 = *(const float4*)&swk[32 * kt + 8 * q];  // zero past the sequence end (Delta = 0)
+        const float4 w1 = *(const float4*)&swk[32 * kt + 8 * q + 4];
         const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         const uint4 rb = ld.b[nt][kt];
         const uint32_t bw2[4] = {rb.x, rb.y, rb.z, rb.w};
@@ -181,7 +183,6 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
       }
       sc[nt] = shi + slo;
     }
-    __syncthreads();  // sw is rewritten by the next chunk
     // hand the incoming state to the output kernel, already split into the hi/lo bf16 operands it
     // takes, then advance it over the chunk
     uint4* Sin = (uint4*)a.S + ((bh * a.chunks + c) * (kP / 16) + pt) * (N / 16) * 64 + lane;
@@ -203,20 +204,23 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
   };
   // kDepth register sets in a ring; the loop is unrolled over the ring so that every set has a
   // fixed register home
+  // Past the last chunk a fetch reloads the last chunk (unused), so that whole rounds of kDepth
+  // chunks are straight-line code.
   Loads ld[kDepth];
+  const int last_c = a.chunks - 1;
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k)
-    if (k < a.chunks) fetch(k, ld[k]);
-  for (int c0 = 0; c0 < a.chunks; c0 += kDepth) {
+  for (int k = 0; k < kDepth; ++k) fetch(std::min(k, last_c), ld[k]);
+  int c0 = 0;
+  for (; c0 + kDepth <= a.chunks; c0 += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      const int c = c0 + k;
-      if (c < a.chunks) {
-        combine(c, ld[k]);
-        if (c + kDepth < a.chunks) fetch(c + kDepth, ld[k]);
-      }
+      combine(c0 + k, ld[k], sw[k]);
+      fetch(std::min(c0 + k + kDepth, last_c), ld[k]);
     }
   }
+#pragma unroll
+  for (int k = 0; k < kDepth - 1; ++k)
+    if (c0 + k < a.chunks) combine(c0 + k, ld[k], sw[k]);
   if (a.last) {
 #pragma unroll
     for (int nt = 0; nt < N / 16; ++nt)
