@@ -142,6 +142,36 @@ def scan_inputs(w: Workload | int, seed: int | None = None) -> dict:
                 dt_bias=dt_bias, softplus=True, batch=Bt, dim=Dm, dstate=N, seqlen=L, dtype=w.dtype)
 
 
+def device_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, seed: int, device) -> dict:
+    """Scan inputs too large to draw on the host, drawn on `device` (bf16 I/O, the workloads' distributions).
+
+    u, z, B, C ~ N(0, 1), delta ~ 0.1 N(0, 1), from torch's seeded generator on that device, one batch row at a
+    time in fp32 and rounded to bf16; A (S4D-real), dt_bias and D (N(1, 0.1)) from the host generator as for the
+    workloads.  Both sides read the same device bytes: a checker copies back only the rows it samples.
+    """
+    rng = _rng(seed)
+    dt_bias = _dt_bias(rng, dim)
+    D = _D(rng, dim, False)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(rows, scale=1.0):
+        out = torch.empty((batch, rows, seqlen), dtype=torch.bfloat16, device=device)
+        for b in range(batch):
+            out[b] = (torch.randn((rows, seqlen), generator=g, device=device, dtype=torch.float32) * scale).to(
+                torch.bfloat16)
+        return out
+
+    u = draw(dim)
+    delta = draw(dim, 0.1)
+    z = draw(dim)
+    B = draw(dstate)
+    C = draw(dstate)
+    return dict(u=u, delta=delta, A=_s4d_real_A(dim, dstate).to(device), B=B, C=C, D=D.to(device), z=z,
+                dt_bias=dt_bias.to(device), softplus=True, batch=batch, dim=dim, dstate=dstate, seqlen=seqlen,
+                dtype="bf16")
+
+
 def random_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", seed: int = 0,
                        with_D: bool = True, with_z: bool = True, with_bias: bool = True,
                        softplus: bool = True, delta_scale: float = 0.1, a_mode: str = "s4d") -> dict:

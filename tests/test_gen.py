@@ -82,3 +82,14 @@ def test_decode_inputs():
     assert st["u"].shape == (256, 5120) and st["u"].dtype == torch.bfloat16
     assert st["B"].shape == (256, 16)
     assert p["A"].shape == (5120, 16)
+
+
+def test_device_inputs_are_seeded_and_shaped():
+    # the on-device recipe, here drawn on the CPU device: same seed, same bytes; the stated scales
+    a = gen.device_scan_inputs(2, 3, 4, 4096, seed=5, device="cpu")
+    b = gen.device_scan_inputs(2, 3, 4, 4096, seed=5, device="cpu")
+    for k in ("u", "delta", "z", "B", "C"):
+        assert a[k].dtype == torch.bfloat16 and torch.equal(a[k], b[k]), k
+    assert a["u"].shape == (2, 3, 4096) and a["B"].shape == (2, 4, 4096)
+    assert abs(a["delta"].float().std().item() - 0.1) < 0.01 and abs(a["u"].float().std().item() - 1.0) < 0.05
+    assert torch.equal(a["A"], gen.scan_inputs(0)["A"][:3, :4])

@@ -389,3 +389,27 @@ def test_resume_empty_sequence_copies_state():
     st = h0.clone()
     gpu_scan(x, initial_state=st, last_state=st)
     assert torch.equal(st, h0)
+
+
+# ----------------------------- maximum size ---------------------------------
+def test_scan_past_2_31_elements_sampled():
+    """B*D*L above 2^31 elements (4.3 GB per bf16 tensor): every flat index past 2^31 needs 64-bit
+    addressing.  The inputs are drawn on the device; sampled channels, the last one included, are
+    copied back and checked one by one against the oracle over their whole length."""
+    b, d, L = 2, 1024, 1048584
+    assert b * d * L > 2 ** 31
+    note(f"scan B={b} D={d} L={L} bf16 ({b * d * L} elements), sampled channels")
+    x = gen.device_scan_inputs(b, d, 16, L, seed=11, device="cuda")
+    y, last = ssm.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["dt_bias"])
+    torch.cuda.synchronize()
+    for c in (0, d - 1, d + 517, b * d - 1):
+        bi, di = divmod(c, d)
+        one = {k: x[k][bi:bi + 1, di:di + 1].cpu() for k in ("u", "delta", "z")}
+        yr, lr = oracle.scan(one["u"], one["delta"], x["A"][di:di + 1].cpu(), x["B"][bi:bi + 1].cpu(),
+                             x["C"][bi:bi + 1].cpu(), x["D"][di:di + 1].cpu(), one["z"], x["dt_bias"][di:di + 1].cpu())
+        ey = oracle.rel_err(f64(y[bi, di:di + 1]), yr[0])
+        el = oracle.rel_err(f64(last[bi, di:di + 1]), lr[0])
+        note(f"  channel {c}: y err {ey:.2e}  last_state err {el:.2e}")
+        assert ey <= TOL["bf16"] and el <= TOL["bf16"], (c, ey, el)
+    del x, y, last
+    torch.cuda.empty_cache()
