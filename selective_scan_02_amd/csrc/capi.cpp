@@ -341,7 +341,7 @@ int selective_state_update(float* state, const void* u, const void* delta, const
   if (batch < 1 || dim < 1 || dstate < 1)
     return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld dim=%lld dstate=%lld", (long long)batch, (long long)dim,
                 (long long)dstate);
-  if (too_big(batch, dim, dstate)) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (too_big(batch, dim, dstate) || dim >= (1LL << 34)) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
   if (!ssm::dstate_supported(dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
   const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
