@@ -346,7 +346,7 @@ int selective_state_update(float* state, const void* u, const void* delta, const
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
   const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nx = (uint64_t)batch * dim, nbc = (uint64_t)batch * dstate;
-  // with dstate >= 4 a lane moves 4 consecutive states, A, B and C entries as one vector
+  // with dstate >= 4 a lane moves its states and its A, B and C entries 4 at a time, as vectors
   const uint64_t v4 = dstate >= 4 ? 4 : 1;
   const Range ins[] = {{"u", u, nx * es, es},
                        {"delta", delta, nx * es, es},

@@ -8,9 +8,9 @@
 // h = dA*h + dB*x, y = sum(C*h) + D*x).
 //
 // The step is bound by HBM: 2*dstate*4 bytes of state traffic per (b, d)
-// against a few bytes of inputs.  Layout: each lane owns 4 consecutive states
-// of one (b, d) row (one 16-byte load and store), so a wave reads a contiguous
-// 1 KiB of state per instruction; the dstate/4 lanes of a row combine their
+// against a few bytes of inputs.  Layout: each lane owns 8 consecutive states
+// of one (b, d) row (two 16-byte loads and stores), so a wave reads contiguous
+// state with every instruction; the dstate/8 lanes of a row combine their
 // partial readouts with cross-lane adds.
 #include <hip/hip_runtime.h>
 
@@ -39,16 +39,21 @@ struct StepArgs {
 // A block covers 256 / LPR consecutive channels d (LPR lanes per (b, d) row) of kRPT consecutive
 // batch rows: the channel's parameters (its row of A, dt_bias, D) are loaded once for the kRPT
 // rows, every state load or store instruction of a wave moves one contiguous kilobyte, and each
-// lane keeps kRPT 16-byte state loads in flight.  (b, d) come from the block's coordinates, with
+// lane keeps all its rows' state loads in flight.  (b, d) come from the block's coordinates, with
 // no division.  Grids taller than the launch limit walk the batch groups with a stride.  Two rows
 // per thread measured best on the 2.8B-shaped serving batch (256 x 5120, dstate 16): 29.7 / 38.0 us
 // back to back / cache flushed, against 30.2 / 39.8 for one row and 29.3 / 39.6 for four.
 constexpr int kRPT = 2;
+// States per lane (all of them when dstate is smaller): a lane moves two 16-byte pieces of its row.
+// On the same batch, 8 states per lane with 2 rows measured 28.0 / 37.2 us, 4 per lane 29.6 / 37.6,
+// 16 per lane 35.9 / 47.1.
+constexpr int kSPL = 8;
 
 template <int N, typename T>
 __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
-  constexpr int LPR = N >= 4 ? N / 4 : 1;  // lanes per (b, d) row
-  constexpr int SPL = N / LPR;             // states per lane
+  constexpr int SPL = N >= kSPL ? kSPL : N;  // states per lane
+  constexpr int LPR = N / SPL;               // lanes per (b, d) row
+  constexpr bool kVec = SPL % 4 == 0;        // states, A, B and C moved 4 at a time
   constexpr int kCh = 256 / LPR;           // channels per block
   const int q = (int)(threadIdx.x % LPR);
   const int64_t dr = (int64_t)blockIdx.x * kCh + threadIdx.x / LPR;
@@ -57,9 +62,12 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
 
   // this lane's SPL consecutive entries of A[d], premultiplied by log2(e); dt_bias and D of d
   float a2[SPL];
-  if constexpr (SPL == 4) {
-    const float4 a4 = *reinterpret_cast<const float4*>(a.A + d * N + q * SPL);
-    a2[0] = a4.x * kLog2e; a2[1] = a4.y * kLog2e; a2[2] = a4.z * kLog2e; a2[3] = a4.w * kLog2e;
+  if constexpr (kVec) {
+#pragma unroll
+    for (int k = 0; k < SPL; k += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(a.A + d * N + q * SPL + k);
+      a2[k] = a4.x * kLog2e; a2[k + 1] = a4.y * kLog2e; a2[k + 2] = a4.z * kLog2e; a2[k + 3] = a4.w * kLog2e;
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) a2[j] = a.A[d * N + q * SPL + j] * kLog2e;
@@ -77,9 +85,12 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
       bb[i] = b0 + i < a.batch ? b0 + i : a.batch - 1;
       rr[i] = bb[i] * a.dim + d;
       const float* sp = a.state + rr[i] * N + q * SPL;
-      if constexpr (SPL == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(sp);
-        h[i][0] = v.x; h[i][1] = v.y; h[i][2] = v.z; h[i][3] = v.w;
+      if constexpr (kVec) {
+#pragma unroll
+        for (int k = 0; k < SPL; k += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(sp + k);
+          h[i][k] = v.x; h[i][k + 1] = v.y; h[i][k + 2] = v.z; h[i][k + 3] = v.w;
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) h[i][j] = sp[j];
@@ -92,20 +103,26 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
       const float dt = softplus(ld((const T*)a.delta, r) + bias);
       const float ut = ld((const T*)a.u, r);
       const float du = dt * ut;
-      // this lane's SPL consecutive entries of B[b] and C[b]: one vector load each when SPL == 4
+      // this lane's SPL consecutive entries of B[b] and C[b], 4 per vector load
       float bv[SPL], cv[SPL];
-      if constexpr (SPL == 4 && sizeof(T) == 2) {
-        const uint2 b2 = *reinterpret_cast<const uint2*>((const T*)a.B + b * N + q * SPL);
-        const uint2 c2 = *reinterpret_cast<const uint2*>((const T*)a.C + b * N + q * SPL);
-        bv[0] = __builtin_bit_cast(float, b2.x << 16); bv[1] = __builtin_bit_cast(float, b2.x & 0xffff0000u);
-        bv[2] = __builtin_bit_cast(float, b2.y << 16); bv[3] = __builtin_bit_cast(float, b2.y & 0xffff0000u);
-        cv[0] = __builtin_bit_cast(float, c2.x << 16); cv[1] = __builtin_bit_cast(float, c2.x & 0xffff0000u);
-        cv[2] = __builtin_bit_cast(float, c2.y << 16); cv[3] = __builtin_bit_cast(float, c2.y & 0xffff0000u);
-      } else if constexpr (SPL == 4) {
-        const float4 b4 = *reinterpret_cast<const float4*>((const T*)a.B + b * N + q * SPL);
-        const float4 c4 = *reinterpret_cast<const float4*>((const T*)a.C + b * N + q * SPL);
-        bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
-        cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
+      if constexpr (kVec && sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < SPL; k += 4) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>((const T*)a.B + b * N + q * SPL + k);
+          const uint2 c2 = *reinterpret_cast<const uint2*>((const T*)a.C + b * N + q * SPL + k);
+          bv[k] = __builtin_bit_cast(float, b2.x << 16); bv[k + 1] = __builtin_bit_cast(float, b2.x & 0xffff0000u);
+          bv[k + 2] = __builtin_bit_cast(float, b2.y << 16); bv[k + 3] = __builtin_bit_cast(float, b2.y & 0xffff0000u);
+          cv[k] = __builtin_bit_cast(float, c2.x << 16); cv[k + 1] = __builtin_bit_cast(float, c2.x & 0xffff0000u);
+          cv[k + 2] = __builtin_bit_cast(float, c2.y << 16); cv[k + 3] = __builtin_bit_cast(float, c2.y & 0xffff0000u);
+        }
+      } else if constexpr (kVec) {
+#pragma unroll
+        for (int k = 0; k < SPL; k += 4) {
+          const float4 b4 = *reinterpret_cast<const float4*>((const T*)a.B + b * N + q * SPL + k);
+          const float4 c4 = *reinterpret_cast<const float4*>((const T*)a.C + b * N + q * SPL + k);
+          bv[k] = b4.x; bv[k + 1] = b4.y; bv[k + 2] = b4.z; bv[k + 3] = b4.w;
+          cv[k] = c4.x; cv[k + 1] = c4.y; cv[k + 2] = c4.z; cv[k + 3] = c4.w;
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
@@ -124,8 +141,10 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
       for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
       if (active) {
         float* sp = a.state + r * N + q * SPL;
-        if constexpr (SPL == 4) {
-          *reinterpret_cast<float4*>(sp) = make_float4(h[i][0], h[i][1], h[i][2], h[i][3]);
+        if constexpr (kVec) {
+#pragma unroll
+          for (int k = 0; k < SPL; k += 4)
+            *reinterpret_cast<float4*>(sp + k) = make_float4(h[i][k], h[i][k + 1], h[i][k + 2], h[i][k + 3]);
         } else {
 #pragma unroll
           for (int j = 0; j < SPL; ++j) sp[j] = h[i][j];
@@ -143,7 +162,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
 template <int N, typename T>
 hipError_t run(const StepParams& p, hipStream_t stream) {
   StepArgs a{p.state, p.u, p.delta, p.A, p.B, p.C, p.D, p.z, p.dt_bias, p.y, p.batch, p.dim};
-  constexpr int LPR = N >= 4 ? N / 4 : 1;
+  constexpr int LPR = N / (N >= kSPL ? kSPL : N);
   constexpr int64_t kCh = 256 / LPR;
   const int64_t gx = (p.dim + kCh - 1) / kCh;
   const int64_t gy = std::min<int64_t>((p.batch + kRPT - 1) / kRPT, 65535);
