@@ -547,6 +547,44 @@ __device__ __forceinline__ void stage_rows(T (*tile)[kWave][Tile<T>::kRow], cons
   }
 }
 
+// The same tiles taken in two halves, for the single-wave passes: fetch() loads the next tile's
+// pieces into registers while the current tile is computed, store() writes them to LDS when the
+// tile starts, so the loads' latency is hidden behind a tile of work.
+template <typename T, int NT>
+struct TilePrefetch {
+  static constexpr int P = Tile<T>::kPieces, E = Tile<T>::kPiece, PER = kWave * P, R = PER / kWave;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v[NT][R];
+  __device__ __forceinline__ void fetch(const T* const (&bases)[NT], int nt, const BwdArgs& a, int64_t b,
+                                        int64_t grp, int64_t ts0, int64_t ts1, int lane) {
+    asm volatile("" : "+v"(lane));  // addresses are recomputed per call, not held across the caller's loop
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk) {
+      if (kk >= nt) break;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int pc = k * kWave + lane;
+        const int r = pc / P, pi = pc % P;
+        const int64_t ts = ts0 + (int64_t)pi * E;
+        const int64_t ch = b * a.dim + std::min<int64_t>(grp * kWave + r, a.dim - 1);
+        v[kk][k] = *(const u32x4*)(bases[kk] + ch * a.seqlen + (ts < ts1 ? ts : ts0));
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T (*tile)[kWave][Tile<T>::kRow], int nt, int64_t ts0, int64_t ts1,
+                                        int lane) const {
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk) {
+      if (kk >= nt) break;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int pc = k * kWave + lane;
+        if (ts0 + (int64_t)(pc % P) * E < ts1) *(u32x4*)&tile[kk][pc / P][(pc % P) * E] = v[kk][k];
+      }
+    }
+  }
+};
+
 // Cross-lane sums without LDS.  v_permlane32_swap exchanges lanes 32..63 of its first operand
 // with lanes 0..31 of its second, v_permlane16_swap the odd 16-lane rows of the first with the
 // even rows of the second; adding the two swapped registers halves the lanes a sum spans.
@@ -609,8 +647,19 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
   Raw nb{};
   const T* brow = Bp + (int64_t)(l.lane < N ? l.lane : 0) * L;
   if (l.lane < N) nb = Row8<T>::fetch(brow + t0);
+  // bf16 tiles are prefetched a tile ahead in registers (fp32 tiles would take twice the registers)
+  constexpr bool kPre = sizeof(T) == 2;
+  TilePrefetch<T, 2> pre;
+  if constexpr (kPre) pre.fetch(bases, 2, a, l.b, grp, t0, std::min(t0 + kSC, t1), l.lane);
   for (int64_t tc = t0; tc < t1; tc += kCT) {
-    if ((tc - t0) % kSC == 0) stage_rows<T, kWave, 2>(sIn, bases, 2, a, l.b, grp, tc, std::min(tc + kSC, t1), l.lane);
+    if ((tc - t0) % kSC == 0) {
+      if constexpr (kPre) {
+        pre.store(sIn, 2, tc, std::min(tc + kSC, t1), l.lane);
+        if (tc + kSC < t1) pre.fetch(bases, 2, a, l.b, grp, tc + kSC, std::min(tc + 2 * kSC, t1), l.lane);
+      } else {
+        stage_rows<T, kWave, 2>(sIn, bases, 2, a, l.b, grp, tc, std::min(tc + kSC, t1), l.lane);
+      }
+    }
     const Raw rb = nb;
     if (tc + kCT < t1 && l.lane < N) nb = Row8<T>::fetch(brow + tc + kCT);
     if (tc > t0 && l.active) {
@@ -681,10 +730,24 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
   Raw nc{};
   const T* crow = Cp + (int64_t)(l.lane < N ? l.lane : 0) * L;
   if (l.lane < N) nc = Row8<T>::fetch(crow + t1 - kCT);
+  // bf16 tiles are prefetched a tile ahead (to the left) in registers
+  constexpr bool kPre = sizeof(T) == 2;
+  const int nt = gated ? 3 : 2;
+  TilePrefetch<T, 3> pre;
+  if constexpr (kPre) {
+    const int64_t j0 = t0 + (t1 - kCT - t0) / kSC * kSC;
+    pre.fetch(bases, nt, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane);
+  }
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
     const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
-    if (tc == t1 - kCT || tc + kCT == j0 + kSC)
-      stage_rows<T, kWave, 3>(sIn, bases, gated ? 3 : 2, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane);
+    if (tc == t1 - kCT || tc + kCT == j0 + kSC) {
+      if constexpr (kPre) {
+        pre.store(sIn, nt, j0, std::min(j0 + kSC, t1), l.lane);
+        if (j0 > t0) pre.fetch(bases, nt, a, l.b, grp, j0 - kSC, j0, l.lane);
+      } else {
+        stage_rows<T, kWave, 3>(sIn, bases, nt, a, l.b, grp, j0, std::min(j0 + kSC, t1), l.lane);
+      }
+    }
     const Raw rc = nc;
     if (tc - kCT >= t0 && l.lane < N) nc = Row8<T>::fetch(crow + tc - kCT);
     if (l.lane < N) {
