@@ -410,6 +410,42 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(const float* pB, con
   st(dC, i, sc);
 }
 
+// 5a'. The same with 16-byte loads when count is a multiple of 4: a thread sums 4 consecutive
+// outputs over a quarter of the groups (g = quarter, quarter + 4, ...), and the quarters' sums meet
+// in LDS in a fixed order, so the result is still reproducible bit for bit.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bc_reduce4_kernel(const float* pB, const float* pC, T* dB, T* dC,
+                                                             int64_t count, int groups) {
+  __shared__ float4 sb[4][64], sc[4][64];
+  const int qd = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int64_t i4 = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  float4 b = make_float4(0.f, 0.f, 0.f, 0.f), c = b;
+  if (i4 < count) {
+    for (int g = qd; g < groups; g += 4) {
+      const float4 vb = *(const float4*)(pB + (int64_t)g * count + i4);
+      const float4 vc = *(const float4*)(pC + (int64_t)g * count + i4);
+      b.x += vb.x; b.y += vb.y; b.z += vb.z; b.w += vb.w;
+      c.x += vc.x; c.y += vc.y; c.z += vc.z; c.w += vc.w;
+    }
+  }
+  sb[qd][lane] = b;
+  sc[qd][lane] = c;
+  __syncthreads();
+  if (qd != 0 || i4 >= count) return;
+  float ob[4] = {b.x, b.y, b.z, b.w}, oc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    const float4 xb = sb[k][lane], xc = sc[k][lane];
+    ob[0] += xb.x; ob[1] += xb.y; ob[2] += xb.z; ob[3] += xb.w;
+    oc[0] += xc.x; oc[1] += xc.y; oc[2] += xc.z; oc[3] += xc.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    st(dB, i4 + j, ob[j]);
+    st(dC, i4 + j, oc[j]);
+  }
+}
+
 // 5b. dA, dD, ddt_bias: sum over segments and batch rows, one thread per (d, n).
 __global__ __launch_bounds__(256) void bwd_param_reduce_kernel(const float* pA, const float* pD, const float* pbias,
                                                                float* dA, float* dD, float* dbias, int64_t batch,
@@ -1146,8 +1182,12 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   }
   if (err == hipSuccess) {
     const int64_t count = p.batch * N * L;
-    hipLaunchKernelGGL((bwd_bc_reduce_kernel<T>), dim3(blocks_of(count)), dim3(256), 0, stream, a.pB, a.pC,
-                       (T*)p.dB, (T*)p.dC, count, a.groups);
+    if (count % 4 == 0)
+      hipLaunchKernelGGL((bwd_bc_reduce4_kernel<T>), dim3((unsigned)((count / 4 + 63) / 64)), dim3(256), 0, stream,
+                         a.pB, a.pC, (T*)p.dB, (T*)p.dC, count, a.groups);
+    else
+      hipLaunchKernelGGL((bwd_bc_reduce_kernel<T>), dim3(blocks_of(count)), dim3(256), 0, stream, a.pB, a.pC,
+                         (T*)p.dB, (T*)p.dC, count, a.groups);
     err = hipGetLastError();
   }
   if (err == hipSuccess) {
