@@ -949,18 +949,6 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
     }
     pC[tc] = keepC;
     __syncthreads();
-    if (w == 0 && zz) {
-      float out[kCT];
-#pragma unroll
-      for (int i = 0; i < kCT; ++i) {
-        float s = Dd * uv[i];
-#pragma unroll
-        for (int q = 0; q < W; ++q) s += sS[q][i][lane];
-        const float sg = sigmoid(zv[i]);
-        out[i] = gv[i] * s * sg * __builtin_fmaf(zv[i], 1.0f - sg, 1.0f);
-      }
-      if (active) Row8<T>::store((T*)a.dz + ch * L + tc, out);
-    }
     // adjoint back over the chunk
     float keepB = 0.0f;
 #pragma unroll
@@ -997,6 +985,20 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
     }
     pB[tc] = keepB;
     __syncthreads();
+    // dz (wave 0) and du, ddelta (the last wave) run side by side; sS is not rewritten before the
+    // next chunk's first barrier
+    if (w == 0 && zz) {
+      float out[kCT];
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) {
+        float s = Dd * uv[i];
+#pragma unroll
+        for (int q = 0; q < W; ++q) s += sS[q][i][lane];
+        const float sg = sigmoid(zv[i]);
+        out[i] = gv[i] * s * sg * __builtin_fmaf(zv[i], 1.0f - sg, 1.0f);
+      }
+      if (active) Row8<T>::store((T*)a.dz + ch * L + tc, out);
+    }
     if (w == W - 1) {
       float o_du[kCT], o_dl[kCT];
 #pragma unroll
