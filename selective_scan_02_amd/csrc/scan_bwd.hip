@@ -823,8 +823,8 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
 // 4'. Main pass, 16-byte rows: a workgroup of N/8 waves per (channel group, batch row) and
 // segment; wave w holds states 8w .. 8w+7 of the group's 64 channels.  Per chunk: stage B and
 // C; rerun the forward keeping h_{t-1} (readout partials to LDS, dC partials reduced across
-// lanes); wave 0 writes dz; run the adjoint back (partials of sum lam B and sum q A to LDS,
-// dB partials); the last wave writes du and ddelta.
+// lanes); run the adjoint back (partials of sum lam B and sum q A to LDS, dB partials); after
+// one barrier wave 0 writes dz while the last wave writes du and ddelta.  Two barriers per chunk.
 template <int N, typename T>
 __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fbwd_main_kernel(BwdArgs a) {
   constexpr int W = N / kSPW;
@@ -948,8 +948,8 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
       if ((lane & 7) == i) keepC = r;
     }
     pC[tc] = keepC;
-    __syncthreads();
-    // adjoint back over the chunk
+    // adjoint back over the chunk (no barrier: it reads only this wave's B and C rows; the
+    // readout partials in sS are read after the next barrier)
     float keepB = 0.0f;
 #pragma unroll
     for (int i = kCT - 1; i >= 0; --i) {
