@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   if (w == 0) {
     const float raw = __uint_as_float((uint32_t)dtraw << 16) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
     const float dl = lane < len ? (a.softplus ? softplus(raw) : raw) : 0.0f;
-    scs[lane] = wave_prefix_sum(dl);
+    scs[lane] = A2 * wave_prefix_sum(dl);  // a cs_t, in log2 units
     sdl[lane] = dl;
   }
 #pragma unroll
@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   f32x4 acc[kP / 16];
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int st = 0; st <= w; ++st) {
+  // one 16-step block of the causal product; only the diagonal block (st == w) needs the mask
+  const auto block = [&](int st, bool diag) {
     // G^T[s][t] = sum_n B[s][n] C[t][n]: lane holds s = 16 st + 4 q + j, t = 16 w + r
     f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int sj = 16 * st + 4 * q + jj;
-      const float m = sj <= t ? g[jj] * ex2(A2 * (cst - scs[sj])) * sdl[sj] : 0.0f;
+      const float v = g[jj] * ex2(cst - scs[sj]) * sdl[sj];
+      const float m = diag && sj > t ? 0.0f : v;
       __bf16 hi, lo;
       split_bf16(m, hi, lo);
       mhi[jj] = __builtin_bit_cast(short, hi);
@@ -357,11 +359,13 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
       acc[pt] = mfma16(mhi, bv, acc[pt]);
       acc[pt] = mfma16(mlo, bv, acc[pt]);
     }
-  }
+  };
+  for (int st = 0; st < w; ++st) block(st, false);
+  block(w, true);
   // + diag(exp(a cs_t)) C H_in (accumulator rows are t = 16 w + 4 q + j)
   float dec[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) dec[jj] = ex2(A2 * scs[tq + jj]);
+  for (int jj = 0; jj < 4; ++jj) dec[jj] = ex2(scs[tq + jj]);
 #pragma unroll
   for (int pt = 0; pt < kP / 16; ++pt) {
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
