@@ -183,8 +183,13 @@ struct Smem {
 // end of the unit or entirely after it: the fast path requires seqlen to be a
 // multiple of the piece length, and segments are multiples of kT.  So tails
 // need only whole-piece predicates.
+// The aggregate pass (MODE 2) is held to 128 VGPRs, so two of its workgroups share a CU (its LDS
+// allows it): on the 2^20-step fp32 sequence that made the two-pass scan 7% faster.  N = 64 would
+// spill under that cap and keeps one.
 template <int N, typename TI, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_chunked_kernel(const Args a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(MODE == 2 && N <= 32 ? 4 : 1)))
+void scan_chunked_kernel(const Args a) {
   constexpr int NPW = N / kS;        // states per scanner
   constexpr int ES = sizeof(TI);     // I/O element bytes
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
