@@ -250,6 +250,25 @@ def test_decode_small_shapes():
             assert oracle.rel_err(f64(state), ref_state) <= 1e-5
 
 
+def test_decode_batch_beyond_one_grid_column():
+    # 131075 batch rows: more row pairs than one launch column holds (65535), so the blocks walk the
+    # batch with a stride; an odd count leaves the last pair half empty
+    b, d, n = 131075, 3, 16
+    note(f"decode B={b} D={d} N={n} bf16 (grid stride over the batch)")
+    x = gen.random_scan_inputs(b, d, n, 1, "bf16", seed=17)
+    state0 = torch.randn(b, d, n, generator=torch.Generator().manual_seed(17))
+    state = state0.cuda()
+    g = dev(x)
+    st = {k: g[k][..., 0].contiguous() for k in ("u", "delta", "z", "B", "C")}
+    y = gpu_step(state, g, st)
+    torch.cuda.synchronize()
+    yr, sr = oracle.step(state0.double().numpy(), *(x[k][..., 0].contiguous() for k in ("u", "delta")), x["A"],
+                         x["B"][..., 0].contiguous(), x["C"][..., 0].contiguous(), x["D"], x["z"][..., 0].contiguous(),
+                         x["dt_bias"])
+    assert oracle.rel_err(f64(y), yr) <= TOL["bf16"]
+    assert oracle.rel_err(f64(state), sr) <= 1e-5
+
+
 def test_decode_zero_step_bit_identical_state():
     b, d, n = 4, 96, 16
     x = gen.random_scan_inputs(b, d, n, 1, "bf16", seed=2, with_bias=False)
