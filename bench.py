@@ -287,7 +287,7 @@ def ssd_flops_per_element(N: int, Q: int = 64, P: int = 64) -> float:
 
 def bench_ssd(torch, gen, ssm, steps, fwd_ms):
     """The 2.8B-shaped layer in the SSD form: 80 heads of 64 channels with one decay rate and step
-    size per head, N = 16, bf16; three kernels (chunk states, state passing, chunk outputs)."""
+    size per head, N = 16, bf16; two kernels (chunk states with state passing, chunk outputs)."""
     sp = gen.SSD_LAYER
     Bt, H, P, N, L = sp["batch"], sp["heads"], sp["headdim"], sp["dstate"], sp["seqlen"]
     x = gen.ssd_inputs(Bt, H, P, N, L, sp["dtype"], seed=2)
