@@ -297,3 +297,12 @@ def test_ssd_validation(lib):
     assert lib.ssd_scan_fwd(*ssd_args(x=addr(1) + 8)) == MISALIGNED     # 16-byte rows
     assert lib.ssd_scan_fwd(*ssd_args(y=addr(1) + 64)) == ALIAS
     assert lib.ssd_scan_fwd(*ssd_args(last=addr(9) + 64)) == ALIAS
+
+
+def test_size_limits(lib):
+    # the SSD kernels put batch * heads on one launch dimension (at most 65535); the decode step
+    # caps the channel count at 2^34 so that its grid of channel tiles fits
+    assert lib.ssd_scan_fwd(*ssd_args(batch=65536, heads=1, seqlen=8)) == BAD_SHAPE
+    assert lib.ssd_scan_fwd(*ssd_args(batch=257, heads=256, seqlen=8)) == BAD_SHAPE
+    assert lib.selective_state_update(*step_args(batch=1, dim=1 << 34, dstate=1)) == BAD_SHAPE
+    assert "too large" in ssm.last_error()
