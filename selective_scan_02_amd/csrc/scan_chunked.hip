@@ -68,7 +68,9 @@ namespace ssm {
 namespace chunked {
 
 #ifndef SSM_SPLIT_UNITS_PER_CU
-#define SSM_SPLIT_UNITS_PER_CU 4
+// workgroups per CU in the two-pass split; on the 2^20-step sequence 2, 4, 8, 12 and 16 measured
+// 2.71, 2.65, 2.45-2.56, 2.46 and 2.62 ms
+#define SSM_SPLIT_UNITS_PER_CU 8
 #endif
 #ifndef SSM_HELPER_PRIO
 #define SSM_HELPER_PRIO 1
