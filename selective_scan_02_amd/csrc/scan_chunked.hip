@@ -193,6 +193,10 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 && N <= 32 ? 4 : 1)))
 void scan_chunked_kernel(const Args a) {
   constexpr int NPW = N / kS;        // states per scanner
+  // Helper waves raise their issue priority in the split modes (on the 2^20-step fp32 sequence
+  // 2.44 ms against 2.59 at equal priority); in the interval schedule equal priority measured
+  // better (2.8B-shaped layer: 201 us against 217).
+  constexpr int kHelperPrio = MODE == 0 ? 0 : SSM_HELPER_PRIO;
   constexpr int ES = sizeof(TI);     // I/O element bytes
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
   constexpr int PPR = kT / EPP;      // pieces per tile row
@@ -535,7 +539,7 @@ void scan_chunked_kernel(const Args a) {
     SSM_LOAD_CHUNK_FULL(rs[((S4) + 1 + SSM_PREFETCH) % 4], (J) + 1 + SSM_PREFETCH)                \
     __syncthreads();                                                                              \
   }
-      if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(SSM_HELPER_PRIO);
+      if constexpr (kHelperPrio != 0) __builtin_amdgcn_s_setprio(kHelperPrio);
       // prologue: chunk 0 into LDS, chunks 1..SSM_PREFETCH in flight
       SSM_LOAD_CHUNK(rs[0], 0)
       _Pragma("unroll") for (int c = 1; c <= SSM_PREFETCH; ++c) {
@@ -559,7 +563,7 @@ void scan_chunked_kernel(const Args a) {
         if (j + 2 < last_j) SSM_HELPER_ITER(j + 2, 1)
         if (j + 3 < last_j) SSM_HELPER_ITER(j + 3, 2)
       }
-      if (SSM_HELPER_PRIO) __builtin_amdgcn_s_setprio(0);
+      if constexpr (kHelperPrio != 0) __builtin_amdgcn_s_setprio(0);
 #undef SSM_HELPER_ITER
 #undef SSM_HELPER_STEADY
     }
