@@ -620,32 +620,63 @@ __global__ void zero_ints(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// One thread per (channel, n): turn per-segment end states (from h = 0) into
-// incoming states, in place: seg_h[s] <- state entering segment s.
-__global__ __launch_bounds__(256) void carry_kernel(float* seg_h, const float* seg_dt, const float* A,
-                                                    const float* h0, int64_t chans, int64_t dim, int N, int nseg) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= chans * N) return;
+// Segment carry: turn per-segment end states (from h = 0) into incoming states, in place:
+// seg_h[s] <- state entering segment s.  A workgroup of kCW waves takes 64 consecutive (channel, n)
+// pairs, one per lane (so every load is coalesced), and wave w walks segments [w P, (w+1) P).
+// Each wave first folds its part from zero into (summed step, end state); the parts' folds meet
+// in LDS, where each wave combines those before it into the state entering its part; then it
+// walks its part again writing the incoming states.  The chain a lane walks is 2P segments long
+// instead of nseg.  The last segment's aggregate is never written, and only read where unused.
+constexpr int kCW = 16;
+__global__ __launch_bounds__(kCW * 64) void carry_split_kernel(float* seg_h, const float* seg_dt, const float* A,
+                                                               const float* h0, int64_t chans, int64_t dim, int N,
+                                                               int nseg) {
+  __shared__ float sD[kCW][64], sE[kCW][64];
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+  const int64_t pairs = chans * N;
+  const int64_t i0 = blockIdx.x * 64LL + lane;
+  const bool ok = i0 < pairs;
+  const int64_t i = ok ? i0 : pairs - 1;
   const int64_t chn = i / N;
   const int n = (int)(i % N);
   const float A2 = A[(chn % dim) * N + n] * kLog2e;
-  float h = h0 ? h0[i] : 0.0f;
-  // 16 segments at a time: their loads are all in flight before the first is used (few threads
-  // run this loop, so it is bound by load latency, not bandwidth)
-  constexpr int kBatch = 16;
-  for (int s0 = 0; s0 < nseg; s0 += kBatch) {
-    const int nb = nseg - s0 < kBatch ? nseg - s0 : kBatch;
-    float agg[kBatch], sdt[kBatch];
+  const int P = (nseg + kCW - 1) / kCW;
+  const int s0 = min(nseg, w * P), s1 = min(nseg, s0 + P);
+  const int s1a = min(s1, nseg - 1);  // aggregates exist for segments 0 .. nseg-2
+  constexpr int kB = 8;               // loads in flight per lane
+  float e = 0.0f, dsum = 0.0f;
+  for (int sb = s0; sb < s1a; sb += kB) {
+    float agg[kB], sdt[kB];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (k < nb) {
-        agg[k] = seg_h[(int64_t)(s0 + k) * chans * N + i];
-        sdt[k] = seg_dt[(int64_t)(s0 + k) * chans + chn];
+    for (int k = 0; k < kB; ++k) {
+      const int s = min(sb + k, s1a - 1);
+      agg[k] = seg_h[(int64_t)s * pairs + i];
+      sdt[k] = seg_dt[(int64_t)s * chans + chn];
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (sb + k < s1a) {
+        e = __builtin_fmaf(ex2(A2 * sdt[k]), e, agg[k]);
+        dsum += sdt[k];
       }
+  }
+  sD[w][lane] = dsum;
+  sE[w][lane] = e;
+  __syncthreads();
+  float h = h0 ? h0[i] : 0.0f;
+  for (int v = 0; v < w; ++v) h = __builtin_fmaf(ex2(A2 * sD[v][lane]), h, sE[v][lane]);
+  for (int sb = s0; sb < s1; sb += kB) {
+    float agg[kB], sdt[kB];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (k < nb) {
-        seg_h[(int64_t)(s0 + k) * chans * N + i] = h;
+    for (int k = 0; k < kB; ++k) {
+      const int s = min(sb + k, s1a);  // the last segment reads its predecessor's entry (unused)
+      agg[k] = seg_h[(int64_t)s * pairs + i];
+      sdt[k] = seg_dt[(int64_t)s * chans + chn];
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (sb + k < s1) {
+        if (ok) seg_h[(int64_t)(sb + k) * pairs + i] = h;
         h = __builtin_fmaf(ex2(A2 * sdt[k]), h, agg[k]);
       }
   }
@@ -745,9 +776,9 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2>), dim3(agg.units), dim3(kThreads), 0, stream, agg);
     err = hipGetLastError();
     if (err == hipSuccess) {
-      const int64_t threads = chans * N;
-      hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.seg_h,
-                         a.seg_dt, p.A, p.h0, chans, p.dim, N, (int)K);
+      const int64_t pairs = chans * N;
+      hipLaunchKernelGGL(carry_split_kernel, dim3((unsigned)((pairs + 63) / 64)), dim3(kCW * 64), 0, stream,
+                         a.seg_h, a.seg_dt, p.A, p.h0, chans, p.dim, N, (int)K);
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
