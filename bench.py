@@ -56,7 +56,7 @@ def algo_slots(N: int, gate: bool = True, skip: bool = True, softplus: bool = Tr
 
 # HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, per launch, scaled by
 # the same counters' reading for plain copies of known size; null until measured for the current kernel.
-TRAFFIC = {2: 356.5e6}
+TRAFFIC = {2: 358.9e6}
 
 
 def algo_slots_bwd(N: int) -> int:
