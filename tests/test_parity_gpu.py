@@ -432,3 +432,33 @@ def test_scan_past_2_31_elements_sampled():
         assert ey <= TOL["bf16"] and el <= TOL["bf16"], (c, ey, el)
     del x, y, last
     torch.cuda.empty_cache()
+
+
+def test_concurrent_streams_match_serial():
+    """Calls on two streams at once -- chained intervals and the two-pass split, whose scratch
+    (flags, ticket, segment carries) each call takes stream-ordered from the same pool -- give
+    bit for bit the results of the same calls made one after another."""
+    note("two streams at once")
+    shapes = [(4, 5120, 256), (1, 64, 16384)]
+    xs = [[dev(gen.random_scan_inputs(b, d, 16, l, "bf16", seed=30 + 2 * i + j)) for j in range(2)]
+          for i, (b, d, l) in enumerate(shapes)]
+
+    def call(t):
+        return ssm.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"])
+
+    ref = [[call(t) for t in pair] for pair in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        outs = [[None, None], [None, None]]
+        for j, s in enumerate(streams):
+            s.wait_stream(torch.cuda.current_stream())
+        for i in range(len(shapes)):
+            for j, s in enumerate(streams):
+                with torch.cuda.stream(s):
+                    outs[i][j] = call(xs[i][j])
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            for j in range(2):
+                assert torch.equal(outs[i][j][0], ref[i][j][0]), (rep, shapes[i], j, "y")
+                assert torch.equal(outs[i][j][1], ref[i][j][1]), (rep, shapes[i], j, "last_state")
