@@ -171,13 +171,14 @@ int selective_scan_bwd(const void* u, const void* delta, const float* A, const v
  *   initial_state : [batch, heads*headdim, dstate] fp32, NULL = zeros; may be the same buffer
  *                   as last_state (advanced in place)
  *   last_state    : [batch, heads*headdim, dstate] fp32 output, NULL = not written
- * Supported: dtype SSM_BF16, headdim 64, dstate in {16, 32, 64}, seqlen a multiple of 8, and
+ * Supported: dtype SSM_BF16, headdim 32, 64 or 128, dstate in {16, 32, 64} (at most 32 with
+ * headdim 128), seqlen a multiple of 8, and
  * x, dt, z, y, B, C 16-byte aligned; anything else is SSM_ERR_UNSUPPORTED (or
  * SSM_ERR_MISALIGNED).  The matrix-core products take bf16 operands with fp32 accumulation;
  * operands computed in fp32 (the decay-weighted matrices, the carried state) enter as hi + lo
  * bf16 pairs.  Results match the recurrence within the bf16 tolerance; they are not bit-equal
  * to selective_scan_fwd on the broadcast parameters.  Scratch:
- * 4 * dstate * 64 bytes per (batch, head, 64-step chunk).  Errors as for selective_scan_fwd.
+ * 4 * dstate * headdim bytes per (batch, head, 64-step chunk).  Errors as for selective_scan_fwd.
  */
 int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* dt_bias, int softplus, const float* initial_state, void* y,

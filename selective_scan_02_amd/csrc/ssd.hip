@@ -36,7 +36,8 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;  // steps per chunk
-constexpr int kP = 64;  // channels per head
+// channels per head: the kernels are templates over it (32, 64 or 128: whole 16-channel tiles, and
+// the output kernel's 256 threads move a head's 64-step x tile in whole 16-byte pieces)
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -95,7 +96,7 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // of column p = 16 tile + r.  Per chunk: S_c = sum_s B_s w_s x_s^T on MFMA, the incoming state is
 // written out for the output kernel, then H <- exp(a cs_end) H + S_c.  The following chunks' B, x
 // and steps are in flight while one is combined.
-template <int N>
+template <int N, int kP>
 __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
   constexpr int kDepth = 4;  // chunks whose loads are in flight (2, 4 and 8 measured within 3%)
   // decay weights of the chunks in flight, one row per ring slot.  The block is one wave, whose LDS
@@ -233,8 +234,9 @@ __global__ __launch_bounds__(64) void ssd_state_kernel(SsdArgs a) {
 // t = 16 w .. 16 w + 15 (all 64 channels).  The decay-weighted matrix is formed transposed,
 // G^T = B C^T, whose accumulator layout (rows s, columns t) is exactly the A-operand layout
 // of the next product M x (rows t, reduction index s): it never leaves the registers.
-template <int N>
+template <int N, int kP>
 __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
+  static_assert(kP % 32 == 0 && kP * kQ / 8 % 256 == 0, "whole x-tile pieces per thread");
   constexpr int XS = kQ + 4;  // padded row of the x tile (bf16): 34 banks, so 16 rows' 8-byte reads miss each other
   constexpr int NS = N + 4;   // padded row of the step-major B and C tiles
   __shared__ __align__(16) __bf16 sX[kP][XS];   // x[p][s]
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(SsdArgs a) {
   }
 }
 
-template <int N>
+template <int N, int kP>
 hipError_t run(const SsdParams& p, hipStream_t stream) {
   SsdArgs a{};
   a.x = (const __bf16*)p.x; a.dt = (const __bf16*)p.dt; a.A = p.A; a.B = (const __bf16*)p.B;
@@ -432,10 +434,11 @@ hipError_t run(const SsdParams& p, hipStream_t stream) {
   hipError_t err = scratch_alloc(&scratch, nS * sizeof(float), stream);
   if (err != hipSuccess) return err;
   a.S = (float*)scratch;
-  hipLaunchKernelGGL((ssd_state_kernel<N>), dim3(kP / 16, (unsigned)bh), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((ssd_state_kernel<N, kP>), dim3(kP / 16, (unsigned)bh), dim3(64), 0, stream, a);
   err = hipGetLastError();
   if (err == hipSuccess) {
-    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N>), dim3((unsigned)a.chunks, (unsigned)bh), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((ssd_chunk_scan_kernel<N, kP>), dim3((unsigned)a.chunks, (unsigned)bh), dim3(256), 0, stream,
+                       a);
     err = hipGetLastError();
   }
   const hipError_t ferr = hipFreeAsync(scratch, stream);
@@ -450,23 +453,31 @@ __global__ __launch_bounds__(256) void ssd_empty_state(float* last, const float*
 }  // namespace
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
-  return headdim == kP && (dstate == 16 || dstate == 32 || dstate == 64);
+  const bool n_ok = dstate == 16 || dstate == 32 || dstate == 64;
+  // heads of 128 channels hold 8 x (dstate / 16) incoming-state tiles per lane: dstate 64 would spill
+  return n_ok && (headdim == 32 || headdim == 64 || (headdim == 128 && dstate <= 32));
 }
 
 hipError_t launch_ssd_fwd(const SsdParams& p, hipStream_t stream) {
   if (p.seqlen == 0) {
     if (p.last_state && p.last_state != p.h0) {
-      const int64_t n = p.batch * p.heads * kP * p.dstate;
+      const int64_t n = p.batch * p.heads * p.headdim * p.dstate;
       hipLaunchKernelGGL(ssd_empty_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.last_state,
                          p.h0, n);
       return hipGetLastError();
     }
     return hipSuccess;
   }
-  switch (p.dstate) {
-    case 16: return run<16>(p, stream);
-    case 32: return run<32>(p, stream);
-    case 64: return run<64>(p, stream);
+  if (!ssd_supported(p.headdim, p.dstate)) return hipErrorInvalidValue;
+  switch (p.headdim * 1000 + p.dstate) {
+    case 32016: return run<16, 32>(p, stream);
+    case 32032: return run<32, 32>(p, stream);
+    case 32064: return run<64, 32>(p, stream);
+    case 64016: return run<16, 64>(p, stream);
+    case 64032: return run<32, 64>(p, stream);
+    case 64064: return run<64, 64>(p, stream);
+    case 128016: return run<16, 128>(p, stream);
+    case 128032: return run<32, 128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -290,7 +290,9 @@ def test_ssd_validation(lib):
     for f in ("x", "dt", "A", "B", "C", "y"):
         assert lib.ssd_scan_fwd(*ssd_args(**{f: None})) == NULL_ARG, f
     assert lib.ssd_scan_fwd(*ssd_args(dtype=0)) == UNSUPPORTED          # bf16 only
-    assert lib.ssd_scan_fwd(*ssd_args(headdim=32)) == UNSUPPORTED
+    assert lib.ssd_scan_fwd(*ssd_args(headdim=48)) == UNSUPPORTED      # heads of 32, 64 or 128 channels
+    assert lib.ssd_scan_fwd(*ssd_args(headdim=16)) == UNSUPPORTED
+    assert lib.ssd_scan_fwd(*ssd_args(headdim=128, dstate=64)) == UNSUPPORTED
     assert lib.ssd_scan_fwd(*ssd_args(dstate=8)) == UNSUPPORTED
     assert lib.ssd_scan_fwd(*ssd_args(seqlen=100)) == UNSUPPORTED       # not a multiple of 8
     assert lib.ssd_scan_fwd(*ssd_args(batch=0)) == BAD_SHAPE

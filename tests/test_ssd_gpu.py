@@ -3,8 +3,8 @@
 oracle.ssd is the sequential recurrence with the per-head decay and step broadcast to
 the head's channels (pinned in test_oracle_ssd.py).  Every output is compared element by
 element on small shapes (ragged last chunk, one to three heads, dstate 16/32/64, with and
-without gate, skip, bias, softplus and initial state) and on the 2.8B-shaped layer as 80
-heads of 64 channels.  The matrix-core products take bf16 operands, so the bound is the
+without gate, skip, bias, softplus and initial state; heads of 32, 64 and 128 channels) and on
+the 2.8B-shaped layer as 80 heads of 64 channels.  The matrix-core products take bf16 operands, so the bound is the
 bf16 one (2e-2, metric of oracle.rel_err) for y and for the final state.
 """
 import sys
@@ -69,6 +69,38 @@ def test_ssd_matches_oracle(case):
     if not x["softplus"]:
         x["dt"] = torch.abs(x["dt"])
     ey, el = run(x)
+    note(f"  y {ey:.2e}  last_state {el:.2e}")
+    assert ey <= TOL and el <= TOL
+
+
+# heads of 32 and 128 channels (the kernels are templates over the head size)
+HEAD_CASES = [
+    (32, 1, 2, 16, 200, {}),                                # ragged last chunk
+    (32, 2, 3, 32, 1032, {"with_z": False}),
+    (32, 1, 1, 64, 136, {"with_D": False, "with_bias": False}),
+    (128, 1, 2, 16, 520, {}),
+    (128, 2, 1, 32, 1000, {"softplus": False, "with_bias": False}),
+    (128, 1, 3, 16, 8, {}),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_CASES, ids=lambda c: f"P{c[0]}b{c[1]}h{c[2]}n{c[3]}L{c[4]}")
+def test_ssd_other_head_sizes_match_oracle(case):
+    P, b, h, n, L, opt = case
+    note(f"ssd P={P} B={b} H={h} N={n} L={L} {opt}")
+    x = gen.ssd_inputs(b, h, P, n, L, "bf16", seed=L + n + P, **opt)
+    if not x["softplus"]:
+        x["dt"] = torch.abs(x["dt"])
+    ey, el = run(x)
+    note(f"  y {ey:.2e}  last_state {el:.2e}")
+    assert ey <= TOL and el <= TOL
+
+
+def test_ssd_head_128_from_initial_state():
+    x = gen.ssd_inputs(1, 2, 128, 32, 264, "bf16", seed=9)
+    h0 = torch.from_numpy(np.random.default_rng(9).standard_normal((1, 256, 32), dtype=np.float32))
+    note("ssd P=128 resumed from a state")
+    ey, el = run(x, h0=h0)
     note(f"  y {ey:.2e}  last_state {el:.2e}")
     assert ey <= TOL and el <= TOL
 
