@@ -146,8 +146,8 @@ def time_scan(torch, gen, ssm, w, steps, warmup, x=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); every box here has one GPU "
-              "and nothing in this build shards across GPUs.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs each call on "
+              "one device and does not shard across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
