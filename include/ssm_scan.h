@@ -111,6 +111,26 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
 
 /*
+ * selective_scan_fwd_resume without any memory allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The scan's scratch (carries and hand-over flags of the interval schedule,
+ * segment aggregates of the two-pass plans) lives in a fixed 16 MiB device array, one copy
+ * per GPU, held from the first call on that GPU until the process exits; nothing is taken
+ * from the pool, and no hipMalloc / hipFree is made.  Arguments, results, launch plan and
+ * errors are exactly those of selective_scan_fwd_resume (initial_state NULL = zeros), plus:
+ * a call whose plan needs more scratch than the array holds returns SSM_ERR_UNSUPPORTED
+ * (ssm_last_error() gives both sizes) and touches no output.  The array keeps the last
+ * call's contents; what must start at zero is cleared by a kernel at the start of each call.
+ * Every call on one GPU shares its array: two calls that overlap in time on the same GPU
+ * (on different streams, or from different host threads) race on it and give undefined
+ * results, so such callers must order their calls.
+ */
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* dt_bias, int softplus,
+                               const float* initial_state, void* y, float* last_state, int64_t batch,
+                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
+
+/*
  * Backward of the forward scan: the gradients of a scalar loss through y, given
  * dy = dLoss/dy.  The pages have the fused kernel recompute the intermediate states in
  * the backward pass rather than store them (Mamba summary (junchaoiu.github.io), 方法
@@ -263,7 +283,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
-           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
+           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "last_error"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,8 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd",
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd",
+           "ssd_scan_fwd",
            "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
 
@@ -55,6 +56,8 @@ def load():
         lib.selective_scan_fwd.restype = I
         lib.selective_scan_fwd_resume.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I, P]
         lib.selective_scan_fwd_resume.restype = I
+        lib.selective_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I, P]
+        lib.selective_scan_fwd_noalloc.restype = I
         lib.selective_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I64, I64,
                                            I64, I64, I, P]
         lib.selective_scan_bwd.restype = I
@@ -134,6 +137,10 @@ def selective_scan_fwd(*args) -> int:
 
 def selective_scan_fwd_resume(*args) -> int:
     return int(load().selective_scan_fwd_resume(*args))
+
+
+def selective_scan_fwd_noalloc(*args) -> int:
+    return int(load().selective_scan_fwd_noalloc(*args))
 
 
 def selective_scan_bwd(*args) -> int:

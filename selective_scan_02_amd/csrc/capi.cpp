@@ -63,11 +63,11 @@ namespace ssm {
 
 hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream) {
   static std::mutex mu;
-  static hipMemPool_t pools[256] = {};
+  static hipMemPool_t pools[kMaxDevices] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   hipMemPool_t pool;
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -86,6 +86,20 @@ hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream) {
     pool = pools[dev];
   }
   return hipMallocFromPoolAsync(p, bytes, pool, stream);
+}
+
+hipError_t scratch_acquire(const ScanParams& p, void** ptr, size_t bytes, hipStream_t stream) {
+  if (p.ws) {
+    if (bytes > p.ws_bytes) return hipErrorInvalidValue;
+    *ptr = p.ws;
+    return hipSuccess;
+  }
+  return scratch_alloc(ptr, bytes, stream);
+}
+
+hipError_t scratch_release(const ScanParams& p, void* ptr, hipStream_t stream) {
+  if (p.ws) return hipSuccess;
+  return hipFreeAsync(ptr, stream);
 }
 
 }  // namespace ssm
@@ -125,7 +139,7 @@ namespace {
 int scan_impl(const char* who, const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* dt_bias, int softplus, const float* h0, void* y,
               float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
-              void* stream) {
+              void* stream, bool noalloc = false) {
   g_last_error.clear();
   // With seqlen == 0 the sequence tensors are empty and may be NULL.
   if (seqlen != 0) {
@@ -174,6 +188,15 @@ int scan_impl(const char* who, const void* u, const void* delta, const float* A,
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
   p.softplus = softplus; p.y = y; p.last_state = last_state; p.h0 = h0;
   p.batch = batch; p.dim = dim; p.dstate = dstate; p.seqlen = seqlen; p.dtype = dtype;
+  if (noalloc) {
+    // scratch from the fixed per-GPU array: refuse what it cannot hold, before any launch
+    const size_t need = ssm::scan_scratch_bytes(p, ssm::device_cu_count());
+    if (need > ssm::kNoAllocScratchBytes)
+      return fail(SSM_ERR_UNSUPPORTED, "%s: this scan needs %zu bytes of scratch; the fixed scratch array holds %zu",
+                  who, need, ssm::kNoAllocScratchBytes);
+    // always the array (also when the plan needs none): a launch path then never reaches the pool
+    if (int rc = hip_status(ssm::noalloc_scratch(&p.ws, &p.ws_bytes), who)) return rc;
+  }
   return hip_status(ssm::launch_scan_fwd(p, (hipStream_t)stream), who);
 }
 
@@ -195,6 +218,14 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream) {
   return scan_impl("selective_scan_fwd_resume launch", u, delta, A, B, C, D, z, dt_bias, softplus, initial_state,
                    y, last_state, batch, dim, dstate, seqlen, dtype, stream);
+}
+
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* dt_bias, int softplus,
+                               const float* initial_state, void* y, float* last_state, int64_t batch,
+                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream) {
+  return scan_impl("selective_scan_fwd_noalloc", u, delta, A, B, C, D, z, dt_bias, softplus, initial_state, y,
+                   last_state, batch, dim, dstate, seqlen, dtype, stream, true);
 }
 
 int selective_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -731,6 +731,18 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus) {
   return pl;
 }
 
+int device_cu_count() { return chunked::cu_count(); }
+
+// Scratch of the chunked scan, from the same plan and formulas the launch below uses.
+size_t chunked_scratch_bytes(const ScanParams& p, int cus) {
+  using namespace chunked;
+  const ScanPlan pl = plan_scan(p.batch, p.dim, p.seqlen, cus);
+  const size_t N = (size_t)p.dstate;
+  if (pl.mode == 0) return (size_t)pl.groups * N * kW * sizeof(float) + ((size_t)pl.groups * kS + 64) * sizeof(int);
+  if (pl.nseg > 1) return (size_t)pl.nseg * (size_t)(p.batch * p.dim) * (N + 1) * sizeof(float);
+  return 0;
+}
+
 namespace chunked {
 
 template <int N, typename TI>
@@ -755,7 +767,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.wlen = pl.seg_len / kT;
     const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
     const size_t bytes = carry_bytes + ((size_t)a.groups * kS + 64) * sizeof(int);
-    if ((err = scratch_alloc(&scratch, bytes, stream)) != hipSuccess) return err;
+    if ((err = scratch_acquire(p, &scratch, bytes, stream)) != hipSuccess) return err;
     a.carry = (float*)scratch;
     a.ticket = (int*)((char*)scratch + carry_bytes);
     a.flags = a.ticket + 64;
@@ -768,7 +780,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     }
   } else if (K > 1) {
     const size_t bytes = (size_t)K * chans * (N + 1) * sizeof(float);
-    if ((err = scratch_alloc(&scratch, bytes, stream)) != hipSuccess) return err;
+    if ((err = scratch_acquire(p, &scratch, bytes, stream)) != hipSuccess) return err;
     a.seg_h = (float*)scratch;
     a.seg_dt = a.seg_h + (size_t)K * chans * N;
     Args agg = a;
@@ -792,7 +804,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     err = hipGetLastError();
   }
   if (scratch) {
-    hipError_t ferr = hipFreeAsync(scratch, stream);
+    hipError_t ferr = scratch_release(p, scratch, stream);
     if (err == hipSuccess) err = ferr;
   }
   return err;

@@ -169,6 +169,19 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(float* seg_h, const flo
   }
 }
 
+// Segments of the generic scan: enough waves to fill 256 CUs x 4 SIMDs several times over.
+void generic_segments(const ScanParams& p, int64_t* nseg_out, int64_t* seg_len_out) {
+  const int64_t waves = p.batch * ((p.dim + kWave - 1) / kWave);
+  const int64_t target = 4096;
+  int64_t nseg = std::max<int64_t>(1, (target + waves - 1) / waves);
+  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, p.seqlen / 64));
+  int64_t seg_len = (p.seqlen + nseg - 1) / nseg;
+  seg_len = (seg_len + 7) / 8 * 8;
+  nseg = std::max<int64_t>(1, (p.seqlen + seg_len - 1) / seg_len);
+  *nseg_out = nseg;
+  *seg_len_out = seg_len;
+}
+
 template <int N, typename T>
 hipError_t run(const ScanParams& p, hipStream_t stream) {
   SegArgs a{};
@@ -177,13 +190,8 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.batch = p.batch; a.dim = p.dim; a.seqlen = p.seqlen; a.softplus = p.softplus;
   a.groups = (int)((p.dim + kWave - 1) / kWave);
   const int64_t waves = p.batch * a.groups;
-  // Enough waves to fill 256 CUs x 4 SIMDs several times over.
-  const int64_t target = 4096;
-  int64_t nseg = std::max<int64_t>(1, (target + waves - 1) / waves);
-  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, p.seqlen / 64));
-  int64_t seg_len = (p.seqlen + nseg - 1) / nseg;
-  seg_len = (seg_len + 7) / 8 * 8;
-  nseg = std::max<int64_t>(1, (p.seqlen + seg_len - 1) / seg_len);
+  int64_t nseg, seg_len;
+  generic_segments(p, &nseg, &seg_len);
   a.seg_len = seg_len;
   a.nseg = (int)nseg;
   const int64_t chans = p.batch * p.dim;
@@ -191,7 +199,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   if (nseg > 1) {
     const size_t bytes = (size_t)nseg * chans * (N + 1) * sizeof(float);
     void* scratch = nullptr;
-    err = scratch_alloc(&scratch, bytes, stream);
+    err = scratch_acquire(p, &scratch, bytes, stream);
     if (err != hipSuccess) return err;
     a.seg_h = (float*)scratch;
     a.seg_dt = a.seg_h + (size_t)nseg * chans * N;
@@ -210,7 +218,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
                          stream, a);
       err = hipGetLastError();
     }
-    hipError_t ferr = hipFreeAsync(scratch, stream);
+    hipError_t ferr = scratch_release(p, scratch, stream);
     return err != hipSuccess ? err : ferr;
   }
   hipLaunchKernelGGL((scan_segment_kernel<N, T, 0>), dim3((unsigned)waves, 1), dim3(kWave), 0, stream, a);
@@ -234,6 +242,18 @@ hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
 }  // namespace
 
 bool dstate_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
+
+size_t generic_scratch_bytes(const ScanParams& p) {
+  if (p.seqlen == 0) return 0;
+  int64_t nseg, seg_len;
+  generic_segments(p, &nseg, &seg_len);
+  return nseg > 1 ? (size_t)nseg * (size_t)(p.batch * p.dim) * (size_t)(p.dstate + 1) * sizeof(float) : 0;
+}
+
+size_t scan_scratch_bytes(const ScanParams& p, int cus) {
+  if (p.seqlen > 0 && chunked_supported(p)) return chunked_scratch_bytes(p, cus);
+  return generic_scratch_bytes(p);
+}
 
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream) {
   if (p.seqlen == 0) {

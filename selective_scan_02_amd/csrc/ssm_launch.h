@@ -23,6 +23,10 @@ struct ScanParams {
   const float* h0;    // nullable initial state [batch, dim, dstate]
   int64_t batch, dim, dstate, seqlen;
   int dtype;
+  // Scratch supplied by the caller (device memory of ws_bytes bytes); NULL = taken from the
+  // library's stream-ordered pool and returned to it.  With a workspace nothing is allocated.
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
 
 struct StepParams {
@@ -117,6 +121,27 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
 // what it has reserved between calls (no return to the system at synchronisation points), so
 // the carries and flags of one call reuse the memory of the previous one.
 hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream);
+
+// Scratch of one scan call: from the caller's workspace when the parameters carry one (which
+// must hold `bytes`, else hipErrorInvalidValue), otherwise from the pool.  scratch_release
+// returns pool memory on the stream and does nothing for a workspace.
+hipError_t scratch_acquire(const ScanParams& p, void** ptr, size_t bytes, hipStream_t stream);
+hipError_t scratch_release(const ScanParams& p, void* ptr, hipStream_t stream);
+
+// Scratch bytes selective_scan_fwd needs for these parameters on a GPU with `cus` compute
+// units (host-only, mirrors the launch plan: carries and flags of the interval schedule,
+// segment aggregates of the two-pass plans; 0 for one pass).
+size_t scan_scratch_bytes(const ScanParams& p, int cus);
+
+// The allocation-free scan: a fixed device array per GPU (noalloc.hip), 16 MiB.
+constexpr int kMaxDevices = 256;
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// Address and size of this GPU's copy of that array (the current device's); the address is
+// looked up on the first call per device and kept.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+size_t chunked_scratch_bytes(const ScanParams& p, int cus);
+size_t generic_scratch_bytes(const ScanParams& p);
+int device_cu_count();
 
 bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher

@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_bwd", "ssd_scan_fwd",
+    for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc",
+                 "selective_scan_bwd", "ssd_scan_fwd",
                  "selective_state_update",
                  "causal_conv1d_fwd",
                  "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 5
+    assert lib.ssm_abi_version() == 6
 
 
 def scan_args(**over):
@@ -308,3 +309,17 @@ def test_size_limits(lib):
     assert lib.ssd_scan_fwd(*ssd_args(batch=257, heads=256, seqlen=8)) == BAD_SHAPE
     assert lib.selective_state_update(*step_args(batch=1, dim=1 << 34, dstate=1)) == BAD_SHAPE
     assert "too large" in ssm.last_error()
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free scan validates like the resume call, and refuses on the host a plan
+    whose scratch exceeds its fixed array (1 x 256 channels, dstate 64, 2^20 steps in fp32: 512
+    segments of aggregates, 34 MB against 16 MiB) -- before any launch."""
+    f = lib.selective_scan_fwd_noalloc
+    assert f(*resume_args(u=None)) == NULL_ARG
+    assert f(*resume_args(dtype=5)) == BAD_DTYPE
+    assert f(*resume_args(dstate=3)) == UNSUPPORTED
+    assert f(*resume_args(h0=addr(11) + 2)) == MISALIGNED
+    assert f(*resume_args(h0=addr(9) + 64)) == ALIAS
+    assert f(*resume_args(batch=1, dim=256, dstate=64, seqlen=1 << 20, dtype=0)) == UNSUPPORTED
+    assert "scratch" in ssm.last_error()
