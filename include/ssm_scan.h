@@ -277,13 +277,35 @@ int causal_conv1d_update(float* conv_state, const void* x, const float* weight, 
 int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype, int num_cus,
                   int64_t* out);
 
+/*
+ * Hand-over waits that gave up.  When a scan is cut into intervals (launch plan mode 0), a
+ * sequence split between two workgroups continues from the state its first piece hands
+ * over; the wait for it is bounded (2^26 polls) so that no launch can hang.  A wait that
+ * runs out means that state never arrived: the waiting piece then computes from NaN, so
+ * its outputs and the final state are visibly invalid, and a device-side counter is
+ * incremented (once per waiting wave, four per sequence).  This call copies the current
+ * device's counter to *count (a synchronous device read) and, with reset != 0, sets it to
+ * zero.  Required: count.  Errors: SSM_ERR_NULL_ARG, SSM_ERR_HIP.
+ */
+int ssm_handover_failures(int64_t* count, int reset);
+
+/*
+ * Test hook for the give-up path above, process-wide, for the launches that follow:
+ * max_polls bounds the wait (<= 0 restores 2^26) and publish = 0 makes the first pieces
+ * skip setting their hand-over flags, so that every waiting piece gives up after max_polls
+ * polls while every kernel still runs to its end.  (max_polls <= 0, publish = 1) is the
+ * normal setting.  Not for production use; not synchronised with calls in flight.
+ * Always SSM_OK.
+ */
+int ssm_test_handover_wait(int max_polls, int publish);
+
 /* Text describing the calling thread's most recent non-OK status ("" if none). */
 const char* ssm_last_error(void);
 
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

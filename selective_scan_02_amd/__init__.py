@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
            "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
-           "causal_conv1d_update", "last_error"]
+           "causal_conv1d_update", "last_error", "handover_failures", "set_handover_wait"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_PKG, "libssm_scan.so")
@@ -31,7 +31,8 @@ F32, BF16 = 0, 1
 EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd",
            "ssd_scan_fwd",
            "selective_state_update", "causal_conv1d_fwd",
-           "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version")
+           "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
+           "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -75,6 +76,10 @@ def load():
         lib.ssm_abi_version.restype = I
         lib.ssm_scan_plan.argtypes = [I64, I64, I64, I64, I, I, ctypes.POINTER(ctypes.c_int64)]
         lib.ssm_scan_plan.restype = I
+        lib.ssm_handover_failures.argtypes = [ctypes.POINTER(ctypes.c_int64), I]
+        lib.ssm_handover_failures.restype = I
+        lib.ssm_test_handover_wait.argtypes = [I, I]
+        lib.ssm_test_handover_wait.restype = I
         _lib = lib
     return _lib
 
@@ -88,6 +93,18 @@ def scan_plan(batch: int, dim: int, dstate: int, seqlen: int, dtype=torch.bfloat
     code = BF16 if dtype in (torch.bfloat16, "bf16", BF16) else F32
     _check(load().ssm_scan_plan(batch, dim, dstate, seqlen, code, num_cus, out))
     return {"mode": PLAN_MODES[out[0]], "groups": out[1], "segments": out[2], "seg_len": out[3], "units": out[4]}
+
+
+def handover_failures(reset: bool = False) -> int:
+    """Interval hand-over waits that gave up on the current device (their pieces are NaN)."""
+    v = ctypes.c_int64(0)
+    _check(load().ssm_handover_failures(ctypes.byref(v), 1 if reset else 0))
+    return int(v.value)
+
+
+def set_handover_wait(max_polls: int = 0, publish: bool = True) -> None:
+    """Test hook: bound the hand-over wait and optionally suppress the flags (see the header)."""
+    _check(load().ssm_test_handover_wait(int(max_polls), 1 if publish else 0))
 
 
 def last_error() -> str:

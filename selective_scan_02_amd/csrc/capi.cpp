@@ -110,6 +110,21 @@ const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
+int ssm_handover_failures(int64_t* count, int reset) {
+  g_last_error.clear();
+  if (!count) return fail(SSM_ERR_NULL_ARG, "count is NULL");
+  uint64_t v = 0;
+  if (int rc = hip_status(ssm::handover_failures(&v, reset != 0), "ssm_handover_failures")) return rc;
+  *count = (int64_t)v;
+  return SSM_OK;
+}
+
+int ssm_test_handover_wait(int max_polls, int publish) {
+  g_last_error.clear();
+  ssm::set_handover_wait(max_polls, publish);
+  return SSM_OK;
+}
+
 int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype, int num_cus,
                   int64_t* out) {
   g_last_error.clear();
@@ -323,7 +338,9 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
   if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
   if (dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD kernels take bf16 inputs only");
   if (!ssm::ssd_supported(headdim, dstate))
-    return fail(SSM_ERR_UNSUPPORTED, "headdim=%lld dstate=%lld: need headdim 64 and dstate in {16,32,64}",
+    return fail(SSM_ERR_UNSUPPORTED,
+                "headdim=%lld dstate=%lld: need headdim in {32,64,128} and dstate in {16,32,64} (dstate <= 32 with "
+                "headdim 128)",
                 (long long)headdim, (long long)dstate);
   if (seqlen % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "seqlen=%lld is not a multiple of 8", (long long)seqlen);
   if ((seqlen + 63) / 64 > 0x7fffffffLL) return fail(SSM_ERR_BAD_SHAPE, "sizes too large");

@@ -55,11 +55,15 @@
 // Deadlock freedom of MODE 0: a tail piece waits only for the head piece of the
 // interval with the previous ticket.  That workgroup took its ticket earlier, so
 // it is running or done, and it runs its head first, which waits for nothing.
-// The wait is additionally bounded (it gives up after ~2^26 polls), so every
-// wave always reaches the exit.
+// The wait is additionally bounded (it gives up after 2^26 polls), so every
+// wave always reaches the exit.  A wait that gives up means the state at the split
+// point never arrived: the piece's state is set to NaN, so its outputs and the final
+// state visibly fail instead of passing as numbers, and a device counter records it
+// (ssm_handover_failures).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -115,7 +119,12 @@ struct Args {
   int nseg;    // K
   int units;   // MODE 1/2: K * groups; MODE 0: intervals (workgroups)
   int softplus;
+  int max_polls;  // MODE 0: bound of a tail piece's wait for its hand-over flag
+  int publish;    // MODE 0: head pieces set their hand-over flags (0 only under the test hook)
 };
+
+// Hand-over waits that gave up since the counter was last reset (see the MODE 0 wait).
+static __device__ unsigned int handover_giveups;
 
 template <typename TI>
 __device__ __forceinline__ float lds_elem(const unsigned char* row, int e) {
@@ -310,19 +319,31 @@ void scan_chunked_kernel(const Args a) {
     if (MODE == 0 && wait_in) {
       if (scanner) {
         const int* f = a.flags + (int64_t)grp * kS + wv;
+        bool arrived = true;  // wave-uniform: the flag is read through readfirstlane
         for (int spin = 0;
              __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
              ++spin) {
-          if (spin > (1 << 26)) break;  // bounded: never hang (only a broken launch could get here)
+          if (spin >= a.max_polls) {  // bounded: never hang (only a broken launch could get here)
+            arrived = false;
+            break;
+          }
           __builtin_amdgcn_s_sleep(1);
         }
-        // Hand-over protocol (the writer is at the unit end): flag and state are device-scope
-        // atomics, coherent across the XCDs' L2 caches without any cache-wide write-back or
-        // invalidation; the state loads are issued only after the flag has been observed.
-        const float* cp = a.carry + (int64_t)grp * N * kW;
+        if (arrived) {
+          // Hand-over protocol (the writer is at the unit end): flag and state are device-scope
+          // atomics, coherent across the XCDs' L2 caches without any cache-wide write-back or
+          // invalidation; the state loads are issued only after the flag has been observed.
+          const float* cp = a.carry + (int64_t)grp * N * kW;
 #pragma unroll
-        for (int j = 0; j < NPW; ++j)
-          h[j] = __hip_atomic_load(cp + (wv * NPW + j) * kW + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int j = 0; j < NPW; ++j)
+            h[j] = __hip_atomic_load(cp + (wv * NPW + j) * kW + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          // the state at the split point never arrived: poison the piece rather than go on from
+          // whatever the carry buffer holds
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) h[j] = __builtin_nanf("");
+          if (lane == 0) atomicAdd(&handover_giveups, 1u);
+        }
       }
     } else if (scanner) {
       if (MODE == 1 && a.seg_h) {
@@ -601,7 +622,7 @@ void scan_chunked_kernel(const Args a) {
 #pragma unroll
         for (int j2 = 0; j2 < NPW; ++j2)
           __hip_atomic_store(cp + (wv * NPW + j2) * kW + lane, h[j2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        SSM_PUBLISH(grp)
+        if (a.publish) SSM_PUBLISH(grp)
       }
     } else if (MODE == 0 || k == a.nseg - 1) {
       // the piece ends the chain: final state
@@ -682,6 +703,11 @@ __global__ __launch_bounds__(kCW * 64) void carry_split_kernel(float* seg_h, con
   }
 }
 
+// Hand-over wait bound and flag publication for the launches that follow; changed only by the
+// test hook ssm_test_handover_wait.
+std::atomic<int> g_max_polls{1 << 26};
+std::atomic<int> g_publish{1};
+
 int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -751,6 +777,8 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.u = p.u; a.delta = p.delta; a.z = p.z; a.B = p.B; a.C = p.C; a.A = p.A; a.D = p.D; a.dt_bias = p.dt_bias;
   a.h0 = p.h0; a.y = p.y; a.last_state = p.last_state;
   a.batch = p.batch; a.dim = p.dim; a.L = p.seqlen; a.softplus = p.softplus;
+  a.max_polls = g_max_polls.load();
+  a.publish = g_publish.load();
   a.gpr = (int)((p.dim + kW - 1) / kW);
   const int cus = cu_count();
   const ScanPlan pl = plan_scan(p.batch, p.dim, p.seqlen, cus);
@@ -823,6 +851,23 @@ hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
 }
 
 }  // namespace chunked
+
+hipError_t handover_failures(uint64_t* count, bool reset) {
+  unsigned int v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(chunked::handover_giveups), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *count = v;
+  if (reset) {
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(chunked::handover_giveups), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  }
+  return e;
+}
+
+void set_handover_wait(int max_polls, int publish) {
+  chunked::g_max_polls.store(max_polls > 0 ? max_polls : 1 << 26);
+  chunked::g_publish.store(publish ? 1 : 0);
+}
 
 bool chunked_supported(const ScanParams& p) {
   const int es = p.dtype == kBF16 ? 2 : 4;

@@ -143,6 +143,12 @@ size_t chunked_scratch_bytes(const ScanParams& p, int cus);
 size_t generic_scratch_bytes(const ScanParams& p);
 int device_cu_count();
 
+// Interval-schedule hand-over diagnostics: waits that gave up (their pieces poisoned with NaN)
+// on the current device since the last reset; and the test hook that bounds the wait and can
+// suppress the head pieces' flags.
+hipError_t handover_failures(uint64_t* count, bool reset);
+void set_handover_wait(int max_polls, int publish);
+
 bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment

@@ -44,7 +44,8 @@ def test_header_declares_the_entry_points():
                  "selective_scan_bwd", "ssd_scan_fwd",
                  "selective_state_update",
                  "causal_conv1d_fwd",
-                 "causal_conv1d_update", "ssm_scan_plan", "ssm_last_error", "ssm_abi_version"):
+                 "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
+                 "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
 
@@ -56,7 +57,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 6
+    assert lib.ssm_abi_version() == 7
 
 
 def scan_args(**over):
@@ -323,3 +324,8 @@ def test_noalloc_validation(lib):
     assert f(*resume_args(h0=addr(9) + 64)) == ALIAS
     assert f(*resume_args(batch=1, dim=256, dstate=64, seqlen=1 << 20, dtype=0)) == UNSUPPORTED
     assert "scratch" in ssm.last_error()
+
+
+def test_handover_diagnostics_validation(lib):
+    assert lib.ssm_handover_failures(None, 0) == NULL_ARG
+    assert lib.ssm_test_handover_wait(0, 1) == 0   # the normal setting, restored
