@@ -22,19 +22,24 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SSM_ORACLE_LIB names another build of the oracle (the sanitizer build of the tests)
+_LIB_PATH = os.environ.get("SSM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile ssm_oracle.c -> liboracle.so (gcc -O2 -fopenmp, IEEE: no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile ssm_oracle.c -> liboracle.so (gcc -O2 -fopenmp, IEEE: no fast-math).  With
+    ``sanitize``: AddressSanitizer and UndefinedBehaviorSanitizer, at ``out``."""
+    path = out or _LIB_PATH
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp%d" % os.getpid()
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-g"] if sanitize else []
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
-               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+               "-ffp-contract=off", *san, "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 def _load():

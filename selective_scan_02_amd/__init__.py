@@ -22,7 +22,8 @@ __all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update"
            "causal_conv1d_update", "last_error", "handover_failures", "set_handover_wait"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_PKG, "libssm_scan.so")
+# SSM_SCAN_LIB names another build of the same library (the host-sanitizer build of the tests)
+_LIB = os.environ.get("SSM_SCAN_LIB") or os.path.join(_PKG, "libssm_scan.so")
 _lib = None
 
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
