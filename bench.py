@@ -16,8 +16,11 @@ from each other's state under "resume", the decode step (B=256, D=5120,
 N=16, 128 steps) under "decode", flushed and back to back, and the causal
 conv1d + SiLU ahead of the scan (sequence and decode step) under "conv1d",
 the backward scan (selective_scan_bwd, all gradients) of the same layer
-under "backward", and the same layer in the Mamba-2 SSD form (80 heads of
-64 channels, ssd_scan_fwd on the matrix cores) under "ssd".
+under "backward", the same layer in the Mamba-2 SSD form (80 heads of
+64 channels, ssd_scan_fwd on the matrix cores) under "ssd", forward-scan
+throughput against sequence length (8K to 1M steps at a fixed channel count)
+under "l_sweep", and decode-step latency against the number of requests
+under "decode" / "batch_sweep".
 """
 from __future__ import annotations
 
@@ -92,6 +95,7 @@ def parse():
     p.add_argument("--no-conv", action="store_true", help="skip the causal conv1d figures")
     p.add_argument("--no-bwd", action="store_true", help="skip the backward-scan figure")
     p.add_argument("--no-ssd", action="store_true", help="skip the SSD (Mamba-2 form) figure")
+    p.add_argument("--no-sweeps", action="store_true", help="skip the sequence-length and decode-batch sweeps")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the scan, run 5 plain device copies of MIB MiB each (reference dispatches for "
@@ -100,15 +104,17 @@ def parse():
 
 
 def time_scan(torch, gen, ssm, w, steps, warmup, x=None):
-    """Time `steps` selective_scan_fwd calls on workload w; inputs resident in HBM.
-    Consecutive steps rotate over enough input copies to exceed the 256 MB last-level cache."""
+    """Time `steps` selective_scan_fwd calls on workload w (or on the inputs x, which carry their
+    sizes); inputs resident in HBM.  Host-drawn inputs are copied to the device several times and
+    consecutive steps rotate over the copies, enough to exceed the 256 MB last-level cache; inputs
+    drawn on the device are used as they are (they are larger than that cache)."""
     import numpy as np
     x = gen.scan_inputs(w) if x is None else x
-    B, D, N, L = w.batch, w.dim, w.dstate, w.seqlen
-    es = 2 if w.dtype == "bf16" else 4
+    B, D, N, L = x["batch"], x["dim"], x["dstate"], x["seqlen"]
+    es = 2 if x["dtype"] == "bf16" else 4
     elems = B * D * L
     bytes_step = algo_bytes(B, D, N, L, es)
-    copies = max(1, min(4, int(np.ceil(1.0e9 / bytes_step))))
+    copies = 1 if x["u"].is_cuda else max(1, min(4, int(np.ceil(1.0e9 / bytes_step))))
     ins = [{k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()} for _ in range(copies)]
     y = torch.empty_like(ins[0]["u"])
     last = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
@@ -136,7 +142,7 @@ def time_scan(torch, gen, ssm, w, steps, warmup, x=None):
     slots = algo_slots(N)
     tops = elems * slots / (ms * 1e-3) / 1e12
     gbs = bytes_step / (ms * 1e-3) / 1e9
-    plan = ssm.scan_plan(B, D, N, L, torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+    plan = ssm.scan_plan(B, D, N, L, torch.bfloat16 if x["dtype"] == "bf16" else torch.float32,
                          torch.cuda.get_device_properties(0).multi_processor_count)
     del ins, y, last
     return dict(ms=ms, value=elems / (ms * 1e-3), elems=elems, slots=slots, tops=tops, gbs=gbs,
@@ -192,15 +198,23 @@ def main():
         wl = gen.WORKLOADS[3]
         rl = time_scan(torch, gen, ssm, wl, max(3, args.steps // 10), 1)
         out["long"] = {"workload": wl.name, "ms_per_step": rl["ms"], "value": rl["value"], "unit": "elements/s",
-                       "alu": {"achieved": rl["tops"], "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
-                               "frac": rl["tops"] / PEAK_VALU_TOPS},
+                       "roofline": {"bound": "alu", "achieved": rl["tops"], "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
+                                    "frac": rl["tops"] / PEAK_VALU_TOPS, "traffic": TRAFFIC.get(3),
+                                    "ops_per_element": rl["slots"],
+                                    "op": "fp32 VALU issue slot per lane (exp/log/rcp = 2)",
+                                    "kernel": "the call's three kernels: aggregate pass, segment carry, output pass "
+                                              "(elements counted once)"},
                        "hbm": {"achieved": rl["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": rl["gbs"] / PEAK_HBM_GBS, "bytes_per_step": rl["bytes_step"]},
                        "launch_plan": rl["plan"]}
+    if not args.no_sweeps and args.workload == 2:
+        out["l_sweep"] = bench_l_sweep(torch, gen, ssm)
     if not args.no_resume and args.workload == 2:
         out["resume"] = bench_resume(torch, gen, ssm, w, x, max(5, args.steps // 5))
     if not args.no_decode:
         out["decode"] = bench_decode(torch, gen, ssm, args)
+        if not args.no_sweeps:
+            out["decode"]["batch_sweep"] = bench_decode_sweep(torch, gen, ssm)
     if not args.no_conv:
         out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
     if not args.no_bwd and args.workload == 2:
@@ -212,6 +226,82 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np, gen, x, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+L_SWEEP = (8192, 32768, 131072, 524288, 1 << 20)
+
+
+def bench_l_sweep(torch, gen, ssm):
+    """Forward-scan throughput against sequence length at a fixed channel count B*D: the
+    2^20-step workload's shape (1 x 256 channels, fp32) and one sequence of a 1024-channel layer
+    (bf16), L from 8K to 1M.  Inputs drawn on the device (same distributions).  The pages
+    describe throughput that scales almost linearly from 8K to 1M tokens: elements/s flat in L."""
+    res = []
+    for B, D, dt in ((1, 256, "f32"), (1, 1024, "bf16")):
+        for L in L_SWEEP:
+            x = gen.device_scan_inputs(B, D, 16, L, seed=L % 1000 + D, device="cuda", dtype=dt)
+            el = B * D * L
+            steps = max(3, min(20, int(2e9 // el)))
+            r = time_scan(torch, gen, ssm, None, steps, 2, x)
+            res.append({"batch": B, "d_inner": D, "seqlen": L, "io_dtype": dt, "steps": steps,
+                        "ms_per_step": r["ms"], "elements_per_s": r["value"],
+                        "alu_frac": r["tops"] / PEAK_VALU_TOPS, "launch_plan": r["plan"]["mode"]})
+            del x
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_sweep(torch, gen, ssm, batches=(1, 4, 16, 64, 256, 1024)):
+    """Decode-step latency and throughput against the number of requests (2.8B-shaped layer:
+    D = 5120, N = 16, bf16 inputs, fp32 state), back to back and with the cache flushed before each
+    step.  Calls go through the C ABI with prepared arguments so that Python does not starve the
+    GPU at small batches."""
+    p = {k: v.cuda() for k, v in gen.decode_params(4).items()}
+    D, N = 5120, 16
+    lib = ssm.load()
+    stream = torch.cuda.current_stream()
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    res = []
+    for Bt in batches:
+        state = torch.randn((Bt, D, N), generator=g, device="cuda")
+        ins = []
+        for _ in range(4):
+            t = {k: (torch.randn((Bt, D), generator=g, device="cuda") * (0.1 if k == "delta" else 1.0)).to(
+                torch.bfloat16) for k in ("u", "delta", "z")}
+            t.update({k: torch.randn((Bt, N), generator=g, device="cuda").to(torch.bfloat16) for k in ("B", "C")})
+            ins.append(t)
+        y = torch.empty((Bt, D), dtype=torch.bfloat16, device="cuda")
+        args = [(state.data_ptr(), t["u"].data_ptr(), t["delta"].data_ptr(), p["A"].data_ptr(), t["B"].data_ptr(),
+                 t["C"].data_ptr(), p["D"].data_ptr(), t["z"].data_ptr(), p["dt_bias"].data_ptr(), y.data_ptr(), Bt,
+                 D, N, 1, stream.cuda_stream) for t in ins]
+        for i in range(4):
+            assert lib.selective_state_update(*args[i]) == 0, ssm.last_error()
+        torch.cuda.synchronize()
+        n = 64
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            lib.selective_state_update(*args[i % 4])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(16)]
+        for i, (a, b) in enumerate(evs):
+            torch.sum(flush, dim=0, out=sink)
+            a.record(stream)
+            lib.selective_state_update(*args[i % 4])
+            b.record(stream)
+        torch.cuda.synchronize()
+        us_f = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+        by = Bt * D * (N * 8 + 8) + 2 * Bt * N * 2 + D * (N + 2) * 4
+        res.append({"batch": Bt, "us_per_step": us, "us_per_step_flushed": us_f,
+                    "tokens_per_s": Bt / (us * 1e-6), "tokens_per_s_flushed": Bt / (us_f * 1e-6),
+                    "hbm_frac_flushed": by / (us_f * 1e-6) / 1e9 / PEAK_HBM_GBS, "bytes_per_step": by})
+        del state, ins, y
+    del flush
+    return res
 
 
 def bench_resume(torch, gen, ssm, w, x, steps, pieces=4):
@@ -466,8 +556,19 @@ def cpu_baseline(np, gen, x, w, target_s):
     el = reps * k * w.seqlen
     what = (f"the whole workload ({total} (b, d) channels x L={w.seqlen}) run {reps} times" if k == total
             else f"the first {k} of {total} (b, d) channels, full length L={w.seqlen}")
+    # the same oracle on one thread, over the first channels (about a third of the time budget)
+    t = time.perf_counter()
+    oracle.scan(*args, chans=np.arange(16), threads=1)
+    dt1 = max(time.perf_counter() - t, 1e-6)
+    k1 = int(min(total, max(16, 16 * (target_s / 3) / dt1)))
+    t = time.perf_counter()
+    oracle.scan(*args, chans=np.arange(k1), threads=1)
+    sec1 = time.perf_counter() - t
     return {"value": el / sec, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}: {el} elements in {sec:.1f} s, fp64, OpenMP over channels"}
+            "sample": f"{what}: {el} elements in {sec:.1f} s, fp64, OpenMP over channels",
+            "single_core": {"value": k1 * w.seqlen / sec1, "unit": "elements/s", "cores": 1,
+                            "sample": f"the first {k1} (b, d) channels, full length L={w.seqlen}, one thread: "
+                                      f"{k1 * w.seqlen} elements in {sec1:.1f} s"}}
 
 
 if __name__ == "__main__":

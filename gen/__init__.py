@@ -142,13 +142,16 @@ def scan_inputs(w: Workload | int, seed: int | None = None) -> dict:
                 dt_bias=dt_bias, softplus=True, batch=Bt, dim=Dm, dstate=N, seqlen=L, dtype=w.dtype)
 
 
-def device_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, seed: int, device) -> dict:
-    """Scan inputs too large to draw on the host, drawn on `device` (bf16 I/O, the workloads' distributions).
+def device_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, seed: int, device,
+                       dtype: str = "bf16") -> dict:
+    """Scan inputs too large to draw on the host, drawn on `device` (the workloads' distributions).
 
     u, z, B, C ~ N(0, 1), delta ~ 0.1 N(0, 1), from torch's seeded generator on that device, one batch row at a
-    time in fp32 and rounded to bf16; A (S4D-real), dt_bias and D (N(1, 0.1)) from the host generator as for the
-    workloads.  Both sides read the same device bytes: a checker copies back only the rows it samples.
+    time in fp32 (rounded to bf16 for dtype "bf16"); A (S4D-real), dt_bias and D (N(1, 0.1)) from the host
+    generator as for the workloads.  Both sides read the same device bytes: a checker copies back only the rows
+    it samples.
     """
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     rng = _rng(seed)
     dt_bias = _dt_bias(rng, dim)
     D = _D(rng, dim, False)
@@ -156,10 +159,9 @@ def device_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, seed: int
     g.manual_seed(seed)
 
     def draw(rows, scale=1.0):
-        out = torch.empty((batch, rows, seqlen), dtype=torch.bfloat16, device=device)
+        out = torch.empty((batch, rows, seqlen), dtype=tdt, device=device)
         for b in range(batch):
-            out[b] = (torch.randn((rows, seqlen), generator=g, device=device, dtype=torch.float32) * scale).to(
-                torch.bfloat16)
+            out[b] = (torch.randn((rows, seqlen), generator=g, device=device, dtype=torch.float32) * scale).to(tdt)
         return out
 
     u = draw(dim)
@@ -169,7 +171,7 @@ def device_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, seed: int
     C = draw(dstate)
     return dict(u=u, delta=delta, A=_s4d_real_A(dim, dstate).to(device), B=B, C=C, D=D.to(device), z=z,
                 dt_bias=dt_bias.to(device), softplus=True, batch=batch, dim=dim, dstate=dstate, seqlen=seqlen,
-                dtype="bf16")
+                dtype=dtype)
 
 
 def random_scan_inputs(batch: int, dim: int, dstate: int, seqlen: int, dtype: str = "f32", seed: int = 0,
