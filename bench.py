@@ -217,6 +217,8 @@ def main():
             out["decode"]["batch_sweep"] = bench_decode_sweep(torch, gen, ssm)
     if not args.no_conv:
         out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
+        if args.workload == 2:
+            out["conv1d"]["fused_scan"] = bench_conv_scan(torch, gen, ssm, w, max(10, args.steps // 2))
     if not args.no_bwd and args.workload == 2:
         out["backward"] = bench_bwd(torch, ssm, w, x, max(5, args.steps // 5), r["ms"])
     if not args.no_ssd and args.workload == 2:
@@ -468,6 +470,57 @@ def bench_conv(torch, np, ssm, steps, K=4):
     res["update"] = {"shape": [R, Dd], "width": K, "dtype": "bf16", "steps": n, "us_per_step": ms * 1e3,
                      "hbm_GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "bytes_per_step": by,
                      "note": "back to back: the 15.7 MB window state stays in the last-level cache"}
+    return res
+
+
+def bench_conv_scan(torch, gen, ssm, w, steps, K=4):
+    """The causal conv1d + SiLU and the scan of the 2.8B-shaped layer, two ways: fused
+    (selective_scan_fwd_conv: u computed inside the scan kernels, never stored) and separate
+    (causal_conv1d_fwd writing u, then selective_scan_fwd reading it).  Inputs rotated over
+    three copies."""
+    import numpy as np
+    x = gen.scan_inputs(w)
+    g = np.random.default_rng(5)
+    cw = torch.from_numpy((g.standard_normal((w.dim, K)) * 0.5).astype(np.float32)).cuda()
+    cb = torch.from_numpy((g.standard_normal(w.dim) * 0.1).astype(np.float32)).cuda()
+    ins = [{k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()} for _ in range(3)]
+    y = torch.empty_like(ins[0]["u"])
+    u = torch.empty_like(ins[0]["u"])
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+    cso = torch.empty((w.batch, w.dim, K - 1), dtype=torch.float32, device="cuda")
+
+    def fused(i):
+        a = ins[i % 3]
+        ssm.scan_fwd_conv(a["u"], cw, a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], True,
+                          conv_bias=cb, y=y, last_state=last, conv_state_out=cso)
+
+    def separate(i):
+        a = ins[i % 3]
+        ssm.conv1d_fwd(a["u"], cw, cb, True, None, out=u, state_out=cso)
+        ssm.scan_fwd(u, a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], True,
+                     y=y, last_state=last)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_us_per_call"] = e0.elapsed_time(e1) / steps * 1e3
+    el = w.batch * w.dim * w.seqlen
+    res.update({"workload": f"{w.name}, causal conv1d width {K} + SiLU ahead of the scan",
+                "steps": steps, "fused_elements_per_s": el / (res["fused_us_per_call"] * 1e-6),
+                "fused_vs_separate": res["separate_us_per_call"] / res["fused_us_per_call"],
+                "hbm_bytes_saved_per_call": 2 * el * 2,
+                "note": "fused: u = silu(conv(x)) inside the scan kernels; separate: u written by the conv "
+                        "kernel and read back by the scan"})
+    del ins, y, u
     return res
 
 

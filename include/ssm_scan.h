@@ -111,6 +111,38 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
 
 /*
+ * The causal conv1d + SiLU of the Mamba block fused ahead of the scan: the scan's input u is
+ * computed from x inside the scan kernels instead of being read from memory,
+ *   u_t = silu(conv_bias[d] + sum_{k<width} conv_weight[d,k] * x[t-(width-1)+k])
+ * (Mamba summary (junchaoiu.github.io), 方法 third step: 1-D convolution for local features, then
+ * SiLU, then the selective SSM; mlqm.cn tutorial §7.1), and then exactly the scan of
+ * selective_scan_fwd_resume on that u.  u never reaches memory: against causal_conv1d_fwd
+ * followed by the scan, this saves writing u and reading it back.  (A model that also feeds u
+ * to other layers needs causal_conv1d_fwd for it.)
+ *
+ *   x               : [batch, dim, seqlen] (dtype), the convolution's input
+ *   conv_weight     : [dim, width] fp32, width in 1..4 (required); conv_bias : [dim] fp32, NULL = 0
+ *   conv_state_in   : [batch, dim, width-1] fp32, the inputs before step 0, oldest first; NULL = zeros
+ *   conv_state_out  : [batch, dim, width-1] fp32 output, the last width-1 inputs (the state the next
+ *                     piece or causal_conv1d_update continues from); NULL = not written.  Must not
+ *                     overlap any other argument.
+ *   delta, A, B, C, D, z, dt_bias, softplus, initial_state, y, last_state, sizes, dtype, stream:
+ *                     as for selective_scan_fwd_resume.
+ * u is kept in fp32 between the convolution and the scan (causal_conv1d_fwd followed by the scan
+ * rounds it to dtype in between), so the two routes agree within the dtype's rounding of u.
+ * Calls the fast scan kernels cannot take (dstate < 4, rows that are not whole 16-byte pieces,
+ * unaligned tensors) run the convolution into pool scratch and the scan on it.  Errors as for
+ * selective_scan_fwd; width outside 1..4 is SSM_ERR_UNSUPPORTED, a NULL conv_weight
+ * SSM_ERR_NULL_ARG.
+ */
+int selective_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                            const float* conv_state_in, float* conv_state_out, int64_t width, const void* delta,
+                            const float* A, const void* B, const void* C, const float* D, const void* z,
+                            const float* dt_bias, int softplus, const float* initial_state, void* y,
+                            float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                            int dtype, void* stream);
+
+/*
  * selective_scan_fwd_resume without any memory allocation, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The scan's scratch (carries and hand-over flags of the interval schedule,
@@ -305,7 +337,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

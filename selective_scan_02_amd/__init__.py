@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
-           "STATUS", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
+           "STATUS", "scan_fwd_conv", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc",
+           "selective_scan_fwd_conv", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "last_error", "handover_failures", "set_handover_wait"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +30,8 @@ _lib = None
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM_ERR_BAD_DTYPE",
           -4: "SSM_ERR_MISALIGNED", -5: "SSM_ERR_ALIAS", -6: "SSM_ERR_UNSUPPORTED", -7: "SSM_ERR_HIP"}
 F32, BF16 = 0, 1
-EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_bwd",
+EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_fwd_conv",
+           "selective_scan_bwd",
            "ssd_scan_fwd",
            "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
@@ -60,6 +62,9 @@ def load():
         lib.selective_scan_fwd_resume.restype = I
         lib.selective_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I, P]
         lib.selective_scan_fwd_noalloc.restype = I
+        lib.selective_scan_fwd_conv.argtypes = [P, P, P, P, P, I64, P, P, P, P, P, P, P, I, P, P, P, I64, I64,
+                                                I64, I64, I, P]
+        lib.selective_scan_fwd_conv.restype = I
         lib.selective_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I64, I64,
                                            I64, I64, I, P]
         lib.selective_scan_bwd.restype = I
@@ -161,6 +166,10 @@ def selective_scan_fwd_noalloc(*args) -> int:
     return int(load().selective_scan_fwd_noalloc(*args))
 
 
+def selective_scan_fwd_conv(*args) -> int:
+    return int(load().selective_scan_fwd_conv(*args))
+
+
 def selective_scan_bwd(*args) -> int:
     return int(load().selective_scan_bwd(*args))
 
@@ -220,6 +229,46 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = T
                                     L, _dtype_code(u), _stream(dev))
     _check(rc)
     return y, last_state
+
+
+def scan_fwd_conv(x, conv_weight, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True,
+                  conv_bias=None, conv_state=None, return_conv_state: bool = True, initial_state=None,
+                  return_last_state: bool = True, y=None, last_state=None, conv_state_out=None):
+    """Causal conv1d + SiLU fused ahead of the forward scan: u = silu(conv(x)) is computed inside
+    the scan kernels.  x, delta, z: [batch, dim, L]; conv_weight [dim, K] fp32 (K <= 4); conv_bias
+    [dim]; conv_state [batch, dim, K-1] fp32 (inputs before step 0).  Returns
+    (y, last_state, conv_state_out)."""
+    lib = load()
+    if x.dim() != 3 or A.dim() != 2 or conv_weight.dim() != 2:
+        raise ValueError("x must be [batch, dim, seqlen], A [dim, dstate], conv_weight [dim, width]")
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    K = conv_weight.shape[1]
+    dev, dt = x.device, x.dtype
+    for t, name, shape in ((x, "x", (batch, dim, L)), (delta, "delta", (batch, dim, L)), (z, "z", (batch, dim, L)),
+                           (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+        _require(t, name, shape, dt, dev)
+    _require(A, "A", (dim, N), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (dim,), torch.float32, dev)
+    _require(conv_weight, "conv_weight", (dim, K), torch.float32, dev)
+    _require(conv_bias, "conv_bias", (dim,), torch.float32, dev)
+    _require(conv_state, "conv_state", (batch, dim, K - 1), torch.float32, dev)
+    _require(initial_state, "initial_state", (batch, dim, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _require(y, "y", (batch, dim, L), dt, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _require(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    if return_conv_state and conv_state_out is None and K > 1:
+        conv_state_out = torch.empty((batch, dim, K - 1), dtype=torch.float32, device=dev)
+    _require(conv_state_out, "conv_state_out", (batch, dim, K - 1), torch.float32, dev)
+    _check(lib.selective_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state),
+                                       _ptr(conv_state_out), K, _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(z), _ptr(dt_bias), 1 if softplus else 0, _ptr(initial_state), _ptr(y),
+                                       _ptr(last_state), batch, dim, N, L, _dtype_code(x), _stream(dev)))
+    return y, last_state, conv_state_out
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, dy=None,

@@ -151,14 +151,25 @@ int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, in
 
 namespace {
 
+// The causal conv1d + SiLU fused ahead of the scan: u is computed from x.
+struct ConvIn {
+  const float* weight = nullptr;  // NULL: no convolution, the first tensor is u
+  const float* bias = nullptr;
+  const float* state_in = nullptr;
+  float* state_out = nullptr;
+  int64_t width = 0;
+};
+
 int scan_impl(const char* who, const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* dt_bias, int softplus, const float* h0, void* y,
               float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
-              void* stream, bool noalloc = false) {
+              void* stream, bool noalloc = false, const ConvIn& cv = ConvIn()) {
   g_last_error.clear();
+  const bool conv = cv.weight != nullptr;
+  const char* uname = conv ? "x" : "u";
   // With seqlen == 0 the sequence tensors are empty and may be NULL.
   if (seqlen != 0) {
-    if (!u) return fail(SSM_ERR_NULL_ARG, "u is NULL");
+    if (!u) return fail(SSM_ERR_NULL_ARG, "%s is NULL", uname);
     if (!delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
     if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
     if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
@@ -175,10 +186,20 @@ int scan_impl(const char* who, const void* u, const void* delta, const float* A,
   if (!ssm::dstate_supported(dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
   if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
+  if (conv && (cv.width < 1 || cv.width > 4))
+    return fail(SSM_ERR_UNSUPPORTED, "width=%lld not in 1..4", (long long)cv.width);
   const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nx = (uint64_t)batch * dim * seqlen, nbc = (uint64_t)batch * dstate * seqlen;
   const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
-  const Range ins[] = {{"u", u, nx * es, es},
+  const uint64_t ncs = conv ? (uint64_t)batch * dim * (cv.width - 1) * 4 : 0;
+  const Range cins[] = {{"conv_weight", cv.weight, conv ? (uint64_t)dim * cv.width * 4 : 0, 4},
+                        {"conv_bias", cv.bias, conv ? (uint64_t)dim * 4 : 0, 4},
+                        {"conv_state_in", cv.state_in, ncs, 4}};
+  const Range rcs{"conv_state_out", cv.state_out, ncs, 4};
+  for (const Range& r : cins)
+    if (int rc = check_aligned(r)) return rc;
+  if (int rc = check_aligned(rcs)) return rc;
+  const Range ins[] = {{uname, u, nx * es, es},
                        {"delta", delta, nx * es, es},
                        {"z", z, nx * es, es},
                        {"B", B, nbc * es, es},
@@ -198,11 +219,23 @@ int scan_impl(const char* who, const void* u, const void* delta, const float* A,
     if (overlap(rl, r) && !(r.p == h0 && last_state == h0)) return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
   }
   if (overlap(ry, rl)) return fail(SSM_ERR_ALIAS, "y overlaps last_state");
+  for (const Range& r : cins) {
+    if (overlap(ry, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+    if (overlap(rl, r)) return fail(SSM_ERR_ALIAS, "last_state overlaps %s", r.name);
+    if (overlap(rcs, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
+  }
+  for (const Range& r : ins)
+    if (overlap(rcs, r)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
+  if (overlap(rcs, ry)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps y");
+  if (overlap(rcs, rl)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps last_state");
 
   ssm::ScanParams p{};
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
   p.softplus = softplus; p.y = y; p.last_state = last_state; p.h0 = h0;
   p.batch = batch; p.dim = dim; p.dstate = dstate; p.seqlen = seqlen; p.dtype = dtype;
+  if (conv) {
+    p.cw = cv.weight; p.cb = cv.bias; p.cst = cv.state_in; p.cst_out = cv.state_out; p.ck = cv.width;
+  }
   if (noalloc) {
     // scratch from the fixed per-GPU array: refuse what it cannot hold, before any launch
     const size_t need = ssm::scan_scratch_bytes(p, ssm::device_cu_count());
@@ -233,6 +266,23 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream) {
   return scan_impl("selective_scan_fwd_resume launch", u, delta, A, B, C, D, z, dt_bias, softplus, initial_state,
                    y, last_state, batch, dim, dstate, seqlen, dtype, stream);
+}
+
+int selective_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                            const float* conv_state_in, float* conv_state_out, int64_t width, const void* delta,
+                            const float* A, const void* B, const void* C, const float* D, const void* z,
+                            const float* dt_bias, int softplus, const float* initial_state, void* y,
+                            float* last_state, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                            int dtype, void* stream) {
+  if (!conv_weight) {
+    g_last_error.clear();
+    return fail(SSM_ERR_NULL_ARG, "conv_weight is NULL");
+  }
+  ConvIn cv;
+  cv.weight = conv_weight; cv.bias = conv_bias; cv.state_in = conv_state_in; cv.state_out = conv_state_out;
+  cv.width = width;
+  return scan_impl("selective_scan_fwd_conv launch", x, delta, A, B, C, D, z, dt_bias, softplus, initial_state, y,
+                   last_state, batch, dim, dstate, seqlen, dtype, stream, false, cv);
 }
 
 int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -169,6 +169,19 @@ __global__ __launch_bounds__(256) void conv1d_copy_state(float* dst, const float
   if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
+// The last K-1 inputs of every row (oldest first), reaching into the state before step 0 when
+// the row is shorter: the state causal_conv1d_fwd leaves, for callers that fuse the convolution.
+template <typename T>
+__global__ __launch_bounds__(256) void conv1d_state_tail(const T* x, const float* st_in, float* st_out, int64_t rows,
+                                                         int64_t L, int K) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= rows * (K - 1)) return;
+  const int64_t row = i / (K - 1);
+  const int j = (int)(i - row * (K - 1));
+  const int64_t s = L - (K - 1) + j;
+  st_out[i] = s >= 0 ? ld(x, row * L + s) : (st_in ? st_in[row * (K - 1) + (K - 1) + s] : 0.0f);
+}
+
 struct UpdArgs {
   float* state;
   const void* x;
@@ -250,6 +263,19 @@ hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream) {
     return hipSuccess;
   }
   return p.dtype == kBF16 ? dispatch_fwd<__bf16>(p, stream) : dispatch_fwd<float>(p, stream);
+}
+
+hipError_t launch_conv1d_state_out(const ConvParams& p, hipStream_t stream) {
+  if (!p.state_out || p.width <= 1) return hipSuccess;
+  const int64_t n = p.batch * p.dim * (p.width - 1);
+  const dim3 g((unsigned)((n + 255) / 256));
+  if (p.dtype == kBF16)
+    hipLaunchKernelGGL(conv1d_state_tail<__bf16>, g, dim3(256), 0, stream, (const __bf16*)p.x, p.state_in, p.state_out,
+                       p.batch * p.dim, p.seqlen, (int)p.width);
+  else
+    hipLaunchKernelGGL(conv1d_state_tail<float>, g, dim3(256), 0, stream, (const float*)p.x, p.state_in, p.state_out,
+                       p.batch * p.dim, p.seqlen, (int)p.width);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream) {

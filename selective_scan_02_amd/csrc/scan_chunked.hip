@@ -86,13 +86,26 @@ namespace chunked {
 #define SSM_GATE_BLEND 1
 #endif
 
+#ifndef SSM_HELPERS_BF16
+#define SSM_HELPERS_BF16 4
+#endif
+#ifndef SSM_HELPERS_F32
+#define SSM_HELPERS_F32 4
+#endif
+
 constexpr int kT = 16;  // time steps per chunk (= lanes of a DPP row)
 constexpr int kW = 64;  // channels per group = lanes per wave
 constexpr int kS = 4;   // scanner waves
-constexpr int kH = 4;   // helper waves
-constexpr int kThreads = (kS + kH) * kW;
-constexpr int kHT = kH * kW;  // helper threads
-constexpr int kTPH = kT / kH; // steps per helper thread per chunk
+
+// Helper waves per workgroup: 4 in the aggregate pass; the output kernels can take more.
+template <int MODE, typename TI>
+constexpr int helpers() {
+  return MODE == 2 ? 4 : sizeof(TI) == 2 ? SSM_HELPERS_BF16 : SSM_HELPERS_F32;
+}
+template <int MODE, typename TI>
+constexpr int threads() {
+  return (kS + helpers<MODE, TI>()) * kW;
+}
 
 struct Args {
   const void* u;
@@ -121,6 +134,11 @@ struct Args {
   int softplus;
   int max_polls;  // MODE 0: bound of a tail piece's wait for its hand-over flag
   int publish;    // MODE 0: head pieces set their hand-over flags (0 only under the test hook)
+  // CONV kernels: u = silu(conv(x)) is computed in place of loading u (`u` above points to x)
+  const float* cw;   // [dim, ck] causal depthwise filter
+  const float* cb;   // [dim] its bias, or NULL
+  const float* cst;  // [batch*dim, ck-1] inputs before step 0 (oldest first), or NULL = zeros
+  int ck;            // filter width, 1..4
 };
 
 // Hand-over waits that gave up since the counter was last reset (see the MODE 0 wait).
@@ -176,7 +194,8 @@ struct Smem {
   float part[OUT ? 2 : 1][OUT ? kS : 1][kT][kW];     // partial readouts of the scanners
   unsigned char ytile[OUT ? 2 : 1][kW * ROWB];       // y of one chunk, [channel][t]
   alignas(16) float bc[4][2][N][kT];                 // B, C of a chunk in fp32 (ring, as tile)
-  float red[kH][kW];
+  float red[OUT ? 1 : 4][kW];                         // aggregate pass: the helpers' sums of Delta
+  float xh[kW][4];   // CONV: the 3 inputs before the unit's first step, per channel (fp32)
   int unit;     // MODE 0: this workgroup's interval
 };
 
@@ -197,8 +216,8 @@ struct Smem {
 // The aggregate pass (MODE 2) is held to 128 VGPRs, so two of its workgroups share a CU (its LDS
 // allows it): on the 2^20-step fp32 sequence that made the two-pass scan 7% faster.  N = 64 would
 // spill under that cap and keeps one.
-template <int N, typename TI, int MODE>
-__global__ __launch_bounds__(kThreads)
+template <int N, typename TI, int MODE, bool CONV>
+__global__ __launch_bounds__((threads<MODE, TI>()))
 __attribute__((amdgpu_waves_per_eu(MODE == 2 && N <= 32 ? 4 : 1)))
 void scan_chunked_kernel(const Args a) {
   constexpr int NPW = N / kS;        // states per scanner
@@ -206,6 +225,10 @@ void scan_chunked_kernel(const Args a) {
   // 2.44 ms against 2.59 at equal priority); in the interval schedule equal priority measured
   // better (2.8B-shaped layer: 201 us against 217).
   constexpr int kHelperPrio = MODE == 0 ? 0 : SSM_HELPER_PRIO;
+  constexpr int kH = helpers<MODE, TI>();  // helper waves
+  constexpr int kHT = kH * kW;             // helper threads
+  constexpr int kTPH = kT / kH;            // steps per helper thread per chunk
+  static_assert(kT % kH == 0, "helpers split a chunk's steps evenly");
   constexpr int ES = sizeof(TI);     // I/O element bytes
   constexpr int EPP = 16 / ES;       // elements per 16-byte piece
   constexpr int PPR = kT / EPP;      // pieces per tile row
@@ -366,6 +389,20 @@ void scan_chunked_kernel(const Args a) {
     asm volatile("" : "+v"(gmask));  // opaque: the gate select below stays a bit blend, not a branch
     const bool sp = a.softplus != 0;
     float sdt = 0.0f;
+    // CONV: taps of this channel's filter on the window t-3 .. t (width K fills the last K
+    // positions); positions before the window are never read (selected to 0, not weighted by 0,
+    // so that a non-finite input there cannot leak in)
+    float cwv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f;
+    int cskip = 0;  // window positions before the filter's first tap
+    if constexpr (CONV) {
+      cskip = 4 - a.ck;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) cwv[m] = m >= cskip ? a.cw[(int64_t)cc * a.ck + (m - cskip)] : 0.0f;
+      cbias = a.cb ? a.cb[cc] : 0.0f;
+    }
+    // CONV: u of a chunk from its prep to its finalize, two iterations later (slot = chunk % 2:
+    // an iteration finalizes chunk J-2 before it preps chunk J into the same slot)
+    float ukeep[2][kTPH];
     const TI* lsrc[LPT];               // NULL: piece unused or past a tensor's rows
     const TI* lsrc_f[LPT];             // unconditional-load version (a harmless valid address)
     int lstep[LPT];                    // first step of the piece within a chunk
@@ -418,7 +455,7 @@ void scan_chunked_kernel(const Args a) {
   }
     // prep chunk J: Delta, Delta*u to LDS; D*u and silu(z) kept in registers for finalize.
     // TAIL: steps past the end of the unit become identity steps (Delta = 0).
-#define SSM_PREP(J, TB, TAIL)                                                                     \
+#define SSM_PREP(J, TB, TAIL, US)                                                                 \
   {                                                                                               \
     const unsigned char* ru = &sm.tile[(J) & 3][0][lane * ROWB];                                  \
     const unsigned char* rd = &sm.tile[(J) & 3][1][lane * ROWB];                                  \
@@ -426,6 +463,27 @@ void scan_chunked_kernel(const Args a) {
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
       xv[i] = lds_elem<TI>(rd, hw * kTPH + i);                                                    \
       uv[i] = lds_elem<TI>(ru, hw * kTPH + i);                                                    \
+    }                                                                                             \
+    if constexpr (CONV) {                                                                         \
+      /* the tile holds x: u = silu(bias + taps . x[t-3 .. t]), the 3 inputs before this       */ \
+      /* thread's first step from the same row, the previous chunk's row, or the unit's halo   */ \
+      float xw[kTPH + 3];                                                                         \
+      _Pragma("unroll") for (int i = 0; i < kTPH; ++i) xw[3 + i] = uv[i];                        \
+      if (hw > 0) {                                                                               \
+        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = lds_elem<TI>(ru, hw * kTPH - 3 + m); \
+      } else if ((J) == 0) {                                                                      \
+        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = sm.xh[lane][m];                     \
+      } else {                                                                                    \
+        const unsigned char* rp = &sm.tile[((J) - 1) & 3][0][lane * ROWB];                        \
+        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = lds_elem<TI>(rp, kT - 3 + m);     \
+      }                                                                                           \
+      _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                          \
+        float v = cbias;                                                                          \
+        _Pragma("unroll") for (int m = 0; m < 4; ++m)                                             \
+          v = __builtin_fmaf(cwv[m], m >= cskip ? xw[i + m] : 0.0f, v);                           \
+        uv[i] = silu(v);                                                                          \
+        ukeep[US][i] = uv[i];                                                                     \
+      }                                                                                           \
     }                                                                                             \
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
       const int tl = hw * kTPH + i;                                                               \
@@ -438,7 +496,7 @@ void scan_chunked_kernel(const Args a) {
     }                                                                                             \
   }
     // finalize a chunk (LDS buffer TB): sum the partial readouts, add D*u, gate, round into the y tile
-#define SSM_FINALIZE(J, TB)                                                                       \
+#define SSM_FINALIZE(J, TB, US)                                                                   \
   if (OUT) {                                                                                      \
     unsigned char* ry = &sm.ytile[OUT ? (TB) : 0][lane * ROWB];                                   \
     const unsigned char* ru = &sm.tile[(J) & 3][0][lane * ROWB];                                  \
@@ -446,7 +504,7 @@ void scan_chunked_kernel(const Args a) {
     float pp[kTPH][kS], uv[kTPH], zv[kTPH];                                                       \
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
       _Pragma("unroll") for (int w = 0; w < kS; ++w) pp[i][w] = sm.part[OUT ? (TB) : 0][w][hw * kTPH + i][lane]; \
-      uv[i] = lds_elem<TI>(ru, hw * kTPH + i);                                                    \
+      uv[i] = CONV ? ukeep[US][i] : lds_elem<TI>(ru, hw * kTPH + i);                              \
       zv[i] = lds_elem<TI>(rz, hw * kTPH + i);                                                    \
     }                                                                                             \
     _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                            \
@@ -514,7 +572,7 @@ void scan_chunked_kernel(const Args a) {
   }
 
     // ---------------- iterations ------------------------------------------------------------
-    // Iteration J: helpers prefetch chunk J+2, store y(J-3), prep(J), finalize(J-2) and stage
+    // Iteration J: helpers prefetch chunk J+2, store y(J-3), finalize(J-2), prep(J) and stage
     // chunk J+1 into LDS; scanners scan(J-1).  One workgroup barrier per iteration.  The two
     // roles run separate loops with the same barrier sequence, so their registers never
     // overlap.  Steady-state iterations (all stages active, full chunks) use compile-time LDS
@@ -545,8 +603,8 @@ void scan_chunked_kernel(const Args a) {
 #define SSM_HELPER_ITER(J, S4)                                                                    \
   {                                                                                               \
     if ((J) >= 3) SSM_STORE_Y((J) - 3, ((S4) + 1) & 1, true)                                      \
-    if ((J) < nch) SSM_PREP(J, (S4) & 1, true)                                                    \
-    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE((J) - 2, (S4) & 1)                              \
+    if ((J) >= 2 && (J) <= nch + 1) SSM_FINALIZE((J) - 2, (S4) & 1, (S4) & 1)                     \
+    if ((J) < nch) SSM_PREP(J, (S4) & 1, true, (S4) & 1)                                          \
     if ((J) + 1 < nch) SSM_STORE_TILE((J) + 1, 0, rs[((S4) + 1) % 4])                              \
     if ((J) + 1 + SSM_PREFETCH < nch) SSM_LOAD_CHUNK(rs[((S4) + 1 + SSM_PREFETCH) % 4], (J) + 1 + SSM_PREFETCH) \
     __syncthreads();                                                                              \
@@ -554,8 +612,8 @@ void scan_chunked_kernel(const Args a) {
 #define SSM_HELPER_STEADY(J, S4)                                                                  \
   {                                                                                               \
     SSM_STORE_Y((J) - 3, ((S4) + 1) & 1, false)                                                   \
-    SSM_PREP(J, (S4) & 1, false)                                                                  \
-    SSM_FINALIZE((J) - 2, (S4) & 1)                                                               \
+    SSM_FINALIZE((J) - 2, (S4) & 1, (S4) & 1)                                                     \
+    SSM_PREP(J, (S4) & 1, false, (S4) & 1)                                                        \
     SSM_STORE_TILE((J) + 1, 0, rs[((S4) + 1) % 4])                                                \
     SSM_LOAD_CHUNK_FULL(rs[((S4) + 1 + SSM_PREFETCH) % 4], (J) + 1 + SSM_PREFETCH)                \
     __syncthreads();                                                                              \
@@ -567,6 +625,21 @@ void scan_chunked_kernel(const Args a) {
         if (c < nch) SSM_LOAD_CHUNK(rs[c], c)
       }
       SSM_STORE_TILE(0, 0, rs[0])
+      if constexpr (CONV) {
+        // the 3 inputs before the unit's first step: from x, or (at step 0) from the state
+        // the caller passes, oldest first, zeros where it has none
+        if (htid < 3 * kW) {
+          const int r = htid % kW, m = htid / kW;
+          const int64_t pos = t_begin - 3 + m;
+          float v = 0.0f;
+          if (d0 + r < a.dim) {
+            const int64_t row = (int64_t)b * a.dim + d0 + r;
+            if (pos >= 0) v = ld<TI>((const TI*)a.u, row * L + pos);
+            else if (a.cst && a.ck - 1 + pos >= 0) v = a.cst[row * (a.ck - 1) + (a.ck - 1 + pos)];
+          }
+          sm.xh[r][m] = v;
+        }
+      }
       __syncthreads();
       SSM_HELPER_ITER(0, 0)
       if (1 < last_j) SSM_HELPER_ITER(1, 1)
@@ -601,7 +674,7 @@ void scan_chunked_kernel(const Args a) {
 #undef SSM_SCAN
 
     // ---- unit end: hand the state on ----
-    if (MODE == 2) {
+    if constexpr (MODE == 2) {
       if (scanner && active) {
 #pragma unroll
         for (int j2 = 0; j2 < NPW; ++j2) a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + wv * NPW + j2] = h[j2];
@@ -771,7 +844,7 @@ size_t chunked_scratch_bytes(const ScanParams& p, int cus) {
 
 namespace chunked {
 
-template <int N, typename TI>
+template <int N, typename TI, bool CONV>
 hipError_t run(const ScanParams& p, hipStream_t stream) {
   Args a{};
   a.u = p.u; a.delta = p.delta; a.z = p.z; a.B = p.B; a.C = p.C; a.A = p.A; a.D = p.D; a.dt_bias = p.dt_bias;
@@ -779,6 +852,9 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.batch = p.batch; a.dim = p.dim; a.L = p.seqlen; a.softplus = p.softplus;
   a.max_polls = g_max_polls.load();
   a.publish = g_publish.load();
+  if constexpr (CONV) {  // p.u is x
+    a.cw = p.cw; a.cb = p.cb; a.cst = p.cst; a.ck = (int)p.ck;
+  }
   a.gpr = (int)((p.dim + kW - 1) / kW);
   const int cus = cu_count();
   const ScanPlan pl = plan_scan(p.batch, p.dim, p.seqlen, cus);
@@ -803,7 +879,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
     err = hipGetLastError();
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0>), dim3(a.units), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0, CONV>), dim3(a.units), dim3(threads<0, TI>()), 0, stream, a);
       err = hipGetLastError();
     }
   } else if (K > 1) {
@@ -813,7 +889,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.seg_dt = a.seg_h + (size_t)K * chans * N;
     Args agg = a;
     agg.units = (int)((K - 1) * a.groups);  // the last segment's aggregate is never needed
-    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2>), dim3(agg.units), dim3(kThreads), 0, stream, agg);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2, CONV>), dim3(agg.units), dim3(threads<2, TI>()), 0, stream, agg);
     err = hipGetLastError();
     if (err == hipSuccess) {
       const int64_t pairs = chans * N;
@@ -822,13 +898,13 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1>), dim3(a.units), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, TI>()), 0, stream, a);
       err = hipGetLastError();
     }
   } else {
     // one segment: a plain output pass from h0 / zeros
     a.nseg = 1;
-    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1>), dim3(a.units), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, TI>()), 0, stream, a);
     err = hipGetLastError();
   }
   if (scratch) {
@@ -841,11 +917,11 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
 template <typename TI>
 hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
   switch (p.dstate) {
-    case 4: return run<4, TI>(p, s);
-    case 8: return run<8, TI>(p, s);
-    case 16: return run<16, TI>(p, s);
-    case 32: return run<32, TI>(p, s);
-    case 64: return run<64, TI>(p, s);
+    case 4: return run<4, TI, false>(p, s);
+    case 8: return run<8, TI, false>(p, s);
+    case 16: return run<16, TI, false>(p, s);
+    case 32: return run<32, TI, false>(p, s);
+    case 64: return run<64, TI, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -876,7 +952,13 @@ bool chunked_supported(const ScanParams& p) {
          p.batch < (1LL << 30) && al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C);
 }
 
+bool chunked_conv_supported(const ScanParams& p) { return p.dstate == 16 && chunked_supported(p); }
+
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream) {
+  if (p.cw) {  // fused convolution: dstate 16 (the others take the convolution kernel, then the scan)
+    if (p.dstate != 16) return hipErrorInvalidValue;
+    return p.dtype == kBF16 ? chunked::run<16, __bf16, true>(p, stream) : chunked::run<16, float, true>(p, stream);
+  }
   return p.dtype == kBF16 ? chunked::dispatch_n<__bf16>(p, stream) : chunked::dispatch_n<float>(p, stream);
 }
 

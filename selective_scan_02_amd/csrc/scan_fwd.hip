@@ -268,7 +268,39 @@ hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream) {
   return p.dtype == kBF16 ? dispatch_n<__bf16>(p, stream) : dispatch_n<float>(p, stream);
 }
 
+// Causal conv1d + SiLU and the scan in one call (p.cw set, p.u = x).  On the fast path the
+// convolution runs inside the scan kernels (u never reaches memory); otherwise the convolution
+// kernel writes u to scratch and the scan reads it.  Either way the convolution state is written
+// as causal_conv1d_fwd writes it.
+static hipError_t launch_scan_fwd_conv(const ScanParams& p, hipStream_t stream) {
+  ConvParams c{p.u, p.cw, p.cb, p.cst, 1, nullptr, p.cst_out, p.batch, p.dim, p.seqlen, p.ck, p.dtype};
+  ScanParams q = p;
+  q.cw = nullptr; q.cb = nullptr; q.cst = nullptr; q.cst_out = nullptr; q.ck = 0;
+  q.ws = nullptr; q.ws_bytes = 0;
+  if (p.seqlen == 0) {
+    hipError_t e = launch_conv1d_fwd(c, stream);  // state in -> state out
+    return e != hipSuccess ? e : launch_scan_generic(q, stream);
+  }
+  if (chunked_conv_supported(p)) {
+    hipError_t e = launch_scan_chunked(p, stream);
+    return e != hipSuccess ? e : launch_conv1d_state_out(c, stream);
+  }
+  const size_t bytes = (size_t)(p.batch * p.dim * p.seqlen) * (p.dtype == kBF16 ? 2 : 4);
+  void* u = nullptr;
+  hipError_t e = scratch_alloc(&u, bytes, stream);
+  if (e != hipSuccess) return e;
+  c.out = u;
+  e = launch_conv1d_fwd(c, stream);
+  if (e == hipSuccess) {
+    q.u = u;
+    e = launch_scan_fwd(q, stream);
+  }
+  const hipError_t f = hipFreeAsync(u, stream);
+  return e != hipSuccess ? e : f;
+}
+
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream) {
+  if (p.cw) return launch_scan_fwd_conv(p, stream);
   if (p.seqlen > 0 && chunked_supported(p)) return launch_scan_chunked(p, stream);
   return launch_scan_generic(p, stream);
 }

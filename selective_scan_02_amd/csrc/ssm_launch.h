@@ -27,6 +27,13 @@ struct ScanParams {
   // library's stream-ordered pool and returned to it.  With a workspace nothing is allocated.
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  // Causal conv1d + SiLU ahead of the scan (cw non-NULL): u = silu(conv(x)) is computed from
+  // x, which `u` then points to; cst = the inputs before step 0, cst_out receives the last ck-1.
+  const float* cw = nullptr;   // [dim, ck]
+  const float* cb = nullptr;   // [dim] or NULL
+  const float* cst = nullptr;  // [batch, dim, ck-1] or NULL
+  float* cst_out = nullptr;    // [batch, dim, ck-1] or NULL
+  int64_t ck = 0;
 };
 
 struct StepParams {
@@ -153,6 +160,7 @@ bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment
 bool chunked_supported(const ScanParams& p);
+bool chunked_conv_supported(const ScanParams& p);  // the fused convolution path (dstate 16)
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
 hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);
@@ -160,5 +168,8 @@ hipError_t launch_ssd_fwd(const SsdParams& p, hipStream_t stream);
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream);
+// The convolution state a sequence leaves (its last width-1 inputs, from the state before it
+// where the sequence is shorter), as causal_conv1d_fwd writes it.
+hipError_t launch_conv1d_state_out(const ConvParams& p, hipStream_t stream);
 
 }  // namespace ssm

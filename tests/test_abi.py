@@ -41,6 +41,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc",
+                 "selective_scan_fwd_conv",
                  "selective_scan_bwd", "ssd_scan_fwd",
                  "selective_state_update",
                  "causal_conv1d_fwd",
@@ -57,7 +58,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 7
+    assert lib.ssm_abi_version() == 8
 
 
 def scan_args(**over):
@@ -329,3 +330,23 @@ def test_noalloc_validation(lib):
 def test_handover_diagnostics_validation(lib):
     assert lib.ssm_handover_failures(None, 0) == NULL_ARG
     assert lib.ssm_test_handover_wait(0, 1) == 0   # the normal setting, restored
+
+
+def conv_scan_args(x=addr(1), w=addr(12), cb=addr(13), cst=addr(14), cso=addr(15), width=4, h0=None, **over):
+    a = scan_args(**over)
+    # (x, w, cb, st_in, st_out, width, delta, A, B, C, D, z, dt_bias, softplus, h0, y, last, sizes..., dtype, stream)
+    return [x if "u" not in over else a[0], w, cb, cst, cso, width] + a[1:9] + [h0] + a[9:]
+
+
+def test_conv_scan_validation(lib):
+    f = lib.selective_scan_fwd_conv
+    assert f(*conv_scan_args(w=None)) == NULL_ARG
+    assert f(*conv_scan_args(x=None)) == NULL_ARG
+    assert "x is NULL" in ssm.last_error()
+    assert f(*conv_scan_args(width=5)) == UNSUPPORTED
+    assert f(*conv_scan_args(width=0)) == UNSUPPORTED
+    assert f(*conv_scan_args(dstate=3)) == UNSUPPORTED
+    assert f(*conv_scan_args(w=addr(12) + 2)) == MISALIGNED
+    assert f(*conv_scan_args(cso=addr(14))) == ALIAS          # state out on state in
+    assert f(*conv_scan_args(cso=addr(9) + 64)) == ALIAS      # state out inside y
+    assert f(*conv_scan_args(cst=addr(9))) == ALIAS            # y over the state in
