@@ -76,6 +76,12 @@ namespace chunked {
 // 2.71, 2.65, 2.45-2.56, 2.46 and 2.62 ms
 #define SSM_SPLIT_UNITS_PER_CU 8
 #endif
+#ifndef SSM_SPLIT_OUT_PER_CU
+// output-pass workgroups per CU in the two-pass split: each continues through several
+// aggregate segments, so the pipeline fills and drains once per output unit (2^20-step fp32
+// sequence, 512 segments: 1, 2 and 8 output units per CU measured 2.44, 2.75-2.79, 2.50 ms)
+#define SSM_SPLIT_OUT_PER_CU 1
+#endif
 #ifndef SSM_HELPER_PRIO
 #define SSM_HELPER_PRIO 1
 #endif
@@ -127,6 +133,7 @@ struct Args {
   int64_t batch, dim, L, seg_len;
   int64_t tch;    // MODE 0: chunks per chain (ceil(L / kT))
   int64_t wlen;   // MODE 0: chunks per interval
+  int seg_stride;  // MODE 1 after MODE 2: aggregate segments per output unit (seg_h index step)
   int gpr;     // channel groups per batch row
   int groups;  // batch * gpr
   int nseg;    // K
@@ -370,8 +377,9 @@ void scan_chunked_kernel(const Args a) {
       }
     } else if (scanner) {
       if (MODE == 1 && a.seg_h) {
+        const int64_t ks = (int64_t)k * a.seg_stride;  // the aggregate segment this unit starts at
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[((int64_t)k * a.batch * a.dim + ch) * N + wv * NPW + j];
+        for (int j = 0; j < NPW; ++j) h[j] = a.seg_h[(ks * a.batch * a.dim + ch) * N + wv * NPW + j];
       } else if (MODE != 2 && t_begin == 0 && a.h0) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) h[j] = a.h0[ch * N + wv * NPW + j];
@@ -826,7 +834,12 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus) {
   pl.seg_len = ((nch_total + K - 1) / K) * kT;
   pl.nseg = std::max<int64_t>(1, (seqlen + pl.seg_len - 1) / pl.seg_len);
   pl.mode = pl.nseg == 1 ? 1 : 2;
-  pl.units = pl.nseg * pl.groups;
+  pl.out_stride = 1;
+  if (pl.mode == 2) {
+    const int64_t out_target = (int64_t)SSM_SPLIT_OUT_PER_CU * cus;
+    pl.out_stride = std::max<int64_t>(1, pl.nseg * pl.groups / std::max<int64_t>(1, out_target));
+  }
+  pl.units = ((pl.nseg + pl.out_stride - 1) / pl.out_stride) * pl.groups;
   return pl;
 }
 
@@ -862,6 +875,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
   a.seg_len = pl.seg_len;
   a.nseg = (int)pl.nseg;
   a.units = (int)pl.units;
+  a.seg_stride = 1;
   const int64_t K = pl.nseg;
   const int64_t chans = p.batch * p.dim;
   hipError_t err = hipSuccess;
@@ -889,6 +903,10 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.seg_dt = a.seg_h + (size_t)K * chans * N;
     Args agg = a;
     agg.units = (int)((K - 1) * a.groups);  // the last segment's aggregate is never needed
+    // the output pass: units of seg_stride consecutive segments, each from the carry at its start
+    a.seg_stride = (int)pl.out_stride;
+    a.seg_len = pl.seg_len * pl.out_stride;
+    a.nseg = (int)((K + pl.out_stride - 1) / pl.out_stride);
     hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2, CONV>), dim3(agg.units), dim3(threads<2, TI>()), 0, stream, agg);
     err = hipGetLastError();
     if (err == hipSuccess) {

@@ -121,6 +121,7 @@ struct ScanPlan {
   int64_t nseg;      // segments per group (modes 1, 2); intervals (mode 0)
   int64_t seg_len;   // steps per segment or per interval
   int64_t units;     // workgroups of the output pass
+  int64_t out_stride;  // mode 2: aggregate segments per output-pass workgroup
 };
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
 

@@ -16,7 +16,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "selective_scan_02_amd", "csrc", "scan_chunked.hip")
+SRCS = [os.path.join(ROOT, "selective_scan_02_amd", "csrc", f) for f in ("scan_chunked.hip",)]
 
 VGPR = re.compile(r"\bv\[?(\d+)(?::(\d+))?\]?")
 
@@ -31,12 +31,13 @@ def regs(tok):
     return set()
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "scan_chunked.s"
+@pytest.fixture(scope="module", params=SRCS, ids=lambda p: os.path.basename(p))
+def asm(request, tmp_path_factory):
+    src = request.param
+    out = tmp_path_factory.mktemp("isa") / (os.path.basename(src) + ".s")
     cmd = ["/opt/rocm/bin/hipcc", "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-o", str(out), SRC]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+           "-I", os.path.join(ROOT, "include"), "-o", str(out), src]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text().splitlines()
 
