@@ -92,25 +92,31 @@ namespace chunked {
 #define SSM_GATE_BLEND 1
 #endif
 
-#ifndef SSM_HELPERS_BF16
-#define SSM_HELPERS_BF16 4
+#ifndef SSM_SCAN_SG
+#define SSM_SCAN_SG 0  // 0: by states per scanner wave
 #endif
-#ifndef SSM_HELPERS_F32
-#define SSM_HELPERS_F32 4
+#ifndef SSM_HELPERS
+// helper waves of the output kernels: 8 (two per SIMD next to its scanner) measured 5% faster
+// than 4 on the 2.8B-shaped layer (0.229-0.232 against 0.241-0.246 ms, same box) and about 2%
+// on the 2^20-step sequence; the kernels with the fused convolution keep 4 (with 8 their helper
+// registers spill)
+#define SSM_HELPERS 8
 #endif
 
 constexpr int kT = 16;  // time steps per chunk (= lanes of a DPP row)
 constexpr int kW = 64;  // channels per group = lanes per wave
 constexpr int kS = 4;   // scanner waves
 
-// Helper waves per workgroup: 4 in the aggregate pass; the output kernels can take more.
-template <int MODE, typename TI>
+// Helper waves per workgroup: 4 in the aggregate pass, with the fused convolution and above
+// dstate 16 (twelve waves leave 168 registers per lane, and those scanners need more),
+// otherwise SSM_HELPERS.
+template <int MODE, bool CONV, int N>
 constexpr int helpers() {
-  return MODE == 2 ? 4 : sizeof(TI) == 2 ? SSM_HELPERS_BF16 : SSM_HELPERS_F32;
+  return MODE == 2 || CONV || N > 16 ? 4 : SSM_HELPERS;
 }
-template <int MODE, typename TI>
+template <int MODE, bool CONV, int N>
 constexpr int threads() {
-  return (kS + helpers<MODE, TI>()) * kW;
+  return (kS + helpers<MODE, CONV, N>()) * kW;
 }
 
 struct Args {
@@ -224,7 +230,7 @@ struct Smem {
 // allows it): on the 2^20-step fp32 sequence that made the two-pass scan 7% faster.  N = 64 would
 // spill under that cap and keeps one.
 template <int N, typename TI, int MODE, bool CONV>
-__global__ __launch_bounds__((threads<MODE, TI>()))
+__global__ __launch_bounds__((threads<MODE, CONV, N>()))
 __attribute__((amdgpu_waves_per_eu(MODE == 2 && N <= 32 ? 4 : 1)))
 void scan_chunked_kernel(const Args a) {
   constexpr int NPW = N / kS;        // states per scanner
@@ -232,7 +238,7 @@ void scan_chunked_kernel(const Args a) {
   // 2.44 ms against 2.59 at equal priority); in the interval schedule equal priority measured
   // better (2.8B-shaped layer: 201 us against 217).
   constexpr int kHelperPrio = MODE == 0 ? 0 : SSM_HELPER_PRIO;
-  constexpr int kH = helpers<MODE, TI>();  // helper waves
+  constexpr int kH = helpers<MODE, CONV, N>();  // helper waves
   constexpr int kHT = kH * kW;             // helper threads
   constexpr int kTPH = kT / kH;            // steps per helper thread per chunk
   static_assert(kT % kH == 0, "helpers split a chunk's steps evenly");
@@ -246,7 +252,7 @@ void scan_chunked_kernel(const Args a) {
   constexpr int LPT = (PIECES + kHT - 1) / kHT;  // pieces per helper thread
   constexpr int ROWB = Smem<N, TI, OUT>::ROWB;
   // steps per group of the scanner's exp-ahead / recurrence split (bounds the registers)
-  constexpr int SG = NPW <= 2 ? 16 : NPW <= 4 ? 8 : 4;
+  constexpr int SG = SSM_SCAN_SG > 0 ? SSM_SCAN_SG : NPW <= 2 ? 16 : NPW <= 4 ? 8 : 4;
   static_assert(N % kS == 0 && NPW >= 1, "dstate must be a multiple of 4");
   static_assert(kW * PPR <= kHT, "one y piece per helper thread");
 
@@ -893,7 +899,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
     err = hipGetLastError();
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0, CONV>), dim3(a.units), dim3(threads<0, TI>()), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0, CONV>), dim3(a.units), dim3(threads<0, CONV, N>()), 0, stream, a);
       err = hipGetLastError();
     }
   } else if (K > 1) {
@@ -907,7 +913,7 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.seg_stride = (int)pl.out_stride;
     a.seg_len = pl.seg_len * pl.out_stride;
     a.nseg = (int)((K + pl.out_stride - 1) / pl.out_stride);
-    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2, CONV>), dim3(agg.units), dim3(threads<2, TI>()), 0, stream, agg);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 2, CONV>), dim3(agg.units), dim3(threads<2, CONV, N>()), 0, stream, agg);
     err = hipGetLastError();
     if (err == hipSuccess) {
       const int64_t pairs = chans * N;
@@ -916,13 +922,13 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
-      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, TI>()), 0, stream, a);
+      hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, CONV, N>()), 0, stream, a);
       err = hipGetLastError();
     }
   } else {
     // one segment: a plain output pass from h0 / zeros
     a.nseg = 1;
-    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, TI>()), 0, stream, a);
+    hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 1, CONV>), dim3(a.units), dim3(threads<1, CONV, N>()), 0, stream, a);
     err = hipGetLastError();
   }
   if (scratch) {
