@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -540,23 +541,33 @@ struct Row8<float> {
 // group: consecutive threads take consecutive 16-byte pieces along a row, so every row segment
 // is read once and whole (a lane reading only its own row, 16 bytes at a time, leaves most of
 // each cache line to be fetched again by later chunks once other rows have evicted it).
-constexpr int kSC = 32;  // steps per staged tile (4 chunks)
-template <typename T>
+#ifndef SSM_BWD_PRE_TILE
+#define SSM_BWD_PRE_TILE 32
+#endif
+#ifndef SSM_BWD_MAIN_TILE
+#define SSM_BWD_MAIN_TILE 32
+#endif
+constexpr int kSC = SSM_BWD_PRE_TILE;    // steps per staged tile of the pre-passes
+constexpr int kSCM = SSM_BWD_MAIN_TILE;  // and of the main pass
+constexpr int kSCG = kSC > kSCM ? kSC : kSCM;  // segments are whole tiles of both
+static_assert(kSC % 8 == 0 && kSCM % 8 == 0 && kSCG % kSC == 0 && kSCG % kSCM == 0, "tiles of whole chunks");
+template <typename T, int SC = kSC>
 struct Tile {
   static constexpr int kPiece = 16 / (int)sizeof(T);              // elements per 16-byte piece
-  static constexpr int kRow = kSC + kPiece;                       // padded row (elements)
-  static constexpr int kPieces = kSC / kPiece;                    // pieces per row
+  static constexpr int kRow = SC + kPiece;                        // padded row (elements)
+  static constexpr int kPieces = SC / kPiece;                     // pieces per row
 };
 
 // Stage steps [ts0, ts1) (a multiple of 8, at most kSC) of the first `nt` of the NT tensors: rows
 // of the 64 channels of group `grp` of batch row `b` (channels past the end repeat the last one).
-// NTH threads take a tensor's pieces in rounds of 4 per thread; a round's loads are all issued
+// NTH threads take a tensor's pieces in rounds of up to 4 per thread; a round's loads are all issued
 // before the first is written to LDS.
-template <typename T, int NTH, int NT>
-__device__ __forceinline__ void stage_rows(T (*tile)[kWave][Tile<T>::kRow], const T* const (&bases)[NT], int nt,
+template <typename T, int NTH, int NT, int SC = kSC>
+__device__ __forceinline__ void stage_rows(T (*tile)[kWave][SC + 16 / sizeof(T)], const T* const (&bases)[NT], int nt,
                                            const BwdArgs& a, int64_t b, int64_t grp, int64_t ts0, int64_t ts1,
                                            int tid) {
-  constexpr int P = Tile<T>::kPieces, E = Tile<T>::kPiece, R = 4, PER = kWave * P;
+  constexpr int P = Tile<T, SC>::kPieces, E = Tile<T, SC>::kPiece, PER = kWave * P;
+  constexpr int R = (PER + NTH - 1) / NTH < 4 ? (PER + NTH - 1) / NTH : 4;
   asm volatile("" : "+v"(tid));  // addresses are recomputed per call, not held across the caller's loop
 #pragma unroll
   for (int kk = 0; kk < NT; ++kk) {
@@ -656,15 +667,23 @@ __device__ __forceinline__ float reduce8(const float (&v)[8], bool hi8) {
   return z;
 }
 
-// 1'. Checkpoint pass, 16-byte rows.
+// LDS of the fast pre-passes, which run in one launch: the checkpoint pass takes B rows and
+// two input tiles (u, delta), the adjoint aggregate C rows and three (delta, dy, z).
 template <int N, typename T>
-__global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
+struct PreLds {
+  static constexpr int kRows = kCT * N * (int)sizeof(float);
+  static constexpr int kTile = kWave * Tile<T>::kRow * (int)sizeof(T);
+  static constexpr int kBytes = kRows + 3 * kTile;
+};
+
+// 1'. Checkpoint pass, 16-byte rows: segment `seg` of this workgroup's channel group.
+template <int N, typename T>
+__device__ __forceinline__ void fbwd_checkpoint(const BwdArgs& a, int seg, unsigned char* lds) {
   using TL = Tile<T>;
-  __shared__ __align__(16) float sB[kCT][N];
-  __shared__ __align__(16) T sIn[2][kWave][TL::kRow];  // u, delta
+  float(*sB)[N] = reinterpret_cast<float(*)[N]>(lds);
+  T(*sIn)[kWave][TL::kRow] = reinterpret_cast<T(*)[kWave][TL::kRow]>(lds + PreLds<N, T>::kRows);  // u, delta
   const Lane l = lane_of(a);
   const int64_t grp = blockIdx.x % a.groups;
-  const int seg = blockIdx.y;
   const int64_t L = a.seqlen;
   const int64_t t0 = (int64_t)seg * a.seg_len;
   const int64_t t1 = std::min(t0 + a.seg_len, L);
@@ -740,15 +759,14 @@ __global__ __launch_bounds__(kWave) void fbwd_checkpoint_kernel(BwdArgs a) {
   a.seg_dt[(int64_t)seg * a.chans + l.ch] = cum;
 }
 
-// 3a'. Adjoint aggregate, 16-byte rows.
+// 3a'. Adjoint aggregate, 16-byte rows: segment `seg` (>= 1) of this workgroup's channel group.
 template <int N, typename T>
-__global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a) {
+__device__ __forceinline__ void fbwd_adjoint_aggregate(const BwdArgs& a, int seg, unsigned char* lds) {
   using TL = Tile<T>;
-  __shared__ __align__(16) float sC[kCT][N];
-  __shared__ __align__(16) T sIn[3][kWave][TL::kRow];  // delta, dy, z
+  float(*sC)[N] = reinterpret_cast<float(*)[N]>(lds);
+  T(*sIn)[kWave][TL::kRow] = reinterpret_cast<T(*)[kWave][TL::kRow]>(lds + PreLds<N, T>::kRows);  // delta, dy, z
   const Lane l = lane_of(a);
   const int64_t grp = blockIdx.x % a.groups;
-  const int seg = blockIdx.y + 1;
   const int64_t L = a.seqlen;
   const int64_t t0 = (int64_t)seg * a.seg_len;
   const int64_t t1 = std::min(t0 + a.seg_len, L);
@@ -820,6 +838,19 @@ __global__ __launch_bounds__(kWave) void fbwd_adjoint_aggregate_kernel(BwdArgs a
   for (int n = 0; n < N; n += 4) sl[n / 4] = make_float4(lam[n], lam[n + 1], lam[n + 2], lam[n + 3]);
 }
 
+// 1' and 3a' in one launch: rows 0 .. nseg-1 of the grid are the checkpoint pass of each segment,
+// rows nseg .. 2 nseg-2 the adjoint aggregate of segments 1 .. nseg-1.  The two need nothing of each
+// other, and one grid of both keeps twice the waves resident to hide each other's latency.
+template <int N, typename T>
+__global__ __launch_bounds__(kWave) void fbwd_pre_kernel(BwdArgs a) {
+  __shared__ __align__(16) unsigned char lds[PreLds<N, T>::kBytes];
+  const int y = blockIdx.y;
+  if (y < a.nseg)
+    fbwd_checkpoint<N, T>(a, y, lds);
+  else
+    fbwd_adjoint_aggregate<N, T>(a, y - a.nseg + 1, lds);
+}
+
 // 4'. Main pass, 16-byte rows: a workgroup of N/8 waves per (channel group, batch row) and
 // segment; wave w holds states 8w .. 8w+7 of the group's 64 channels.  Per chunk: stage B and
 // C; rerun the forward keeping h_{t-1} (readout partials to LDS, dC partials reduced across
@@ -831,7 +862,7 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   __shared__ __align__(16) float sBC[W][2][kCT][kSPW];
   __shared__ float sS[W][kCT][kWave];
   __shared__ float sP[W][2][kCT][kWave];
-  __shared__ __align__(16) T sIn[4][kWave][Tile<T>::kRow];  // u, delta, dy, z
+  __shared__ __align__(16) T sIn[4][kWave][Tile<T, kSCM>::kRow];  // u, delta, dy, z
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int64_t b = blockIdx.x / a.groups;
@@ -888,9 +919,9 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   };
   fetch(t1 - kCT);
   for (int64_t tc = t1 - kCT; tc >= t0; tc -= kCT) {
-    const int64_t j0 = t0 + (tc - t0) / kSC * kSC;  // start of this chunk's tile
-    if (tc == t1 - kCT || tc + kCT == j0 + kSC)
-      stage_rows<T, kWave * W, 4>(sIn, bases, zz ? 4 : 3, a, b, grp, j0, std::min(j0 + kSC, t1), threadIdx.x);
+    const int64_t j0 = t0 + (tc - t0) / kSCM * kSCM;  // start of this chunk's tile
+    if (tc == t1 - kCT || tc + kCT == j0 + kSCM)
+      stage_rows<T, kWave * W, 4, kSCM>(sIn, bases, zz ? 4 : 3, a, b, grp, j0, std::min(j0 + kSCM, t1), threadIdx.x);
     const Raw rbc = nbc;
     const float4 k0 = nk0, k1 = nk1;
     const float kd = nkd;
@@ -1037,6 +1068,477 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
   }
 }
 
+// 4''. Main pass with roles, 16-byte rows, dstate 8, 16 or 32: a workgroup of 8 waves per
+// (channel group, batch row) and segment.  Scanner waves 0-3 hold N/4 states each of the group's
+// 64 channels; per chunk of 8 steps (right to left) a scanner reruns the forward from the
+// chunk's checkpoint keeping Abar and h_{t-1} of every step in registers, then runs the adjoint
+// back over them, reduces its dB and dC contributions across the wave's lanes and leaves three
+// partial sums over its states per element in LDS.  Helper waves 4-7 own 2 steps of every chunk:
+// they stage the input rows (u, delta, dy, z) in 64-byte tiles, compute the per-element terms the
+// scanners read (Delta, Delta u, ds) and keep those the epilogue needs, stage B and C, and one
+// chunk behind the scanners sum the four partials in a fixed order into dz, du and ddelta, which
+// the next iteration stores as 16-byte row pieces.  One workgroup barrier per chunk: iteration k
+// scans chunk k, preps chunk k+1, finishes chunk k-1 and stores chunk k-2.
+#ifndef SSM_BWD_ROLES
+#define SSM_BWD_ROLES 1
+#endif
+// Scanner waves: 4 (one per SIMD).  Eight (two per SIMD, N/8 states each; bf16 up to dstate 16
+// only, where LDS holds eight scanners' partial sums) measured no faster on the 2.8B-shaped layer:
+// the scanners alone ran 13% faster, but together with the helpers no faster than four.
+#ifndef SSM_BWD_SCANNERS_BF16
+#define SSM_BWD_SCANNERS_BF16 4
+#endif
+template <typename T, int N>
+constexpr int roles_scanners() { return sizeof(T) == 2 && N <= 16 ? SSM_BWD_SCANNERS_BF16 : 4; }
+constexpr int kRH = 4;                      // helper waves, 2 steps of each chunk apiece
+template <typename T, int N>
+constexpr int roles_threads() { return (roles_scanners<T, N>() + kRH) * kWave; }
+constexpr int kRItems = 7;                  // per-element terms: Delta, Delta u, ds, u, sg, gz, gz D u
+
+// Staged input tiles: P 16-byte pieces of each row (64 bytes with four scanners, 32 with eight).
+template <typename T, int P>
+struct RTile {
+  static constexpr int kPieces = P;
+  static constexpr int kPiece = 16 / (int)sizeof(T);      // elements per 16-byte piece
+  static constexpr int kSteps = P * kPiece;               // steps per tile
+  static constexpr int kRow = kSteps + kPiece;            // padded row (elements)
+};
+template <typename T, int N>
+using RTileOf = RTile<T, roles_scanners<T, N>() == 4 ? 4 : 2>;
+
+template <int N, typename T>
+struct RolesSmem {
+  static constexpr int S = roles_scanners<T, N>();
+  T tile[2][4][kWave][RTileOf<T, N>::kRow];      // u, delta, dy, z; tile m in buffer m % 2
+  float prep[2][kRItems][kCT][kWave];         // chunk c in slot c % 2
+  float part[2][3][S][kCT][kWave];            // readout, sum lam B, sum q A per scanner
+  float bcs[S][2][kCT][N / S];                // each scanner's B and C rows of its chunk, [t][n]
+  T out[2][3][kWave][kCT];                    // dz, du, ddelta of a chunk
+  float dbc[2][2][N][kCT];                    // dB and dC partials of a chunk (this channel group)
+};
+
+template <int K>
+__device__ __forceinline__ void lds_vec(const float* p, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < K; k += 4) {
+      const float4 q = *(const float4*)(p + k);
+      v[k] = q.x; v[k + 1] = q.y; v[k + 2] = q.z; v[k + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; k += 2) {
+      const float2 q = *(const float2*)(p + k);
+      v[k] = q.x; v[k + 1] = q.y;
+    }
+  }
+}
+
+// Two consecutive elements of a tile row / an output row.
+__device__ __forceinline__ void lds_pair(const __bf16* p, float& x, float& y) {
+  const uint32_t w = *(const uint32_t*)p;
+  x = __uint_as_float(w << 16);
+  y = __uint_as_float(w & 0xffff0000u);
+}
+__device__ __forceinline__ void lds_pair(const float* p, float& x, float& y) {
+  const float2 q = *(const float2*)p;
+  x = q.x; y = q.y;
+}
+__device__ __forceinline__ void lds_put_pair(__bf16* p, float x, float y) {
+  __bf16 t[2] = {(__bf16)x, (__bf16)y};
+  uint32_t w;
+  __builtin_memcpy(&w, t, sizeof w);
+  *(uint32_t*)p = w;
+}
+__device__ __forceinline__ void lds_put_pair(float* p, float x, float y) { *(float2*)p = make_float2(x, y); }
+
+template <int N, typename T>
+__global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kernel(BwdArgs a) {
+  constexpr int kRS = roles_scanners<T, N>();
+  constexpr int NPW = N / kRS;           // states per scanner
+  constexpr int SPG = kCT / NPW < 1 ? 1 : kCT / NPW;  // steps per 8-value lane reduction
+  static_assert(N % kRS == 0 && NPW * SPG == 8, "a lane reduction takes 8 values: whole steps of NPW states");
+  using RT = RTileOf<T, N>;
+  __shared__ __align__(16) RolesSmem<N, T> sm;
+  const int wv = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t b = blockIdx.x / a.groups;
+  const int64_t grp = blockIdx.x % a.groups;
+  const int64_t d = grp * kWave + lane;
+  const bool active = d < a.dim;
+  const int64_t dd = active ? d : a.dim - 1;
+  const int64_t ch = b * a.dim + dd;
+  const int seg = blockIdx.y;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = (int64_t)seg * a.seg_len;
+  const int64_t t1 = std::min(t0 + a.seg_len, L);
+  const int nch = (int)((t1 - t0) / kCT);  // chunk k covers steps [t1 - 8(k+1), t1 - 8k)
+  const bool gated = a.z != nullptr;
+  const bool multi = a.nseg > 1;
+  auto chunk_t = [&](int k) { return t1 - (int64_t)kCT * (k + 1); };
+  auto tile_of = [&](int k) { return (int)((chunk_t(k) - t0) / RT::kSteps); };
+
+  if (wv < kRS) {
+    // ------------------------------------------------------------------ scanner
+    const int n0 = wv * NPW;
+    float A2[NPW], hin[NPW], lam[NPW], dA[NPW];
+    {
+      const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        A2[j] = a.A[dd * N + n0 + j] * kLog2e;
+        hin[j] = multi ? a.seg_h[k + j] : (a.h0 ? a.h0[ch * N + n0 + j] : 0.0f);
+        lam[j] = (multi && active) ? a.seg_l[k + j] : 0.0f;
+        dA[j] = 0.0f;
+      }
+    }
+    // dB / dC partial of this group: after the 8-value reduction lane l holds value
+    // reduce8_index(l) of reduction (l & 7); NPW * SPG = 8 values per reduction, NPW reductions
+    const int jr = reduce8_index(lane);
+    const bool hi8 = (lane & 8) != 0;
+    const int rsel = lane & 7;
+    const bool rkeep = rsel < NPW;
+    const int ri = (rkeep ? rsel : 0) * SPG + jr / NPW, rj = jr % NPW;  // (step, state) of the kept value
+    float nk[NPW], nkd = 0.0f;
+    auto fetch_ck = [&](int k) {
+      const int64_t tc = chunk_t(k);
+      if (tc > t0) {
+        const int64_t kg = tc / kCT;
+        const float* ck = a.ck_h + (kg * a.chans + ch) * N + n0;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) nk[j] = ck[j];
+        nkd = a.ck_dt[kg * a.chans + ch];
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) nk[j] = 0.0f;
+    // this scanner's B and C rows (its states, the chunk's 8 steps) are loaded a chunk ahead, in
+    // 16-byte pieces, and written to its own LDS rows when the chunk starts: with the checkpoint
+    // they are the scanner's only memory traffic, all loads, waited for a whole chunk later
+    constexpr int kPPR = (int)sizeof(T) * kCT / 16;  // pieces per row (1 bf16, 2 fp32)
+    constexpr int kE = 16 / (int)sizeof(T);           // steps per piece
+    static_assert(2 * NPW * kPPR <= kWave, "one B/C piece per lane");
+    const bool sbl = lane < 2 * NPW * kPPR;
+    const int sbw = lane / (NPW * kPPR), sbn = (lane / kPPR) % NPW, sbq = lane % kPPR;
+    const T* sbrow = (sbw == 0 ? (const T*)a.B : (const T*)a.C) + (b * N + n0 + (sbl ? sbn : 0)) * L + sbq * kE;
+    typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+    u32x4s sbv = {0, 0, 0, 0};
+    auto sb_load = [&](int k) {
+      if (sbl) sbv = *(const u32x4s*)(sbrow + chunk_t(k));
+    };
+    auto sb_store = [&]() {
+      if (!sbl) return;
+      float v[kE];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(sbv[i] << 16);
+          v[2 * i + 1] = __uint_as_float(sbv[i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(sbv[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kE; ++i) sm.bcs[wv][sbw][sbq * kE + i][sbn] = v[i];
+    };
+    if (nch > 0) {
+      fetch_ck(0);
+      sb_load(0);
+    }
+    __syncthreads();  // prologue: tiles staged
+    __syncthreads();  // prologue: chunk 0 prepared
+    for (int k = 0; k < nch + 2; ++k) {
+      if (k < nch) {
+        const int64_t tc = chunk_t(k);
+        const int sl = k & 1;
+        float h[NPW];
+        if (tc == t0) {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) h[j] = hin[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * nkd), hin[j], nk[j]);
+        }
+        sb_store();
+        if (k + 1 < nch) {
+          sb_load(k + 1);
+          fetch_ck(k + 1);
+        }
+        float dt[kCT], dut[kCT], ds[kCT];
+#pragma unroll
+        for (int i = 0; i < kCT; ++i) {
+          dt[i] = sm.prep[sl][0][i][lane];
+          dut[i] = sm.prep[sl][1][i][lane];
+          ds[i] = sm.prep[sl][2][i][lane];
+        }
+        // forward over the chunk: Abar and h_{t-1} kept for the adjoint
+        float ab[kCT][NPW], hp[kCT][NPW];
+        float keepC = 0.0f, vals[8];
+#pragma unroll
+        for (int i = 0; i < kCT; ++i) {
+          float Bv[NPW], Cv[NPW];
+          lds_vec<NPW>(&sm.bcs[wv][0][i][0], Bv);
+          lds_vec<NPW>(&sm.bcs[wv][1][i][0], Cv);
+          float s = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) {
+            ab[i][j] = ex2(dt[i] * A2[j]);
+            hp[i][j] = h[j];
+            h[j] = __builtin_fmaf(ab[i][j], h[j], dut[i] * Bv[j]);
+            s = __builtin_fmaf(Cv[j], h[j], s);
+            vals[(i % SPG) * NPW + j] = ds[i] * h[j];
+          }
+          sm.part[sl][0][wv][i][lane] = s;
+          if (i % SPG == SPG - 1) {
+            const float r = reduce8(vals, hi8);
+            if (rsel == i / SPG) keepC = r;
+          }
+        }
+        if (rkeep) sm.dbc[sl][1][n0 + rj][ri] = keepC;
+        // adjoint back over the chunk
+        float keepB = 0.0f;
+#pragma unroll
+        for (int i = kCT - 1; i >= 0; --i) {
+          float Bv[NPW], Cv[NPW];
+          lds_vec<NPW>(&sm.bcs[wv][0][i][0], Bv);
+          lds_vec<NPW>(&sm.bcs[wv][1][i][0], Cv);
+          float accB = 0.0f, accQ = 0.0f;
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) {
+            const float lt = __builtin_fmaf(ds[i], Cv[j], lam[j]);
+            accB = __builtin_fmaf(lt, Bv[j], accB);
+            vals[(i % SPG) * NPW + j] = lt * dut[i];
+            const float lp = ab[i][j] * lt;
+            const float q = lp * hp[i][j];
+            accQ = __builtin_fmaf(q, A2[j], accQ);
+            dA[j] = __builtin_fmaf(q, dt[i], dA[j]);
+            lam[j] = lp;
+          }
+          sm.part[sl][1][wv][i][lane] = accB;
+          sm.part[sl][2][wv][i][lane] = accQ;
+          if (i % SPG == 0) {
+            const float r = reduce8(vals, hi8);
+            if (rsel == i / SPG) keepB = r;
+          }
+        }
+        if (rkeep) sm.dbc[sl][0][n0 + rj][ri] = keepB;
+      }
+      __syncthreads();
+    }
+    __syncthreads();  // the helpers' sums
+    if (active) {
+      const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) a.pA[k + j] = dA[j];
+      if (seg == 0 && a.dh0) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) a.dh0[ch * N + n0 + j] = lam[j];
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------------- helper
+  const int hw = wv - kRS;       // this thread's steps of a chunk: 2 hw and 2 hw + 1
+  const int htid = threadIdx.x - kRS * kWave;
+  const float bias = a.dt_bias ? a.dt_bias[dd] : 0.0f;
+  const float Dd = a.D ? a.D[dd] : 0.0f;
+  const int ntens = gated ? 4 : 3;
+  const T* const bases[4] = {(const T*)a.u, (const T*)a.delta, (const T*)a.dy, (const T*)a.z};
+  float accD = 0.0f, accbias = 0.0f;
+  // tile pieces: helper waves 0 and 1 load them (64 rows x P pieces of each tensor, P/2 per thread)
+  // a whole tile ahead; loads are all these two waves issue, so their waits cover nothing else
+  constexpr int TP = RT::kPieces, TPT = TP / 2;
+  const bool tl = hw < 2;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 tv[TPT][4];
+  auto piece = [&](int j, int& row, int& pc) {
+    const int p = htid + j * 2 * kWave;
+    row = p / TP;
+    pc = p % TP;
+  };
+  auto tile_load = [&](int m) {
+    if (!tl) return;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      int row, pc;
+      piece(j, row, pc);
+      const int64_t tch = b * a.dim + std::min<int64_t>(grp * kWave + row, a.dim - 1);
+      const int64_t ts = t0 + (int64_t)m * RT::kSteps + pc * RT::kPiece;
+      const int64_t tsl = ts < t1 ? ts : t0 + (int64_t)m * RT::kSteps;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < ntens) tv[j][q] = *(const u32x4*)(bases[q] + tch * L + tsl);
+    }
+  };
+  auto tile_store = [&](int m) {
+    if (!tl) return;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      int row, pc;
+      piece(j, row, pc);
+      const int64_t ts = t0 + (int64_t)m * RT::kSteps + pc * RT::kPiece;
+      if (ts < t1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < ntens) *(u32x4*)&sm.tile[m & 1][q][row][pc * RT::kPiece] = tv[j][q];
+      }
+    }
+  };
+  // the per-element terms of chunk k for this thread's two steps
+  auto prep = [&](int k) {
+    const int sl = k & 1;
+    const int64_t tc = chunk_t(k);
+    const int m = tile_of(k);
+    const int off = (int)(tc - (t0 + (int64_t)m * RT::kSteps)) + 2 * hw;
+    float uu[2], dl[2], gy[2], zz[2] = {0.0f, 0.0f};
+    lds_pair(&sm.tile[m & 1][0][lane][off], uu[0], uu[1]);
+    lds_pair(&sm.tile[m & 1][1][lane][off], dl[0], dl[1]);
+    lds_pair(&sm.tile[m & 1][2][lane][off], gy[0], gy[1]);
+    if (gated) lds_pair(&sm.tile[m & 1][3][lane][off], zz[0], zz[1]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * hw + e;
+      const float x = dl[e] + bias;
+      const float dt = step_size(x, a.softplus);
+      float ds = gy[e], gz = 0.0f;
+      if (gated) {
+        const float sz = sigmoid(zz[e]);
+        ds = gy[e] * zz[e] * sz;
+        gz = gy[e] * sz * __builtin_fmaf(zz[e], 1.0f - sz, 1.0f);
+      }
+      if (!active) ds = 0.0f;
+      accD = __builtin_fmaf(ds, uu[e], accD);
+      sm.prep[sl][0][i][lane] = dt;
+      sm.prep[sl][1][i][lane] = dt * uu[e];
+      sm.prep[sl][2][i][lane] = ds;
+      sm.prep[sl][3][i][lane] = uu[e];
+      sm.prep[sl][4][i][lane] = a.softplus ? sigmoid(x) : 1.0f;
+      sm.prep[sl][5][i][lane] = gz;
+      sm.prep[sl][6][i][lane] = gz * Dd * uu[e];
+    }
+  };
+  // dz, du, ddelta of chunk k for this thread's two steps, into the output tile
+  auto finish = [&](int k) {
+    const int sl = k & 1;
+    float o[3][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * hw + e;
+      float s = 0.0f, sb = 0.0f, sq = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kRS; ++w) {
+        s += sm.part[sl][0][w][i][lane];
+        sb += sm.part[sl][1][w][i][lane];
+        sq += sm.part[sl][2][w][i][lane];
+      }
+      const float dt = sm.prep[sl][0][i][lane], ds = sm.prep[sl][2][i][lane];
+      const float uu = sm.prep[sl][3][i][lane], sg = sm.prep[sl][4][i][lane];
+      o[0][e] = __builtin_fmaf(sm.prep[sl][5][i][lane], s, sm.prep[sl][6][i][lane]);
+      o[1][e] = __builtin_fmaf(dt, sb, ds * Dd);
+      o[2][e] = __builtin_fmaf(sq, kLn2, uu * sb) * sg;
+      accbias += o[2][e];
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) lds_put_pair(&sm.out[sl][q][lane][2 * hw], o[q][0], o[q][1]);
+  };
+  T* const outs[3] = {(T*)a.dz, (T*)a.du, (T*)a.ddelta};
+  // all global stores come from the last helper wave (dz, du, ddelta rows here, the dB and dC
+  // partials below): reusing a register a store reads waits for the store to complete, and only
+  // this wave should pay for that
+  auto store = [&](int k) {
+    if (hw != kRH - 1 || !active) return;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (q == 0 && !gated) continue;
+      float v[kCT];
+#pragma unroll
+      for (int i = 0; i < kCT; i += 2) lds_pair(&sm.out[k & 1][q][lane][i], v[i], v[i + 1]);
+      Row8<T>::store(outs[q] + ch * L + chunk_t(k), v);
+    }
+  };
+
+  // the dB and dC partials of chunk k (from LDS, 4 steps per 16-byte piece) by helper wave 3
+  auto store_bc = [&](int k) {
+    if (hw != kRH - 1) return;
+    const int64_t tc = chunk_t(k);
+#pragma unroll
+    for (int p0 = 0; p0 < 4 * N; p0 += kWave) {
+      const int q = p0 + lane;
+      if (q < 4 * N) {
+        const int w = q / (2 * N), n = (q / 2) % N, hf = q % 2;
+        const float4 v = *(const float4*)&sm.dbc[k & 1][w][n][4 * hf];
+        float* dst = (w == 0 ? a.pB : a.pC) + ((grp * a.batch + b) * N + n) * L + tc + 4 * hf;
+        *(float4*)dst = v;
+      }
+    }
+  };
+
+  // Helper waves 0 and 1 only load (tiles, a whole tile ahead), wave 3 only stores: on this GPU
+  // one counter tracks a wave's loads and stores together, and reusing a register a store reads
+  // waits for the store to complete, so a wave that mixed them would wait for its stores too.
+  int tnext = -1;  // the tile whose pieces are in flight in tv
+  if (nch > 0) {  // prologue: the tiles of chunks 0 and 1 (they differ when chunk 0 ends a short last tile)
+    int last = tile_of(0);
+    tile_load(last);
+    tile_store(last);
+    if (nch > 1 && tile_of(1) != last) {
+      last = tile_of(1);
+      tile_load(last);
+      tile_store(last);
+    }
+    if (last > 0) {
+      tnext = last - 1;
+      tile_load(tnext);
+    }
+  }
+  __syncthreads();
+  if (nch > 0) prep(0);
+  __syncthreads();
+  // the storing wave runs its own copy of the loop, so that the waits its stores need are not
+  // compiled into the loaders' code
+  auto loop = [&](auto storer) {
+    for (int k = 0; k < nch + 2; ++k) {
+      if constexpr (decltype(storer)::value) {
+        if (k >= 2) store(k - 2);
+        if (k >= 1 && k - 1 < nch) store_bc(k - 1);
+      }
+      if (k >= 1 && k - 1 < nch) finish(k - 1);
+      if (k + 1 < nch) prep(k + 1);
+      if constexpr (!decltype(storer)::value) {
+        // chunk k+2 starts the tile in flight: it goes to LDS now, and the next one is requested
+        if (k + 2 < nch && tile_of(k + 2) != tile_of(k + 1)) {
+          tile_store(tnext);
+          tnext = tnext > 0 ? tnext - 1 : -1;
+          if (tnext >= 0) tile_load(tnext);
+        }
+      }
+      __syncthreads();
+    }
+  };
+  if (hw == kRH - 1)
+    loop(std::true_type{});
+  else
+    loop(std::false_type{});
+  // the helpers' dD and ddt_bias sums, through the partials' LDS (no longer in use)
+  float(*acc)[2][kWave] = reinterpret_cast<float(*)[2][kWave]>(&sm.part[0][0][0][0][0]);
+  static_assert(sizeof(sm.part) >= sizeof(float) * kRH * 2 * kWave, "room for the helpers' sums");
+  acc[hw][0][lane] = accD;
+  acc[hw][1][lane] = accbias;
+  __syncthreads();
+  if (hw == 0 && active) {
+    float sD = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kRH; ++w) {
+      sD += acc[w][0][lane];
+      sb += acc[w][1][lane];
+    }
+    a.pD[(int64_t)seg * a.chans + ch] = sD;
+    a.pbias[(int64_t)seg * a.chans + ch] = sb;
+  }
+}
+
 hipError_t zero(float* p, int64_t n, hipStream_t s) {
   if (!p || n == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
@@ -1079,8 +1581,10 @@ bool fast_ok(const BwdParams& p) {
 
 template <int N, typename T, bool FAST>
 hipError_t run(const BwdParams& p, hipStream_t stream) {
+  // the main pass with scanner and helper roles (dstate 8, 16, 32), else the symmetric one
+  constexpr bool ROLES = FAST && SSM_BWD_ROLES && (N == 8 || N == 16 || N == 32);
   constexpr int CT = FAST ? kCT : Chunk<N>::T;
-  constexpr int GR = FAST ? kSC : CT;     // segment lengths are multiples of this (whole staged tiles)
+  constexpr int GR = FAST ? kSCG : CT;    // segment lengths are multiples of this (whole staged tiles)
   constexpr int W = FAST ? N / kSPW : 1;  // waves per workgroup of the main pass
   BwdArgs a{};
   a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
@@ -1098,14 +1602,19 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   };
   static const Slots sl = [] {
     const int64_t cus = bwd_cu_count();
-    if constexpr (FAST)
-      return Slots{cus * resident_blocks(fbwd_main_kernel<N, T>, kWave * W),
-                   cus * resident_blocks(fbwd_checkpoint_kernel<N, T>, kWave),
-                   cus * resident_blocks(fbwd_adjoint_aggregate_kernel<N, T>, kWave)};
-    else
+    if constexpr (FAST) {
+      int64_t m;
+      if constexpr (ROLES)
+        m = cus * resident_blocks(fbwd_main_roles_kernel<N, T>, roles_threads<T, N>());
+      else
+        m = cus * resident_blocks(fbwd_main_kernel<N, T>, kWave * W);
+      return Slots{m, cus * resident_blocks(fbwd_pre_kernel<N, T>, kWave),
+                   cus * resident_blocks(fbwd_pre_kernel<N, T>, kWave)};
+    } else {
       return Slots{cus * resident_blocks(bwd_main_kernel<N, T>, kWave),
                    cus * resident_blocks(bwd_checkpoint_kernel<N, T>, kWave),
                    cus * resident_blocks(bwd_adjoint_aggregate_kernel<N, T>, kWave)};
+    }
   }();
   const int64_t slots_main = sl.main, slots_ck = sl.ck, slots_adj = sl.adj;
   int64_t nseg = 1, seg_len = (L + GR - 1) / GR * GR;
@@ -1118,8 +1627,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
       const int64_t len = ((L + k - 1) / k + GR - 1) / GR * GR;
       const int64_t real = (L + len - 1) / len;
       // a workgroup's start (first loads, checkpoint, carries) costs about 4 chunks
-      const int64_t cost = (len + 4 * CT) * (2 * rounds(units * real, slots_main) + rounds(units * real, slots_ck) +
-                                             (real > 1 ? rounds(units * (real - 1), slots_adj) : 0));
+      // (the fast path runs the two pre-passes as one grid)
+      const int64_t pre = FAST ? rounds(units * (2 * real - 1), slots_ck)
+                               : rounds(units * real, slots_ck) + (real > 1 ? rounds(units * (real - 1), slots_adj) : 0);
+      const int64_t cost = (len + 4 * CT) * (2 * rounds(units * real, slots_main) + pre);
       if (best < 0 || cost < best || (cost == best && real < nseg)) {
         best = cost;
         nseg = real;
@@ -1152,8 +1663,9 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     q += (fl[i] + 63) / 64 * 64;
   }
   const dim3 grid((unsigned)units, (unsigned)nseg);
-  if constexpr (FAST)
-    hipLaunchKernelGGL((fbwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
+  if constexpr (FAST)  // checkpoints and adjoint aggregates in one grid
+    hipLaunchKernelGGL((fbwd_pre_kernel<N, T>), dim3((unsigned)units, (unsigned)(2 * nseg - 1)), dim3(kWave), 0,
+                       stream, a);
   else
     hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
   err = hipGetLastError();
@@ -1161,12 +1673,9 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_fwd_carry_kernel, dim3(blocks_of(chans * N)), dim3(256), 0, stream, a.seg_h, a.seg_dt,
                        p.A, p.h0, chans, p.dim, N, (int)nseg);
     err = hipGetLastError();
-    if (err == hipSuccess) {
+    if (err == hipSuccess && !FAST) {
       const dim3 g1((unsigned)units, (unsigned)(nseg - 1));
-      if constexpr (FAST)
-        hipLaunchKernelGGL((fbwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
+      hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
       err = hipGetLastError();
     }
     if (err == hipSuccess) {
@@ -1176,7 +1685,9 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     }
   }
   if (err == hipSuccess) {
-    if constexpr (FAST)
+    if constexpr (ROLES)
+      hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T>), grid, dim3(roles_threads<T, N>()), 0, stream, a);
+    else if constexpr (FAST)
       hipLaunchKernelGGL((fbwd_main_kernel<N, T>), grid, dim3(kWave * W), 0, stream, a);
     else
       hipLaunchKernelGGL((bwd_main_kernel<N, T>), grid, dim3(kWave), 0, stream, a);

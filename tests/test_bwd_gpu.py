@@ -90,11 +90,17 @@ SMALL = [
     (1, 20, 64, 77, "f32", {"h0": True}),
     (1, 5, 16, 1, "f32", {"h0": True}),
     (1, 192, 16, 2048, "bf16", {}),
-    # 16-byte rows (fast path): partial staged tiles, one to eight waves per channel group
+    # 16-byte rows (fast path): partial staged tiles; the main pass with scanner and helper waves
+    # (dstate 8-32: eight scanners with bf16 inputs up to dstate 16, else four) or with symmetric
+    # waves (dstate 64)
     (2, 130, 16, 520, "bf16", {"h0": True}),
     (1, 64, 8, 264, "f32", {"with_z": False}),
     (2, 100, 64, 136, "bf16", {}),
     (1, 70, 32, 4104, "f32", {"h0": True}),
+    (2, 100, 8, 264, "bf16", {"h0": True}),
+    (1, 70, 32, 1032, "bf16", {}),
+    (1, 64, 16, 24, "bf16", {"with_z": False, "h0": True}),     # one short last tile: three chunks
+    (1, 130, 16, 808, "f32", {"softplus": False, "with_bias": False, "delta_scale": 0.02}),
 ]
 
 
