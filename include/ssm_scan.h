@@ -315,14 +315,18 @@ int ssm_scan_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, in
  * over; the wait for it is bounded (2^26 polls) so that no launch can hang.  A wait that
  * runs out means that state never arrived: the waiting piece then computes from NaN, so
  * its outputs and the final state are visibly invalid, and a device-side counter is
- * incremented (once per waiting wave, four per sequence).  This call copies the current
- * device's counter to *count (a synchronous device read) and, with reset != 0, sets it to
- * zero.  Required: count.  Errors: SSM_ERR_NULL_ARG, SSM_ERR_HIP.
+ * incremented (once per waiting wave, four per sequence).  The backward's main pass, when
+ * it runs on intervals (chains, batch row x channel group, at least as many as resident
+ * workgroups), hands the adjoint on the same way, right to left, and counts its give-ups
+ * in a second counter (a give-up poisons the adjoint, hence the gradients of that part of
+ * the sequence and the parameter gradients).  This call copies the sum of the current
+ * device's counters to *count (a synchronous device read) and, with reset != 0, sets them
+ * to zero.  Required: count.  Errors: SSM_ERR_NULL_ARG, SSM_ERR_HIP.
  */
 int ssm_handover_failures(int64_t* count, int reset);
 
 /*
- * Test hook for the give-up path above, process-wide, for the launches that follow:
+ * Test hook for the give-up path above (scan and backward), process-wide, for the launches that follow:
  * max_polls bounds the wait (<= 0 restores 2^26) and publish = 0 makes the first pieces
  * skip setting their hand-over flags, so that every waiting piece gives up after max_polls
  * polls while every kernel still runs to its end.  (max_polls <= 0, publish = 1) is the

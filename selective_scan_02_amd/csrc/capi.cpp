@@ -113,9 +113,10 @@ int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 int ssm_handover_failures(int64_t* count, int reset) {
   g_last_error.clear();
   if (!count) return fail(SSM_ERR_NULL_ARG, "count is NULL");
-  uint64_t v = 0;
+  uint64_t v = 0, w = 0;
   if (int rc = hip_status(ssm::handover_failures(&v, reset != 0), "ssm_handover_failures")) return rc;
-  *count = (int64_t)v;
+  if (int rc = hip_status(ssm::bwd_handover_failures(&w, reset != 0), "ssm_handover_failures")) return rc;
+  *count = (int64_t)(v + w);
   return SSM_OK;
 }
 

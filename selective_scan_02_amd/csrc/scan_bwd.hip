@@ -83,7 +83,18 @@ struct BwdArgs {
   float* pbias;   // [S, chans]
   int64_t batch, dim, seqlen, seg_len, chans;
   int groups, nseg, softplus;
+  // main pass on the interval plan (iunits > 0)
+  int* ticket;    // 1 counter
+  int* flags;     // [chains, scanner waves] hand-over flags
+  float* hand_l;  // [chains, N, 64] the adjoint handed over at a split point
+  int64_t wlen;   // chunks per interval
+  int iunits;     // intervals (workgroups); 0: the segment plan
+  int max_polls;  // bound of a hand-over wait
+  int publish;    // 0 only under the test hook: split points never publish
 };
+
+// Hand-over waits of the main pass that gave up (bwd_handover_failures).
+static __device__ unsigned int bwd_handover_giveups;
 
 struct Lane {
   int lane;
@@ -1082,6 +1093,9 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
 #ifndef SSM_BWD_ROLES
 #define SSM_BWD_ROLES 1
 #endif
+#ifndef SSM_BWD_INTERVALS
+#define SSM_BWD_INTERVALS 1
+#endif
 // Scanner waves: 4 (one per SIMD).  Eight (two per SIMD, N/8 states each; bf16 up to dstate 16
 // only, where LDS holds eight scanners' partial sums) measured no faster on the 2.8B-shaped layer:
 // the scanners alone ran 13% faster, but together with the helpers no faster than four.
@@ -1115,6 +1129,7 @@ struct RolesSmem {
   float bcs[S][2][kCT][N / S];                // each scanner's B and C rows of its chunk, [t][n]
   T out[2][3][kWave][kCT];                    // dz, du, ddelta of a chunk
   float dbc[2][2][N][kCT];                    // dB and dC partials of a chunk (this channel group)
+  int ticket;                                 // interval plan: this workgroup's interval
 };
 
 template <int K>
@@ -1162,35 +1177,111 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
   __shared__ __align__(16) RolesSmem<N, T> sm;
   const int wv = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int64_t b = blockIdx.x / a.groups;
-  const int64_t grp = blockIdx.x % a.groups;
+  const int64_t L = a.seqlen;
+  const int64_t tchn = L / kCT;  // chunks per chain
+  const bool gated = a.z != nullptr;
+  const bool multi = a.nseg > 1;  // checkpoints relative to segments with a carried incoming state
+
+  // The pieces this workgroup runs.  Segment plan: one, segment blockIdx.y of chain blockIdx.x,
+  // with the adjoint entering from the right taken from the reverse carry.  Interval plan: the
+  // chains (batch row x channel group) laid end to end in processing order, right to left, cut
+  // into one interval of wlen chunks per workgroup (wlen >= a chain, so a chain is split at most
+  // once); the interval comes from a ticket.  Its pieces run in the order: the right part of its
+  // last chain first (it waits for nothing, and the next interval's workgroup waits for the
+  // adjoint it hands over at its left end), then the whole chains, then the left part of its
+  // first chain, which starts from the adjoint the previous interval's workgroup handed over.
+  int64_t is = 0, ie = 0, cf = 0, cl = 0;
+  bool itail = false, ihead = false;
+  int npieces = 1;
+  if (a.iunits > 0) {
+    if (threadIdx.x == 0) sm.ticket = atomicAdd(a.ticket, 1);
+    __syncthreads();
+    const int ival = __builtin_amdgcn_readfirstlane(sm.ticket);
+    if (ival >= a.iunits) return;  // uniform: the whole workgroup leaves
+    const int64_t total = a.batch * a.groups * tchn;
+    is = (int64_t)ival * a.wlen;
+    ie = is + a.wlen < total ? is + a.wlen : total;
+    cf = is / tchn;
+    cl = (ie - 1) / tchn;
+    itail = is > cf * tchn;
+    ihead = ie < (cl + 1) * tchn;
+    npieces = (int)(cl - cf + 1);
+  }
+  for (int pc = 0; pc < npieces; ++pc) {
+  int64_t cid, k0, k1;  // chain, and its chunks [k0, k1) in processing order (chunk 0: the last 8 steps)
+  int slot;             // where the piece's sums over time go (pA, pD, pbias)
+  if (a.iunits > 0) {
+    if (ihead && pc == 0) {
+      cid = cl;
+    } else {
+      const int q = pc - (ihead ? 1 : 0);
+      const int nfull = npieces - (ihead ? 1 : 0) - (itail ? 1 : 0);
+      cid = q < nfull ? cf + (itail ? 1 : 0) + q : cf;
+    }
+    const int64_t p0 = cid * tchn > is ? cid * tchn : is;
+    const int64_t p1 = (cid + 1) * tchn < ie ? (cid + 1) * tchn : ie;
+    k0 = p0 - cid * tchn;
+    k1 = p1 - cid * tchn;
+    slot = k0 > 0 ? 1 : 0;
+  } else {
+    cid = blockIdx.x;
+    slot = blockIdx.y;
+    const int64_t s0 = (int64_t)blockIdx.y * a.seg_len;
+    const int64_t s1 = s0 + a.seg_len < L ? s0 + a.seg_len : L;
+    k0 = (L - s1) / kCT;
+    k1 = (L - s0) / kCT;
+  }
+  const bool wait_in = a.iunits > 0 && k0 > 0;      // the adjoint comes from another workgroup
+  const bool hand_out = a.iunits > 0 && k1 < tchn;  // and goes to another one
+  const bool whole = a.iunits > 0 && k0 == 0 && k1 == tchn;  // slot 1 of the chain stays zero
+  const int64_t b = cid / a.groups;
+  const int64_t grp = cid % a.groups;
   const int64_t d = grp * kWave + lane;
   const bool active = d < a.dim;
   const int64_t dd = active ? d : a.dim - 1;
   const int64_t ch = b * a.dim + dd;
-  const int seg = blockIdx.y;
-  const int64_t L = a.seqlen;
-  const int64_t t0 = (int64_t)seg * a.seg_len;
-  const int64_t t1 = std::min(t0 + a.seg_len, L);
-  const int nch = (int)((t1 - t0) / kCT);  // chunk k covers steps [t1 - 8(k+1), t1 - 8k)
-  const bool gated = a.z != nullptr;
-  const bool multi = a.nseg > 1;
+  const int64_t t0 = L - kCT * k1;
+  const int64_t t1 = L - kCT * k0;
+  const int nch = (int)(k1 - k0);  // chunk k of the piece covers steps [t1 - 8(k+1), t1 - 8k)
   auto chunk_t = [&](int k) { return t1 - (int64_t)kCT * (k + 1); };
   auto tile_of = [&](int k) { return (int)((chunk_t(k) - t0) / RT::kSteps); };
 
   if (wv < kRS) {
     // ------------------------------------------------------------------ scanner
     const int n0 = wv * NPW;
-    float A2[NPW], hin[NPW], lam[NPW], dA[NPW];
-    {
-      const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+    float A2[NPW], lam[NPW], dA[NPW];
 #pragma unroll
-      for (int j = 0; j < NPW; ++j) {
-        A2[j] = a.A[dd * N + n0 + j] * kLog2e;
-        hin[j] = multi ? a.seg_h[k + j] : (a.h0 ? a.h0[ch * N + n0 + j] : 0.0f);
-        lam[j] = (multi && active) ? a.seg_l[k + j] : 0.0f;
-        dA[j] = 0.0f;
+    for (int j = 0; j < NPW; ++j) {
+      A2[j] = a.A[dd * N + n0 + j] * kLog2e;
+      dA[j] = 0.0f;
+    }
+    if (wait_in) {
+      // Hand-over (interval plan): wait for the flag of the matching scanner wave of the
+      // chain's right part, then read its rows of the adjoint.  Flag and adjoint are device-scope
+      // atomics, coherent across the XCDs' L2 caches; the loads are issued only after the flag
+      // has been seen.  The wait is bounded; if it runs out the piece is poisoned with NaN and
+      // counted, so that a broken hand-over cannot pass for numbers.
+      const int* f = a.flags + cid * kRS + wv;
+      bool arrived = true;
+      for (int spin = 0;
+           __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
+           ++spin) {
+        if (spin >= a.max_polls) {
+          arrived = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
+      const float* hp0 = a.hand_l + cid * N * kWave;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j)
+        lam[j] = arrived ? __hip_atomic_load(hp0 + (n0 + j) * kWave + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : __builtin_nanf("");
+      if (!arrived && lane == 0) atomicAdd(&bwd_handover_giveups, 1u);
+    } else {
+      const int64_t k = ((int64_t)slot * a.chans + ch) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) lam[j] = (a.iunits == 0 && multi && active) ? a.seg_l[k + j] : 0.0f;
     }
     // dB / dC partial of this group: after the 8-value reduction lane l holds value
     // reduce8_index(l) of reduction (l & 7); NPW * SPG = 8 values per reduction, NPW reductions
@@ -1199,19 +1290,28 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
     const int rsel = lane & 7;
     const bool rkeep = rsel < NPW;
     const int ri = (rkeep ? rsel : 0) * SPG + jr / NPW, rj = jr % NPW;  // (step, state) of the kept value
-    float nk[NPW], nkd = 0.0f;
+    // a chunk's starting state: its checkpoint (relative to the checkpoint pass's segment) plus
+    // exp(A * sum Delta) times that segment's incoming state, or the incoming state itself when
+    // the chunk starts the segment
+    float nk[NPW], nhin[NPW], nkd = 0.0f;
+    bool nat = false;
     auto fetch_ck = [&](int k) {
       const int64_t tc = chunk_t(k);
-      if (tc > t0) {
+      const int64_t s = tc / a.seg_len;
+      nat = tc == s * a.seg_len;
+      if (!nat) {
         const int64_t kg = tc / kCT;
         const float* ck = a.ck_h + (kg * a.chans + ch) * N + n0;
 #pragma unroll
         for (int j = 0; j < NPW; ++j) nk[j] = ck[j];
         nkd = a.ck_dt[kg * a.chans + ch];
       }
+      const int64_t ks = (s * a.chans + ch) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) nhin[j] = multi ? a.seg_h[ks + j] : (a.h0 ? a.h0[ch * N + n0 + j] : 0.0f);
     };
 #pragma unroll
-    for (int j = 0; j < NPW; ++j) nk[j] = 0.0f;
+    for (int j = 0; j < NPW; ++j) nk[j] = nhin[j] = 0.0f;
     // this scanner's B and C rows (its states, the chunk's 8 steps) are loaded a chunk ahead, in
     // 16-byte pieces, and written to its own LDS rows when the chunk starts: with the checkpoint
     // they are the scanner's only memory traffic, all loads, waited for a whole chunk later
@@ -1253,12 +1353,12 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
         const int64_t tc = chunk_t(k);
         const int sl = k & 1;
         float h[NPW];
-        if (tc == t0) {
+        if (nat) {
 #pragma unroll
-          for (int j = 0; j < NPW; ++j) h[j] = hin[j];
+          for (int j = 0; j < NPW; ++j) h[j] = nhin[j];
         } else {
 #pragma unroll
-          for (int j = 0; j < NPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * nkd), hin[j], nk[j]);
+          for (int j = 0; j < NPW; ++j) h[j] = __builtin_fmaf(ex2(A2[j] * nkd), nhin[j], nk[j]);
         }
         sb_store();
         if (k + 1 < nch) {
@@ -1326,18 +1426,36 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
       }
       __syncthreads();
     }
+    if (hand_out) {
+      // the adjoint at the piece's left end, for the workgroup that runs the rest of the chain;
+      // the flag is set once every store of it is acknowledged (the signal fences keep the
+      // compiler from moving memory operations across the wait)
+      float* hp0 = a.hand_l + cid * N * kWave;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j)
+        __hip_atomic_store(hp0 + (n0 + j) * kWave + lane, lam[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.publish) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(a.flags + cid * kRS + wv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     __syncthreads();  // the helpers' sums
     if (active) {
-      const int64_t k = ((int64_t)seg * a.chans + ch) * N + n0;
+      const int64_t k = ((int64_t)slot * a.chans + ch) * N + n0;
 #pragma unroll
       for (int j = 0; j < NPW; ++j) a.pA[k + j] = dA[j];
-      if (seg == 0 && a.dh0) {
+      if (whole) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) a.pA[k + a.chans * N + j] = 0.0f;
+      }
+      if (t0 == 0 && a.dh0) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) a.dh0[ch * N + n0 + j] = lam[j];
       }
     }
-    return;
-  }
+  } else {
 
   // -------------------------------------------------------------------- helper
   const int hw = wv - kRS;       // this thread's steps of a chunk: 2 hw and 2 hw + 1
@@ -1534,9 +1652,15 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
       sD += acc[w][0][lane];
       sb += acc[w][1][lane];
     }
-    a.pD[(int64_t)seg * a.chans + ch] = sD;
-    a.pbias[(int64_t)seg * a.chans + ch] = sb;
+    a.pD[(int64_t)slot * a.chans + ch] = sD;
+    a.pbias[(int64_t)slot * a.chans + ch] = sb;
+    if (whole) {
+      a.pD[(int64_t)(slot + 1) * a.chans + ch] = 0.0f;
+      a.pbias[(int64_t)(slot + 1) * a.chans + ch] = 0.0f;
+    }
   }
+  }  // helper
+  }  // pieces
 }
 
 hipError_t zero(float* p, int64_t n, hipStream_t s) {
@@ -1617,6 +1741,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     }
   }();
   const int64_t slots_main = sl.main, slots_ck = sl.ck, slots_adj = sl.adj;
+  // Interval plan for the main pass when there are at least as many chains (batch row x channel
+  // group) as resident main-pass workgroups: no adjoint aggregate, no reverse carry; the
+  // checkpoint pass keeps segments of its own.
+  const bool IV = ROLES && SSM_BWD_INTERVALS && units >= slots_main;
   int64_t nseg = 1, seg_len = (L + GR - 1) / GR * GR;
   {
     const int64_t max_seg = std::max<int64_t>(1, std::min<int64_t>(8192, L / (4 * CT)));
@@ -1628,9 +1756,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
       const int64_t real = (L + len - 1) / len;
       // a workgroup's start (first loads, checkpoint, carries) costs about 4 chunks
       // (the fast path runs the two pre-passes as one grid)
-      const int64_t pre = FAST ? rounds(units * (2 * real - 1), slots_ck)
+      const int64_t pre = FAST ? rounds(units * (IV ? real : 2 * real - 1), slots_ck)
                                : rounds(units * real, slots_ck) + (real > 1 ? rounds(units * (real - 1), slots_adj) : 0);
-      const int64_t cost = (len + 4 * CT) * (2 * rounds(units * real, slots_main) + pre);
+      // on the interval plan the main pass does not depend on the segment count
+      const int64_t cost = (len + 4 * CT) * ((IV ? 0 : 2 * rounds(units * real, slots_main)) + pre);
       if (best < 0 || cost < best || (cost == best && real < nseg)) {
         best = cost;
         nseg = real;
@@ -1647,25 +1776,39 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   a.seg_len = seg_len;
   a.nseg = (int)nseg;
   const int64_t nchunks = (L + CT - 1) / CT;
+  // sums over time per (slot, channel): one slot per segment, or on the interval plan two per chain
+  // (its right part or whole, and its left part)
+  const int64_t pslots = IV ? 2 : nseg;
+  const int kRSc = ROLES ? roles_scanners<T, N>() : 1;
   const size_t fl[] = {(size_t)(nchunks * chans * N), (size_t)(nchunks * chans), (size_t)(nseg * chans * N),
                        (size_t)(nseg * chans), (size_t)(nseg * chans * N), (size_t)(a.groups * p.batch * N * L),
-                       (size_t)(a.groups * p.batch * N * L), (size_t)(nseg * chans * N), (size_t)(nseg * chans),
-                       (size_t)(nseg * chans)};
+                       (size_t)(a.groups * p.batch * N * L), (size_t)(pslots * chans * N), (size_t)(pslots * chans),
+                       (size_t)(pslots * chans), (size_t)(IV ? units * N * kWave : 0),
+                       (size_t)(IV ? 64 + units * kRSc : 0)};
   size_t total = 0;
   for (size_t f : fl) total += (f + 63) / 64 * 64;  // 256-byte aligned pieces
   void* scratch = nullptr;
   hipError_t err = scratch_alloc(&scratch, total * sizeof(float), stream);
   if (err != hipSuccess) return err;
   float* q = (float*)scratch;
-  float** dst[] = {&a.ck_h, &a.ck_dt, &a.seg_h, &a.seg_dt, &a.seg_l, &a.pB, &a.pC, &a.pA, &a.pD, &a.pbias};
-  for (int i = 0; i < 10; ++i) {
+  float* ctl = nullptr;
+  float** dst[] = {&a.ck_h, &a.ck_dt, &a.seg_h, &a.seg_dt, &a.seg_l, &a.pB, &a.pC, &a.pA, &a.pD, &a.pbias, &a.hand_l, &ctl};
+  for (int i = 0; i < 12; ++i) {
     *dst[i] = q;
     q += (fl[i] + 63) / 64 * 64;
   }
+  if (IV) {
+    a.ticket = (int*)ctl;
+    a.flags = a.ticket + 64;
+    const int64_t work = units * (L / kCT);
+    a.wlen = (work + slots_main - 1) / slots_main;  // >= a chain, since units >= slots_main
+    a.iunits = (int)((work + a.wlen - 1) / a.wlen);
+    handover_wait(&a.max_polls, &a.publish);
+  }
   const dim3 grid((unsigned)units, (unsigned)nseg);
-  if constexpr (FAST)  // checkpoints and adjoint aggregates in one grid
-    hipLaunchKernelGGL((fbwd_pre_kernel<N, T>), dim3((unsigned)units, (unsigned)(2 * nseg - 1)), dim3(kWave), 0,
-                       stream, a);
+  if constexpr (FAST)  // checkpoints (and, on the segment plan, adjoint aggregates) in one grid
+    hipLaunchKernelGGL((fbwd_pre_kernel<N, T>), dim3((unsigned)units, (unsigned)(IV ? nseg : 2 * nseg - 1)),
+                       dim3(kWave), 0, stream, a);
   else
     hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
   err = hipGetLastError();
@@ -1678,15 +1821,17 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, T>), g1, dim3(kWave), 0, stream, a);
       err = hipGetLastError();
     }
-    if (err == hipSuccess) {
+    if (err == hipSuccess && !IV) {
       hipLaunchKernelGGL(bwd_adjoint_carry_kernel, dim3(blocks_of(chans * N)), dim3(256), 0, stream, a.seg_l,
                          a.seg_dt, p.A, chans, p.dim, N, (int)nseg);
       err = hipGetLastError();
     }
   }
+  if (err == hipSuccess && IV) err = zero(ctl, 64 + units * kRSc, stream);  // ticket and flags (0.0f is all zero bits)
   if (err == hipSuccess) {
     if constexpr (ROLES)
-      hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T>), grid, dim3(roles_threads<T, N>()), 0, stream, a);
+      hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T>), IV ? dim3((unsigned)a.iunits) : grid,
+                         dim3(roles_threads<T, N>()), 0, stream, a);
     else if constexpr (FAST)
       hipLaunchKernelGGL((fbwd_main_kernel<N, T>), grid, dim3(kWave * W), 0, stream, a);
     else
@@ -1705,7 +1850,7 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   }
   if (err == hipSuccess) {
     hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(blocks_of(p.dim * N)), dim3(256), 0, stream, a.pA, a.pD,
-                       a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)nseg);
+                       a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)pslots);
     err = hipGetLastError();
   }
   const hipError_t ferr = hipFreeAsync(scratch, stream);
@@ -1728,6 +1873,18 @@ hipError_t dispatch_n(const BwdParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t bwd_handover_failures(uint64_t* count, bool reset) {
+  unsigned int v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(bwd_handover_giveups), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *count = v;
+  if (reset) {
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(bwd_handover_giveups), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  }
+  return e;
+}
 
 hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.seqlen == 0) {

@@ -964,6 +964,10 @@ hipError_t handover_failures(uint64_t* count, bool reset) {
   return e;
 }
 
+void handover_wait(int* max_polls, int* publish) {
+  *max_polls = chunked::g_max_polls.load();
+  *publish = chunked::g_publish.load();
+}
 void set_handover_wait(int max_polls, int publish) {
   chunked::g_max_polls.store(max_polls > 0 ? max_polls : 1 << 26);
   chunked::g_publish.store(publish ? 1 : 0);

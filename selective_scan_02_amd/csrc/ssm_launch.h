@@ -155,7 +155,9 @@ int device_cu_count();
 // on the current device since the last reset; and the test hook that bounds the wait and can
 // suppress the head pieces' flags.
 hipError_t handover_failures(uint64_t* count, bool reset);
+hipError_t bwd_handover_failures(uint64_t* count, bool reset);  // the backward main pass's
 void set_handover_wait(int max_polls, int publish);
+void handover_wait(int* max_polls, int* publish);  // the current settings
 
 bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher

@@ -101,6 +101,11 @@ SMALL = [
     (1, 70, 32, 1032, "bf16", {}),
     (1, 64, 16, 24, "bf16", {"with_z": False, "h0": True}),     # one short last tile: three chunks
     (1, 130, 16, 808, "f32", {"softplus": False, "with_bias": False, "delta_scale": 0.02}),
+    # at least as many chains (batch row x channel group) as CUs: the main pass on intervals, chains
+    # split between two workgroups and the adjoint handed over at the split
+    (4, 4100, 16, 136, "bf16", {"h0": True}),
+    (4, 5000, 8, 264, "f32", {"with_z": False}),
+    (2, 8200, 32, 64, "bf16", {}),
 ]
 
 
@@ -153,3 +158,50 @@ def test_bwd_empty_sequence_gives_zero_parameter_gradients():
     for k in ("dA", "dD", "ddt_bias", "dh0"):
         assert torch.count_nonzero(got[k]) == 0, k
     assert got["du"].numel() == 0 and got["dB"].numel() == 0
+
+
+def test_bwd_intervals_deterministic():
+    """The main pass on intervals (chains handed over between workgroups) is bitwise reproducible."""
+    x = gen.random_scan_inputs(4, 4100, 16, 264, "bf16", seed=8)
+    note("bwd on intervals run twice, bitwise")
+    dy = upstream(x, 8)
+    a, b = gpu_bwd(x, dy), gpu_bwd(x, dy)
+    for k in KEYS:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_bwd_handover_giveup_poisons_and_counts():
+    """A hand-over wait of the backward's main pass that gives up (forced from the host: the
+    right parts of split chains skip their flags, the wait is bounded at a few polls) counts one
+    give-up per scanner wave of every split chain and leaves NaN in the gradients that depend on
+    the missing adjoint; every kernel still runs to its end, and the next normal call is
+    bit-identical to one made before."""
+    b, d, n, L = 4, 4100, 16, 264
+    x = gen.random_scan_inputs(b, d, n, L, "bf16", seed=9)
+    dy = upstream(x, 9)
+    note(f"bwd hand-over give-up B={b} D={d} N={n} L={L}")
+    ref = gpu_bwd(x, dy)
+    ssm.handover_failures(reset=True)
+    try:
+        ssm.set_handover_wait(max_polls=64, publish=False)
+        bad = gpu_bwd(x, dy)
+    finally:
+        ssm.set_handover_wait(0, True)
+    count = ssm.handover_failures(reset=True)
+    # the interval plan: chains laid end to end, cut into as many intervals as CUs (one
+    # workgroup of the main pass per CU); a chain is split where an interval boundary falls
+    # inside it
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    chains, tch = b * ((d + 63) // 64), L // 8
+    wlen = -(-chains * tch // cus)
+    units = -(-chains * tch // wlen)
+    split = sum(1 for i in range(1, units) if (i * wlen) % tch)
+    note(f"  {split} split chains, {count} waits gave up")
+    assert split > 0 and count == 4 * split
+    assert torch.isnan(bad["du"].float()).any() and torch.isnan(bad["dA"]).any()
+    again = gpu_bwd(x, dy)
+    assert ssm.handover_failures(reset=True) == 0
+    for k in KEYS:
+        if ref[k] is not None:
+            assert torch.equal(again[k], ref[k]), k
