@@ -64,6 +64,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "ssm_device.h"
 #include "ssm_launch.h"
@@ -134,8 +137,9 @@ struct Args {
   float* seg_h;   // MODE 1/2: [K, batch*dim, N]
   float* seg_dt;  // MODE 2:   [K, batch*dim]
   float* carry;   // MODE 0:   [groups, N, 64] state at a chain's split point
-  int* flags;     // MODE 0:   [groups, kS] one per chain and scanner wave
-  int* ticket;    // MODE 0:   1 counter
+  unsigned long long* flags;   // MODE 0: [groups, kS] one per chain and scanner wave: the call's `gen` once set
+  unsigned long long* ticket;  // MODE 0: interval counter; this call's tickets are tbase, tbase + 1, ...
+  unsigned long long tbase, gen;
   int64_t batch, dim, L, seg_len;
   int64_t tch;    // MODE 0: chunks per chain (ceil(L / kT))
   int64_t wlen;   // MODE 0: chunks per interval
@@ -277,7 +281,7 @@ void scan_chunked_kernel(const Args a) {
     __builtin_amdgcn_s_waitcnt(0);                                                                \
     __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                      \
     if (lane == 0)                                                                                \
-      __hip_atomic_store(a.flags + (int64_t)(U) * kS + wv, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+      __hip_atomic_store(a.flags + (int64_t)(U) * kS + wv, a.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
   }
 
   // MODE 0: this workgroup's interval [is, ie) of the chains laid end to end (chunk units),
@@ -286,7 +290,7 @@ void scan_chunked_kernel(const Args a) {
   bool itail = false, ihead = false;
   int npieces = 1;
   if (MODE == 0) {
-    if (tid == 0) sm.unit = atomicAdd(a.ticket, 1);
+    if (tid == 0) sm.unit = (int)(atomicAdd(a.ticket, 1ull) - a.tbase);
     __syncthreads();
     const int ival = __builtin_amdgcn_readfirstlane(sm.unit);
     if (ival >= a.units) return;  // uniform: the whole workgroup leaves
@@ -354,10 +358,11 @@ void scan_chunked_kernel(const Args a) {
     // helpers meanwhile start loading the piece's first chunks.
     if (MODE == 0 && wait_in) {
       if (scanner) {
-        const int* f = a.flags + (int64_t)grp * kS + wv;
-        bool arrived = true;  // wave-uniform: the flag is read through readfirstlane
+        const unsigned long long* f = a.flags + (int64_t)grp * kS + wv;
+        bool arrived = true;  // wave-uniform: the comparison is read through readfirstlane
         for (int spin = 0;
-             __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
+             __builtin_amdgcn_readfirstlane(
+                 (int)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.gen)) == 0;
              ++spin) {
           if (spin >= a.max_polls) {  // bounded: never hang (only a broken launch could get here)
             arrived = false;
@@ -856,7 +861,8 @@ size_t chunked_scratch_bytes(const ScanParams& p, int cus) {
   using namespace chunked;
   const ScanPlan pl = plan_scan(p.batch, p.dim, p.seqlen, cus);
   const size_t N = (size_t)p.dstate;
-  if (pl.mode == 0) return (size_t)pl.groups * N * kW * sizeof(float) + ((size_t)pl.groups * kS + 64) * sizeof(int);
+  if (pl.mode == 0)
+    return (size_t)pl.groups * N * kW * sizeof(float) + ((size_t)pl.groups * kS + 8) * sizeof(unsigned long long);
   if (pl.nseg > 1) return (size_t)pl.nseg * (size_t)(p.batch * p.dim) * (N + 1) * sizeof(float);
   return 0;
 }
@@ -890,18 +896,31 @@ hipError_t run(const ScanParams& p, hipStream_t stream) {
     a.tch = (p.seqlen + kT - 1) / kT;
     a.wlen = pl.seg_len / kT;
     const size_t carry_bytes = (size_t)a.groups * N * kW * sizeof(float);
-    const size_t bytes = carry_bytes + ((size_t)a.groups * kS + 64) * sizeof(int);
-    if ((err = scratch_acquire(p, &scratch, bytes, stream)) != hipSuccess) return err;
+    // The ticket and the flags: the stream's persistent control block when there is one (no
+    // clearing per call), else in this call's scratch behind the carry, cleared by a fill kernel
+    // (under graph capture, and with a caller's workspace).
+    const bool ctl = p.ws == nullptr && interval_ctl(stream, (int64_t)a.groups * kS, a.units, &a.ticket, &a.flags,
+                                                     &a.tbase, &a.gen);
+    const size_t bytes = carry_bytes + (ctl ? 0 : ((size_t)a.groups * kS + 8) * sizeof(unsigned long long));
+    if ((err = scratch_acquire(p, &scratch, bytes, stream)) != hipSuccess) {
+      if (ctl) interval_ctl_invalidate(stream);
+      return err;
+    }
     a.carry = (float*)scratch;
-    a.ticket = (int*)((char*)scratch + carry_bytes);
-    a.flags = a.ticket + 64;
-    const int nints = a.groups * kS + 64;
-    hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, a.ticket, nints);
-    err = hipGetLastError();
+    if (!ctl) {
+      a.ticket = (unsigned long long*)((char*)scratch + carry_bytes);
+      a.flags = a.ticket + 8;
+      a.tbase = 0;
+      a.gen = 1;
+      const int nints = (a.groups * kS + 8) * 2;
+      hipLaunchKernelGGL(zero_ints, dim3((nints + 255) / 256), dim3(256), 0, stream, (int*)a.ticket, nints);
+      err = hipGetLastError();
+    }
     if (err == hipSuccess) {
       hipLaunchKernelGGL((scan_chunked_kernel<N, TI, 0, CONV>), dim3(a.units), dim3(threads<0, CONV, N>()), 0, stream, a);
       err = hipGetLastError();
     }
+    if (err != hipSuccess && ctl) interval_ctl_invalidate(stream);
   } else if (K > 1) {
     const size_t bytes = (size_t)K * chans * (N + 1) * sizeof(float);
     if ((err = scratch_acquire(p, &scratch, bytes, stream)) != hipSuccess) return err;
@@ -951,6 +970,69 @@ hipError_t dispatch_n(const ScanParams& p, hipStream_t s) {
 }
 
 }  // namespace chunked
+
+// Persistent interval control blocks, one per (device, stream): a 64-bit ticket counter that only
+// grows and the hand-over flags, each holding the generation of the call that set it last.  A call
+// takes tickets base .. base + units - 1 and sets its flags to its own generation, so nothing needs
+// clearing between calls: the calls on one stream run in order, and the host counts the tickets and
+// generations they use.  A block is cleared once, when made; one that is outgrown or whose launch
+// failed is dropped but never freed (work queued before may still use it).
+namespace {
+struct IntervalCtl {
+  unsigned long long* mem = nullptr;  // [ticket, 7 spare, flags ...]
+  int64_t cap = 0;                    // flags held
+  unsigned long long tickets = 0;     // tickets of the calls launched so far
+  unsigned long long gen = 0;         // generation of the last call
+};
+std::mutex g_ctl_mutex;
+std::map<std::pair<int, hipStream_t>, IntervalCtl> g_ctl;
+}  // namespace
+
+bool interval_ctl(hipStream_t s, int64_t nflags, int64_t units, unsigned long long** ticket,
+                  unsigned long long** flags, unsigned long long* base, unsigned long long* gen) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return false;  // a captured launch would replay one generation: clear flags per call instead
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lk(g_ctl_mutex);
+  IntervalCtl& c = g_ctl[{dev, s}];
+  if (c.mem == nullptr || c.cap < nflags) {
+    const int64_t cap = std::max<int64_t>(nflags, 4096);
+    void* m = nullptr;
+    if (hipMalloc(&m, (size_t)(cap + 8) * sizeof(unsigned long long)) != hipSuccess) {
+      (void)hipGetLastError();
+      c.mem = nullptr;
+      return false;
+    }
+    const int nints = (int)((cap + 8) * 2);
+    hipLaunchKernelGGL(chunked::zero_ints, dim3((nints + 255) / 256), dim3(256), 0, s, (int*)m, nints);
+    if (hipGetLastError() != hipSuccess) {
+      c.mem = nullptr;  // m is dropped: the fill may or may not have been queued
+      return false;
+    }
+    c.mem = (unsigned long long*)m;
+    c.cap = cap;
+    c.tickets = 0;
+    c.gen = 0;
+  }
+  *ticket = c.mem;
+  *flags = c.mem + 8;
+  *base = c.tickets;
+  c.tickets += (unsigned long long)units;
+  *gen = ++c.gen;
+  return true;
+}
+
+void interval_ctl_invalidate(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_ctl_mutex);
+  auto it = g_ctl.find({dev, s});
+  if (it != g_ctl.end()) it->second.mem = nullptr;
+}
 
 hipError_t handover_failures(uint64_t* count, bool reset) {
   unsigned int v = 0;

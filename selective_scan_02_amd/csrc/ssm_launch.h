@@ -155,6 +155,12 @@ int device_cu_count();
 // on the current device since the last reset; and the test hook that bounds the wait and can
 // suppress the head pieces' flags.
 hipError_t handover_failures(uint64_t* count, bool reset);
+// The stream's persistent interval control block (ticket and hand-over flags that need no clearing
+// per call): this call's ticket base and flag generation.  False under graph capture or when the
+// block cannot be made; the caller then clears a ticket and flags of its own.
+bool interval_ctl(hipStream_t s, int64_t nflags, int64_t units, unsigned long long** ticket,
+                  unsigned long long** flags, unsigned long long* base, unsigned long long* gen);
+void interval_ctl_invalidate(hipStream_t s);  // after a failed launch: the next call makes a new block
 hipError_t bwd_handover_failures(uint64_t* count, bool reset);  // the backward main pass's
 void set_handover_wait(int max_polls, int publish);
 void handover_wait(int* max_polls, int* publish);  // the current settings
