@@ -417,7 +417,42 @@ def bench_ssd(torch, gen, ssm, steps, fwd_ms):
             "mfma": {"achieved": tf, "peak": 2500.0, "unit": "TFLOP/s", "frac": tf / 2500.0,
                      "flops_per_element": ssd_flops_per_element(N), "dtype": "bf16"},
             "vs_selective_scan": fwd_ms / ms, "inputs_rotated": copies,
-            "note": "bound by HBM (about 6 bytes against 145 matrix-core flops per element)"}
+            "note": "bound by HBM (about 6 bytes against 145 matrix-core flops per element)",
+            "backward": bench_ssd_bwd(torch, ssm, ins, max(3, steps // 5), ms)}
+
+
+def bench_ssd_bwd(torch, ssm, ins, steps, fwd_ms):
+    """ssd_scan_bwd on the same layer: the backward scan's kernels on the step sizes broadcast to
+    the channels, then the per-head sums.  ALU fraction against the backward scan's algorithmic
+    count (algo_slots_bwd), elements counted once."""
+    x0 = ins[0]
+    Bt, dim, L = x0["x"].shape
+    N = x0["B"].shape[1]
+    dy = torch.randn(x0["x"].shape, generator=torch.Generator(device="cuda").manual_seed(5),
+                     device="cuda").to(x0["x"].dtype)
+
+    def step(i):
+        g = ins[i % len(ins)]
+        ssm.ssd_bwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["dt_bias"], True, dy=dy,
+                    headdim=dim // g["A"].shape[0], need_dinitial_state=False)
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    el = Bt * dim * L
+    tops = el * algo_slots_bwd(N) / (ms * 1e-3) / 1e12
+    return {"steps": steps, "ms_per_step": ms, "value": el / (ms * 1e-3), "unit": "elements/s",
+            "alu": {"achieved": tops, "peak": PEAK_VALU_TOPS, "unit": "Tops/s", "frac": tops / PEAK_VALU_TOPS,
+                    "ops_per_element": algo_slots_bwd(N)},
+            "vs_ssd_forward": ms / fwd_ms}
 
 
 def bench_conv(torch, np, ssm, steps, K=4):

@@ -13,6 +13,7 @@
  *                           tutorial §6.
  *   selective_scan_bwd      gradients of the forward scan (training), states recomputed.
  *   ssd_scan_fwd            the Mamba-2 SSD form (scalar decay per head) on the matrix cores.
+ *   ssd_scan_bwd            its backward (every gradient for a given dy).
  *   selective_state_update  one autoregressive decode step: a single-step
  *                           recurrent update of a fixed-size per-request state,
  *                           updated in place (same wiblog.cn page, table of the
@@ -238,6 +239,35 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  int dtype, void* stream);
 
 /*
+ * Backward of ssd_scan_fwd: the gradients of a scalar loss through y, given dy = dLoss/dy
+ * (the Mamba-2 form's training half; mlqm.cn tutorial §8).  The SSD layer is the selective
+ * recurrence with one decay rate and one step size per head, broadcast to the head's channels,
+ * so its gradients are selective_scan_bwd's on the broadcast parameters with the broadcast
+ * parameters' gradients summed back per head (the chain rule):
+ *   ddt[b, h, t] = sum over the head's channels of ddelta;  dA[h] = sum over the head's
+ *   channels and all states of dA;  ddt_bias[h] = sum over the head's channels;
+ * dx, dz, dB, dC, dD and dinitial_state are the scan's own.  Computed by the backward scan's
+ * kernels on the broadcast step sizes, in fp32 state, with every sum in a fixed order (results
+ * reproducible bit for bit); not on the matrix cores.
+ *   x, z, dy, dx, dz : [batch, heads*headdim, seqlen] (dtype)
+ *   dt, ddt          : [batch, heads, seqlen] (dtype)
+ *   A, dA            : [heads] fp32;  dt_bias, ddt_bias : [heads] fp32, NULL = absent / not wanted
+ *   B, C, dB, dC     : [batch, dstate, seqlen] (dtype)
+ *   D, dD            : [heads*headdim] fp32, NULL = absent / not wanted
+ *   initial_state, dinitial_state : [batch, heads*headdim, dstate] fp32, NULL = zero / not wanted
+ * Supported: SSM_F32 or SSM_BF16, any headdim >= 1, dstate in {1, 2, 4, 8, 16, 32, 64}.
+ * Required: x, dt, A, B, C, dy, dx, ddt, dA, dB, dC (and dz when z is given); outputs must not
+ * overlap inputs or each other.  Scratch: batch x heads*headdim x seqlen elements of dtype (the
+ * broadcast step sizes) and as many fp32 (their gradients, summed per head in fp32), plus the
+ * backward scan's.  Errors as for selective_scan_bwd.
+ */
+int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* dt_bias, int softplus, const float* initial_state, const void* dy,
+                 void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
+                 float* dinitial_state, int64_t batch, int64_t heads, int64_t headdim, int64_t dstate,
+                 int64_t seqlen, int dtype, void* stream);
+
+/*
  * One decode step for `batch` independent requests, state updated IN PLACE.
  *
  *   state       : [batch, dim, dstate] fp32, read as h_{t-1} and overwritten with h_t
@@ -341,7 +371,7 @@ const char* ssm_last_error(void);
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

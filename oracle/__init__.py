@@ -281,3 +281,39 @@ def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, headdim: in
     a = torch.as_tensor(A, dtype=torch.float32).repeat_interleave(headdim)[:, None].expand(dim, dstate).contiguous()
     bias = None if dt_bias is None else torch.as_tensor(dt_bias, dtype=torch.float32).repeat_interleave(headdim)
     return scan(x, delta, a, B, C, D, z, bias, softplus, h0=h0, chans=chans, threads=threads)
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, headdim: int = 64, h0=None, dy=None,
+            threads: int = 0) -> dict:
+    """Gradients of sum(dy * y) for the SSD forward ``ssd``, fp64.
+
+    ``ssd`` is ``scan`` with the per-head decay and step size broadcast to the head's channels
+    (A[d, n] = A_heads[d // headdim] for every n, delta[b, d, t] = dt[b, d // headdim, t], dt_bias
+    likewise), so by the chain rule its gradients are those of ``scan_bwd`` on the broadcast
+    problem, with the broadcast parameters' gradients summed back over what they were broadcast to:
+    ddt[b, h, t] = sum over the head's channels of ddelta; dA[h] = sum over its channels and all
+    states of dA; ddt_bias[h] = sum over its channels.  Shapes as for ``ssd`` plus dy [B, H*P, L]
+    (dtype of x).  Returns float64 arrays: dx, dz [B, H*P, L] (dz None without z); ddt [B, H, L];
+    dA [H]; dB, dC [B, N, L]; dD [H*P] (None without D); ddt_bias [H] (None without dt_bias);
+    dh0 [B, H*P, N].  Pinned by tests/test_oracle_ssd_bwd.py against central differences of
+    ``ssd``."""
+    batch, dim, seqlen = (int(s) for s in x.shape)
+    heads = int(A.shape[0])
+    if heads * headdim != dim:
+        raise ValueError("x's channel count must be heads * headdim")
+    dstate = int(B.shape[1])
+    delta = torch.as_tensor(dt).repeat_interleave(headdim, dim=1).contiguous()
+    a = torch.as_tensor(A, dtype=torch.float32).repeat_interleave(headdim)[:, None].expand(dim, dstate).contiguous()
+    bias = None if dt_bias is None else torch.as_tensor(dt_bias, dtype=torch.float32).repeat_interleave(headdim)
+    g = scan_bwd(x, delta, a, B, C, D, z, bias, softplus, h0=h0, dy=dy, threads=threads)
+    return {
+        "dx": g["du"],
+        "ddt": g["ddelta"].reshape(batch, heads, headdim, seqlen).sum(axis=2),
+        "dz": g["dz"],
+        "dA": g["dA"].reshape(heads, headdim * dstate).sum(axis=1),
+        "dB": g["dB"],
+        "dC": g["dC"],
+        "dD": g["dD"],
+        "ddt_bias": None if g["ddt_bias"] is None else g["ddt_bias"].reshape(heads, headdim).sum(axis=1),
+        "dh0": g["dh0"],
+    }

@@ -17,9 +17,10 @@ import os
 
 import torch
 
-__all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
+__all__ = ["load", "lib_path", "scan_fwd", "scan_bwd", "ssd_fwd", "ssd_bwd", "state_update", "conv1d_fwd", "conv1d_update", "scan_plan", "SsmError",
            "STATUS", "scan_fwd_conv", "selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc",
-           "selective_scan_fwd_conv", "selective_scan_bwd", "ssd_scan_fwd", "selective_state_update", "causal_conv1d_fwd",
+           "selective_scan_fwd_conv", "selective_scan_bwd", "ssd_scan_fwd", "ssd_scan_bwd", "selective_state_update",
+           "causal_conv1d_fwd",
            "causal_conv1d_update", "last_error", "handover_failures", "set_handover_wait"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +33,7 @@ STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL_ARG", -2: "SSM_ERR_BAD_SHAPE", -3: "SSM
 F32, BF16 = 0, 1
 EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc", "selective_scan_fwd_conv",
            "selective_scan_bwd",
-           "ssd_scan_fwd",
+           "ssd_scan_fwd", "ssd_scan_bwd",
            "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
            "ssm_last_error", "ssm_abi_version")
@@ -69,6 +70,9 @@ def load():
                                            I64, I64, I, P]
         lib.selective_scan_bwd.restype = I
         lib.ssd_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I64, I64, I64, I64, I, P]
+        lib.ssd_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64,
+                                     I64, I64, I, P]
+        lib.ssd_scan_bwd.restype = I
         lib.ssd_scan_fwd.restype = I
         lib.selective_state_update.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I, P]
         lib.selective_state_update.restype = I
@@ -176,6 +180,10 @@ def selective_scan_bwd(*args) -> int:
 
 def ssd_scan_fwd(*args) -> int:
     return int(load().ssd_scan_fwd(*args))
+
+
+def ssd_scan_bwd(*args) -> int:
+    return int(load().ssd_scan_bwd(*args))
 
 
 def selective_state_update(*args) -> int:
@@ -341,6 +349,45 @@ def ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True,
                             1 if softplus else 0, _ptr(initial_state), _ptr(y), _ptr(last_state), batch, H,
                             headdim, N, L, _dtype_code(x), _stream(dev)))
     return y, last_state
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, dy=None, initial_state=None,
+            headdim: int = 64, need_dD: bool = True, need_ddt_bias: bool = True,
+            need_dinitial_state: bool = True) -> dict:
+    """Gradients of sum(dy * y) for the SSD scan with the same inputs.  Returns a dict: dx, dz
+    (None without z) [batch, H*P, L], ddt [batch, H, L] and dB, dC [batch, N, L] in the dtype of
+    x; dA, ddt_bias [H], dD [H*P] and dinitial_state [batch, H*P, N] in fp32 (None when not
+    requested)."""
+    lib = load()
+    if x.dim() != 3 or A.dim() != 1:
+        raise ValueError("x must be [batch, heads*headdim, seqlen] and A [heads]")
+    batch, dim, L = x.shape
+    H = A.shape[0]
+    if H * headdim != dim:
+        raise ValueError(f"x has {dim} channels, not heads*headdim = {H}*{headdim}")
+    N = B.shape[1]
+    dev, dtp = x.device, x.dtype
+    if dy is None:
+        raise ValueError("dy is required")
+    for t, name, shape in ((x, "x", (batch, dim, L)), (dt, "dt", (batch, H, L)), (z, "z", (batch, dim, L)),
+                           (dy, "dy", (batch, dim, L)), (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+        _require(t, name, shape, dtp, dev)
+    _require(A, "A", (H,), torch.float32, dev)
+    _require(D, "D", (dim,), torch.float32, dev)
+    _require(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _require(initial_state, "initial_state", (batch, dim, N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dz": torch.empty_like(x) if z is not None else None,
+         "dA": torch.empty((H,), **f32), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+         "dD": torch.empty((dim,), **f32) if need_dD else None,
+         "ddt_bias": torch.empty((H,), **f32) if need_ddt_bias else None,
+         "dinitial_state": torch.empty((batch, dim, N), **f32) if need_dinitial_state else None}
+    _check(lib.ssd_scan_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                            1 if softplus else 0, _ptr(initial_state), _ptr(dy), _ptr(g["dx"]), _ptr(g["ddt"]),
+                            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                            _ptr(g["ddt_bias"]), _ptr(g["dinitial_state"]), batch, H, headdim, N, L,
+                            _dtype_code(x), _stream(dev)))
+    return g
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, dt_bias=None, y=None):

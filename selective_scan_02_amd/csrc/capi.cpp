@@ -425,6 +425,79 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
   return hip_status(ssm::launch_ssd_fwd(p, (hipStream_t)stream), "ssd_scan_fwd launch");
 }
 
+int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* dt_bias, int softplus, const float* initial_state, const void* dy,
+                 void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
+                 float* dinitial_state, int64_t batch, int64_t heads, int64_t headdim, int64_t dstate,
+                 int64_t seqlen, int dtype, void* stream) {
+  g_last_error.clear();
+  if (seqlen != 0) {
+    if (!x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+    if (!dt) return fail(SSM_ERR_NULL_ARG, "dt is NULL");
+    if (!B) return fail(SSM_ERR_NULL_ARG, "B is NULL");
+    if (!C) return fail(SSM_ERR_NULL_ARG, "C is NULL");
+    if (!dy) return fail(SSM_ERR_NULL_ARG, "dy is NULL");
+    if (!dx) return fail(SSM_ERR_NULL_ARG, "dx is NULL");
+    if (!ddt) return fail(SSM_ERR_NULL_ARG, "ddt is NULL");
+    if (!dB) return fail(SSM_ERR_NULL_ARG, "dB is NULL");
+    if (!dC) return fail(SSM_ERR_NULL_ARG, "dC is NULL");
+    if (z && !dz) return fail(SSM_ERR_NULL_ARG, "dz is NULL while z is given");
+  }
+  if (!A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+  if (!dA) return fail(SSM_ERR_NULL_ARG, "dA is NULL");
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32/SSM_BF16", dtype);
+  if (batch < 1 || heads < 1 || headdim < 1 || dstate < 1 || seqlen < 0)
+    return fail(SSM_ERR_BAD_SHAPE, "bad sizes batch=%lld heads=%lld headdim=%lld dstate=%lld seqlen=%lld",
+                (long long)batch, (long long)heads, (long long)headdim, (long long)dstate, (long long)seqlen);
+  const int64_t dim = heads * headdim;
+  if (heads > (1LL << 40) / headdim || too_big(batch, dim, seqlen) || too_big(batch, dstate, seqlen) ||
+      too_big(batch, dim, dstate) || batch * ((dim + 63) / 64) > 0x7fffffffLL)
+    return fail(SSM_ERR_BAD_SHAPE, "sizes too large");
+  if (!ssm::dstate_supported(dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16,32,64}", (long long)dstate);
+  if (softplus != 0 && softplus != 1) return fail(SSM_ERR_BAD_SHAPE, "softplus must be 0 or 1");
+  if (!z) dz = nullptr;  // not written without a gate
+  const uint64_t es = dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * dim * seqlen, nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t ndt = (uint64_t)batch * heads * seqlen, nst = (uint64_t)batch * dim * dstate * 4;
+  const Range ins[] = {{"x", x, nx * es, es},
+                       {"dt", dt, ndt * es, es},
+                       {"z", z, nx * es, es},
+                       {"dy", dy, nx * es, es},
+                       {"B", B, nbc * es, es},
+                       {"C", C, nbc * es, es},
+                       {"A", A, (uint64_t)heads * 4, 4},
+                       {"D", D, (uint64_t)dim * 4, 4},
+                       {"dt_bias", dt_bias, (uint64_t)heads * 4, 4},
+                       {"initial_state", initial_state, nst, 4}};
+  const Range outs[] = {{"dx", dx, nx * es, es},
+                        {"ddt", ddt, ndt * es, es},
+                        {"dz", dz, nx * es, es},
+                        {"dB", dB, nbc * es, es},
+                        {"dC", dC, nbc * es, es},
+                        {"dA", dA, (uint64_t)heads * 4, 4},
+                        {"dD", dD, (uint64_t)dim * 4, 4},
+                        {"ddt_bias", ddt_bias, (uint64_t)heads * 4, 4},
+                        {"dinitial_state", dinitial_state, nst, 4}};
+  for (const Range& r : ins)
+    if (int rc = check_aligned(r)) return rc;
+  for (const Range& r : outs)
+    if (int rc = check_aligned(r)) return rc;
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, r.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  ssm::SsdBwdParams p{};
+  p.f.x = x; p.f.dt = dt; p.f.A = A; p.f.B = B; p.f.C = C; p.f.D = D; p.f.z = z; p.f.dt_bias = dt_bias;
+  p.f.softplus = softplus; p.f.h0 = initial_state;
+  p.f.batch = batch; p.f.heads = heads; p.f.headdim = headdim; p.f.dstate = dstate; p.f.seqlen = seqlen;
+  p.dtype = dtype; p.dy = dy; p.dx = dx; p.ddt = ddt; p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.dz = dz;
+  p.ddt_bias = ddt_bias; p.dh0 = dinitial_state;
+  return hip_status(ssm::launch_ssd_bwd(p, (hipStream_t)stream), "ssd_scan_bwd launch");
+}
+
 int selective_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
                            const void* C, const float* D, const void* z, const float* dt_bias, void* y,
                            int64_t batch, int64_t dim, int64_t dstate, int dtype, void* stream) {

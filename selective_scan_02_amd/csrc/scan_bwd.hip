@@ -83,6 +83,7 @@ struct BwdArgs {
   float* pbias;   // [S, chans]
   int64_t batch, dim, seqlen, seg_len, chans;
   int groups, nseg, softplus;
+  int ddelta_f32;  // ddelta is written in fp32 whatever the input dtype (for callers that sum it)
   // main pass on the interval plan (iunits > 0)
   int* ticket;    // 1 counter
   int* flags;     // [chains, scanner waves] hand-over flags
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(kWave) void bwd_main_kernel(BwdArgs a) {
   const T* __restrict__ Cp = (const T*)a.C + l.b * N * L;
   T* __restrict__ du_o = (T*)a.du + l.ch * L;
   T* __restrict__ dl_o = (T*)a.ddelta + l.ch * L;
+  float* __restrict__ dl_of = (float*)a.ddelta + l.ch * L;  // the same row when ddelta is fp32
   T* __restrict__ dz_o = a.z ? (T*)a.dz + l.ch * L : nullptr;
   // this lane's slot in the reduced sums: value n_red, stored by the group's first lane
   const int n_red = l.lane / P;
@@ -389,7 +391,10 @@ __global__ __launch_bounds__(kWave) void bwd_main_kernel(BwdArgs a) {
         const float ddl = dDelta * sgx[i];
         if (l.active) {
           st(du_o, t, __builtin_fmaf(dt, accB, ds * Dd));
-          st(dl_o, t, ddl);
+          if (a.ddelta_f32)
+            dl_of[t] = ddl;
+          else
+            st(dl_o, t, ddl);
         }
         accD = __builtin_fmaf(ds, ut, accD);
         accbias += ddl;
@@ -1059,7 +1064,10 @@ __global__ __launch_bounds__(kWave * (N / kSPW), SSM_BWD_WAVES_PER_SIMD) void fb
       }
       if (active) {
         Row8<T>::store((T*)a.du + ch * L + tc, o_du);
-        Row8<T>::store((T*)a.ddelta + ch * L + tc, o_dl);
+        if (a.ddelta_f32)
+          Row8<float>::store((float*)a.ddelta + ch * L + tc, o_dl);
+        else
+          Row8<T>::store((T*)a.ddelta + ch * L + tc, o_dl);
       }
     }
   }
@@ -1127,7 +1135,7 @@ struct RolesSmem {
   float prep[2][kRItems][kCT][kWave];         // chunk c in slot c % 2
   float part[2][3][S][kCT][kWave];            // readout, sum lam B, sum q A per scanner
   float bcs[S][2][kCT][N / S];                // each scanner's B and C rows of its chunk, [t][n]
-  T out[2][3][kWave][kCT];                    // dz, du, ddelta of a chunk
+  float out[2][3][kWave][kCT];                // dz, du, ddelta of a chunk
   float dbc[2][2][N][kCT];                    // dB and dC partials of a chunk (this channel group)
   int ticket;                                 // interval plan: this workgroup's interval
 };
@@ -1573,7 +1581,10 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
       float v[kCT];
 #pragma unroll
       for (int i = 0; i < kCT; i += 2) lds_pair(&sm.out[k & 1][q][lane][i], v[i], v[i + 1]);
-      Row8<T>::store(outs[q] + ch * L + chunk_t(k), v);
+      if (q == 2 && a.ddelta_f32)
+        Row8<float>::store((float*)a.ddelta + ch * L + chunk_t(k), v);
+      else
+        Row8<T>::store(outs[q] + ch * L + chunk_t(k), v);
     }
   };
 
@@ -1713,6 +1724,7 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   BwdArgs a{};
   a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
   a.h0 = p.h0; a.dy = p.dy; a.du = p.du; a.ddelta = p.ddelta; a.dz = p.dz; a.dh0 = p.dh0;
+  a.ddelta_f32 = p.ddelta_f32 ? 1 : 0;
   a.batch = p.batch; a.dim = p.dim; a.seqlen = p.seqlen; a.softplus = p.softplus;
   a.chans = p.batch * p.dim;
   a.groups = (int)((p.dim + kWave - 1) / kWave);

@@ -95,6 +95,7 @@ struct BwdParams {
   void* dz;              // written when z is given
   float* ddt_bias;       // nullable
   float* dh0;            // nullable
+  bool ddelta_f32 = false;  // ddelta in fp32 whatever dtype is (its row stride is still seqlen)
   int64_t batch, dim, dstate, seqlen;
   int dtype;
 };
@@ -174,6 +175,25 @@ hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fas
 hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);
 hipError_t launch_ssd_fwd(const SsdParams& p, hipStream_t stream);
+
+// Backward of the SSD form: gradients of sum(dy * y).  Shapes as SsdParams; outputs dx, dz like
+// x, ddt like dt (dtype of x), dA [heads], ddt_bias [heads], dD [heads*headdim], dB, dC like B,
+// dh0 like h0.  bf16 or fp32 (dtype), any headdim >= 1 and the backward scan's dstates.
+struct SsdBwdParams {
+  SsdParams f;  // forward inputs (f.y, f.last_state unused)
+  int dtype;    // kF32 or kBF16
+  const void* dy;
+  void* dx;
+  void* ddt;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;        // nullable
+  void* dz;         // written when z is given
+  float* ddt_bias;  // nullable
+  float* dh0;       // nullable
+};
+hipError_t launch_ssd_bwd(const SsdBwdParams& p, hipStream_t stream);
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvParams& p, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvStepParams& p, hipStream_t stream);

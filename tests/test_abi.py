@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fwd_noalloc",
                  "selective_scan_fwd_conv",
-                 "selective_scan_bwd", "ssd_scan_fwd",
+                 "selective_scan_bwd", "ssd_scan_fwd", "ssd_scan_bwd",
                  "selective_state_update",
                  "causal_conv1d_fwd",
                  "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 8
+    assert lib.ssm_abi_version() == 9
 
 
 def scan_args(**over):
@@ -303,6 +303,43 @@ def test_ssd_validation(lib):
     assert lib.ssd_scan_fwd(*ssd_args(x=addr(1) + 8)) == MISALIGNED     # 16-byte rows
     assert lib.ssd_scan_fwd(*ssd_args(y=addr(1) + 64)) == ALIAS
     assert lib.ssd_scan_fwd(*ssd_args(last=addr(9) + 64)) == ALIAS
+
+
+SSD_BWD_FIELDS = ("x", "dt", "A", "B", "C", "D", "z", "dt_bias", "softplus", "h0", "dy", "dx", "ddt", "dA", "dB",
+                  "dC", "dD", "dz", "ddt_bias", "dh0", "batch", "heads", "headdim", "dstate", "seqlen", "dtype",
+                  "stream")
+
+
+def ssd_bwd_args(**over):
+    a = dict(zip(SSD_BWD_FIELDS[:8], [addr(i) for i in range(1, 9)]))
+    a.update(softplus=1, h0=addr(9), dy=addr(10), dx=addr(11), ddt=addr(12), dA=addr(13), dB=addr(14),
+             dC=addr(15), dD=addr(16), dz=addr(17), ddt_bias=addr(18), dh0=addr(19), batch=2, heads=4, headdim=64,
+             dstate=16, seqlen=128, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in SSD_BWD_FIELDS]
+
+
+@pytest.mark.parametrize("field", ["x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC", "dz"])
+def test_ssd_bwd_null_required(lib, field):
+    assert lib.ssd_scan_bwd(*ssd_bwd_args(**{field: None})) == NULL_ARG
+    assert field in ssm.last_error()
+
+
+def test_ssd_bwd_validation(lib):
+    f = lib.ssd_scan_bwd
+    assert f(*ssd_bwd_args(dtype=3)) == BAD_DTYPE
+    assert f(*ssd_bwd_args(dstate=12)) == UNSUPPORTED
+    assert f(*ssd_bwd_args(batch=0)) == BAD_SHAPE
+    assert f(*ssd_bwd_args(headdim=0)) == BAD_SHAPE
+    assert f(*ssd_bwd_args(softplus=2)) == BAD_SHAPE
+    assert f(*ssd_bwd_args(dy=addr(10) + 1)) == MISALIGNED
+    assert f(*ssd_bwd_args(dA=addr(13) + 2)) == MISALIGNED
+    assert f(*ssd_bwd_args(dx=addr(10) + 64)) == ALIAS          # dx inside dy
+    assert f(*ssd_bwd_args(ddt=addr(2) + 64)) == ALIAS          # ddt inside dt
+    assert f(*ssd_bwd_args(dh0=addr(9))) == ALIAS
+    assert "overlaps" in ssm.last_error()
+    # an empty sequence still needs A and dA; the sequence tensors may be absent
+    assert f(*ssd_bwd_args(seqlen=0, dA=None)) == NULL_ARG
 
 
 def test_size_limits(lib):
