@@ -1215,46 +1215,52 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
     ihead = ie < (cl + 1) * tchn;
     npieces = (int)(cl - cf + 1);
   }
-  for (int pc = 0; pc < npieces; ++pc) {
-  int64_t cid, k0, k1;  // chain, and its chunks [k0, k1) in processing order (chunk 0: the last 8 steps)
-  int slot;             // where the piece's sums over time go (pA, pD, pbias)
-  if (a.iunits > 0) {
-    if (ihead && pc == 0) {
-      cid = cl;
-    } else {
-      const int q = pc - (ihead ? 1 : 0);
-      const int nfull = npieces - (ihead ? 1 : 0) - (itail ? 1 : 0);
-      cid = q < nfull ? cf + (itail ? 1 : 0) + q : cf;
-    }
-    const int64_t p0 = cid * tchn > is ? cid * tchn : is;
-    const int64_t p1 = (cid + 1) * tchn < ie ? (cid + 1) * tchn : ie;
-    k0 = p0 - cid * tchn;
-    k1 = p1 - cid * tchn;
-    slot = k0 > 0 ? 1 : 0;
-  } else {
-    cid = blockIdx.x;
-    slot = blockIdx.y;
-    const int64_t s0 = (int64_t)blockIdx.y * a.seg_len;
-    const int64_t s1 = s0 + a.seg_len < L ? s0 + a.seg_len : L;
-    k0 = (L - s1) / kCT;
-    k1 = (L - s0) / kCT;
-  }
-  const bool wait_in = a.iunits > 0 && k0 > 0;      // the adjoint comes from another workgroup
-  const bool hand_out = a.iunits > 0 && k1 < tchn;  // and goes to another one
-  const bool whole = a.iunits > 0 && k0 == 0 && k1 == tchn;  // slot 1 of the chain stays zero
-  const int64_t b = cid / a.groups;
-  const int64_t grp = cid % a.groups;
-  const int64_t d = grp * kWave + lane;
-  const bool active = d < a.dim;
-  const int64_t dd = active ? d : a.dim - 1;
-  const int64_t ch = b * a.dim + dd;
-  const int64_t t0 = L - kCT * k1;
-  const int64_t t1 = L - kCT * k0;
-  const int nch = (int)(k1 - k0);  // chunk k of the piece covers steps [t1 - 8(k+1), t1 - 8k)
-  auto chunk_t = [&](int k) { return t1 - (int64_t)kCT * (k + 1); };
+  // One piece: its chain cid, its chunks [k0, k1) in processing order (chunk 0: the last 8 steps;
+  // chunk k of the piece covers steps [t1 - 8(k+1), t1 - 8k)) and the slot its sums over time go to
+  // (pA, pD, pbias).  wait_in: the adjoint comes from another workgroup; hand_out: and goes to
+  // another one; whole: the chain's slot 1 stays zero.  Each role runs its own loop over the
+  // pieces, so that the compiler keeps the two roles' registers apart.
+#define SSM_BWD_PIECE \
+  int64_t cid, k0, k1; \
+  int slot; \
+  if (a.iunits > 0) { \
+    if (ihead && pc == 0) { \
+      cid = cl; \
+    } else { \
+      const int q = pc - (ihead ? 1 : 0); \
+      const int nfull = npieces - (ihead ? 1 : 0) - (itail ? 1 : 0); \
+      cid = q < nfull ? cf + (itail ? 1 : 0) + q : cf; \
+    } \
+    const int64_t p0 = cid * tchn > is ? cid * tchn : is; \
+    const int64_t p1 = (cid + 1) * tchn < ie ? (cid + 1) * tchn : ie; \
+    k0 = p0 - cid * tchn; \
+    k1 = p1 - cid * tchn; \
+    slot = k0 > 0 ? 1 : 0; \
+  } else { \
+    cid = blockIdx.x; \
+    slot = blockIdx.y; \
+    const int64_t s0 = (int64_t)blockIdx.y * a.seg_len; \
+    const int64_t s1 = s0 + a.seg_len < L ? s0 + a.seg_len : L; \
+    k0 = (L - s1) / kCT; \
+    k1 = (L - s0) / kCT; \
+  } \
+  const bool wait_in = a.iunits > 0 && k0 > 0; \
+  const bool hand_out = a.iunits > 0 && k1 < tchn; \
+  const bool whole = a.iunits > 0 && k0 == 0 && k1 == tchn; \
+  const int64_t b = cid / a.groups; \
+  const int64_t grp = cid % a.groups; \
+  const int64_t d = grp * kWave + lane; \
+  const bool active = d < a.dim; \
+  const int64_t dd = active ? d : a.dim - 1; \
+  const int64_t ch = b * a.dim + dd; \
+  const int64_t t0 = L - kCT * k1; \
+  const int64_t t1 = L - kCT * k0; \
+  const int nch = (int)(k1 - k0); \
+  auto chunk_t = [&](int k) { return t1 - (int64_t)kCT * (k + 1); }; \
   auto tile_of = [&](int k) { return (int)((chunk_t(k) - t0) / RT::kSteps); };
-
   if (wv < kRS) {
+  for (int pc = 0; pc < npieces; ++pc) {
+  SSM_BWD_PIECE
     // ------------------------------------------------------------------ scanner
     const int n0 = wv * NPW;
     float A2[NPW], lam[NPW], dA[NPW];
@@ -1463,7 +1469,10 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
         for (int j = 0; j < NPW; ++j) a.dh0[ch * N + n0 + j] = lam[j];
       }
     }
+  }  // pieces (scanner)
   } else {
+  for (int pc = 0; pc < npieces; ++pc) {
+  SSM_BWD_PIECE
 
   // -------------------------------------------------------------------- helper
   const int hw = wv - kRS;       // this thread's steps of a chunk: 2 hw and 2 hw + 1
@@ -1670,8 +1679,9 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
       a.pbias[(int64_t)(slot + 1) * a.chans + ch] = 0.0f;
     }
   }
-  }  // helper
-  }  // pieces
+  }  // pieces (helper)
+  }
+#undef SSM_BWD_PIECE
 }
 
 hipError_t zero(float* p, int64_t n, hipStream_t s) {
