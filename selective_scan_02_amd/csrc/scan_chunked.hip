@@ -101,8 +101,9 @@ namespace chunked {
 #ifndef SSM_HELPERS
 // helper waves of the output kernels: 8 (two per SIMD next to its scanner) measured 5% faster
 // than 4 on the 2.8B-shaped layer (0.229-0.232 against 0.241-0.246 ms, same box) and about 2%
-// on the 2^20-step sequence; the kernels with the fused convolution keep 4 (with 8 their helper
-// registers spill)
+// on the 2^20-step sequence; the kernels with the fused convolution keep 4: with 8 (each helper
+// then owns 2 steps, its window reaching into the previous chunk) the fused call measured 261-262
+// against 247-248 us, their registers at the 168 cap spilling 96 bytes
 #define SSM_HELPERS 8
 #endif
 
@@ -488,13 +489,16 @@ void scan_chunked_kernel(const Args a) {
       /* thread's first step from the same row, the previous chunk's row, or the unit's halo   */ \
       float xw[kTPH + 3];                                                                         \
       _Pragma("unroll") for (int i = 0; i < kTPH; ++i) xw[3 + i] = uv[i];                        \
-      if (hw > 0) {                                                                               \
-        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = lds_elem<TI>(ru, hw * kTPH - 3 + m); \
-      } else if ((J) == 0) {                                                                      \
-        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = sm.xh[lane][m];                     \
-      } else {                                                                                    \
-        const unsigned char* rp = &sm.tile[((J) - 1) & 3][0][lane * ROWB];                        \
-        _Pragma("unroll") for (int m = 0; m < 3; ++m) xw[m] = lds_elem<TI>(rp, kT - 3 + m);     \
+      /* the 3 inputs before this thread's first step: this chunk's row where they lie in it,  \
+         else the previous chunk's row, or before the unit's first chunk the saved inputs */    \
+      _Pragma("unroll") for (int m = 0; m < 3; ++m) {                                             \
+        const int ix = hw * kTPH - 3 + m;                                                         \
+        if (ix >= 0)                                                                              \
+          xw[m] = lds_elem<TI>(ru, ix);                                                           \
+        else if ((J) == 0)                                                                        \
+          xw[m] = sm.xh[lane][3 + ix];                                                            \
+        else                                                                                      \
+          xw[m] = lds_elem<TI>(&sm.tile[((J) - 1) & 3][0][lane * ROWB], kT + ix);                \
       }                                                                                           \
       _Pragma("unroll") for (int i = 0; i < kTPH; ++i) {                                          \
         float v = cbias;                                                                          \
