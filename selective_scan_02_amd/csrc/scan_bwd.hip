@@ -1128,6 +1128,14 @@ struct RTile {
 template <typename T, int N>
 using RTileOf = RTile<T, roles_scanners<T, N>() == 4 ? 4 : 2>;
 
+// Output rings of the main pass: chunk c of a row in slot c % kRing(slot bytes).  A ring holds the
+// chunks of one 128-byte line still to be stored plus the one being finished.
+constexpr int kOutRingBytes = 160;
+constexpr int kBcRing = 5;
+template <int SB>
+constexpr int out_ring() { return SB == 16 ? 9 : 5; }
+static_assert(9 * 16 <= kOutRingBytes && 5 * 32 <= kOutRingBytes, "ring slots fit a row");
+
 template <int N, typename T>
 struct RolesSmem {
   static constexpr int S = roles_scanners<T, N>();
@@ -1135,8 +1143,11 @@ struct RolesSmem {
   float prep[2][kRItems][kCT][kWave];         // chunk c in slot c % 2
   float part[2][3][S][kCT][kWave];            // readout, sum lam B, sum q A per scanner
   float bcs[S][2][kCT][N / S];                // each scanner's B and C rows of its chunk, [t][n]
-  float out[2][3][kWave][kCT];                // dz, du, ddelta of a chunk
-  float dbc[2][2][N][kCT];                    // dB and dC partials of a chunk (this channel group)
+  // dz, du, ddelta rows of the chunks finished and not yet stored, in a ring of chunk slots per
+  // row (9 slots of 16 bytes, or 5 of 32 for fp32 rows), so that a row's 128-byte line is stored
+  // in one burst once its last chunk is done
+  unsigned char ring[3][kWave][kOutRingBytes];
+  float dbc[kBcRing][2][N][kCT];              // dB and dC partials of chunk c (this channel group) in slot c % 5
   int ticket;                                 // interval plan: this workgroup's interval
 };
 
@@ -1409,7 +1420,7 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
             if (rsel == i / SPG) keepC = r;
           }
         }
-        if (rkeep) sm.dbc[sl][1][n0 + rj][ri] = keepC;
+        if (rkeep) sm.dbc[k % kBcRing][1][n0 + rj][ri] = keepC;
         // adjoint back over the chunk
         float keepB = 0.0f;
 #pragma unroll
@@ -1436,7 +1447,7 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
             if (rsel == i / SPG) keepB = r;
           }
         }
-        if (rkeep) sm.dbc[sl][0][n0 + rj][ri] = keepB;
+        if (rkeep) sm.dbc[k % kBcRing][0][n0 + rj][ri] = keepB;
       }
       __syncthreads();
     }
@@ -1575,40 +1586,78 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
       o[2][e] = __builtin_fmaf(sq, kLn2, uu * sb) * sg;
       accbias += o[2][e];
     }
+    constexpr int RT_ = out_ring<kCT * sizeof(T)>();
 #pragma unroll
-    for (int q = 0; q < 3; ++q) lds_put_pair(&sm.out[sl][q][lane][2 * hw], o[q][0], o[q][1]);
+    for (int q = 0; q < 2; ++q)
+      lds_put_pair((T*)&sm.ring[q][lane][(k % RT_) * kCT * sizeof(T)] + 2 * hw, o[q][0], o[q][1]);
+    if (a.ddelta_f32)
+      lds_put_pair((float*)&sm.ring[2][lane][(k % 5) * kCT * 4] + 2 * hw, o[2][0], o[2][1]);
+    else
+      lds_put_pair((T*)&sm.ring[2][lane][(k % RT_) * kCT * sizeof(T)] + 2 * hw, o[2][0], o[2][1]);
   };
   T* const outs[3] = {(T*)a.dz, (T*)a.du, (T*)a.ddelta};
   // all global stores come from the last helper wave (dz, du, ddelta rows here, the dB and dC
   // partials below): reusing a register a store reads waits for the store to complete, and only
   // this wave should pay for that
-  auto store = [&](int k) {
+  //
+  // A row's chunks wait in its ring until the chunk that starts a 128-byte line (in address) is
+  // done, or the piece's last chunk, and are then stored together: the line is written whole
+  // within one iteration instead of a piece per chunk over eight.  A ring never holds more than
+  // its size less one (the slot being finished), which the pending count also enforces.
+  int pend[3] = {0, 0, 0};
+  auto flush_row = [&](auto sbc, const unsigned char* ring_row, char* g, int c, int& np) {
+    constexpr int SB = decltype(sbc)::value, R = out_ring<SB>();
+    ++np;
+    if (((uintptr_t)g & 127) >= (uintptr_t)SB && c != nch - 1 && np < R - 1) return;
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) {
+      if (j < np) {
+        const int slot = (c - j) % R;
+#pragma unroll
+        for (int h = 0; h < SB / 16; ++h)
+          *(uint4*)(g + j * SB + 16 * h) = *(const uint4*)(ring_row + slot * SB + 16 * h);
+      }
+    }
+    np = 0;
+  };
+  auto store = [&](int c) {
     if (hw != kRH - 1 || !active) return;
+    constexpr int SBT = kCT * (int)sizeof(T);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       if (q == 0 && !gated) continue;
-      float v[kCT];
-#pragma unroll
-      for (int i = 0; i < kCT; i += 2) lds_pair(&sm.out[k & 1][q][lane][i], v[i], v[i + 1]);
       if (q == 2 && a.ddelta_f32)
-        Row8<float>::store((float*)a.ddelta + ch * L + chunk_t(k), v);
+        flush_row(std::integral_constant<int, kCT * 4>{}, sm.ring[2][lane],
+                  (char*)((float*)a.ddelta + ch * L + chunk_t(c)), c, pend[2]);
       else
-        Row8<T>::store(outs[q] + ch * L + chunk_t(k), v);
+        flush_row(std::integral_constant<int, SBT>{}, sm.ring[q][lane], (char*)(outs[q] + ch * L + chunk_t(c)), c,
+                  pend[q]);
     }
   };
 
-  // the dB and dC partials of chunk k (from LDS, 4 steps per 16-byte piece) by helper wave 3
-  auto store_bc = [&](int k) {
+  // the dB and dC partials of chunk c (4 steps per 16-byte piece) by helper wave 3, from the
+  // scanners' ring in LDS, stored the same way: a row's chunks together once a line is complete
+  constexpr int kBcPer = (4 * N + kWave - 1) / kWave;
+  int pendbc[kBcPer];
+#pragma unroll
+  for (int i = 0; i < kBcPer; ++i) pendbc[i] = 0;
+  auto store_bc = [&](int c) {
     if (hw != kRH - 1) return;
-    const int64_t tc = chunk_t(k);
+    const int64_t tc = chunk_t(c);
 #pragma unroll
     for (int p0 = 0; p0 < 4 * N; p0 += kWave) {
       const int q = p0 + lane;
       if (q < 4 * N) {
         const int w = q / (2 * N), n = (q / 2) % N, hf = q % 2;
-        const float4 v = *(const float4*)&sm.dbc[k & 1][w][n][4 * hf];
-        float* dst = (w == 0 ? a.pB : a.pC) + ((grp * a.batch + b) * N + n) * L + tc + 4 * hf;
-        *(float4*)dst = v;
+        float* row = (w == 0 ? a.pB : a.pC) + ((grp * a.batch + b) * N + n) * L + tc;
+        int& np = pendbc[p0 / kWave];
+        ++np;
+        if (((uintptr_t)row & 127) < 32 || c == nch - 1 || np == kBcRing - 1) {
+#pragma unroll
+          for (int j = 0; j < kBcRing - 1; ++j)
+            if (j < np) *(float4*)(row + kCT * j + 4 * hf) = *(const float4*)&sm.dbc[(c - j) % kBcRing][w][n][4 * hf];
+          np = 0;
+        }
       }
     }
   };

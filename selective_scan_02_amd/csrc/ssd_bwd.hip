@@ -53,33 +53,58 @@ __global__ __launch_bounds__(256) void ssd_bcast_param_kernel(const float* A, co
   if (bias_full && i % N == 0) bias_full[d] = dt_bias[d / P];
 }
 
-// ddt[b, h, t] = sum_{p < P} ddelta[b, h*P + p, t], in fp32, p ascending (ddelta is fp32).
-template <typename T>
+// ddt[b, h, t] = sum_{p < P} ddelta[b, h*P + p, t], in fp32, p ascending (ddelta is fp32).  A thread
+// takes E consecutive steps (16-byte loads when rows allow), and the p loop is unrolled so that
+// several rows' loads are in flight at once; each step's sum keeps the same order either way.
+template <typename T, int E>
 __global__ __launch_bounds__(256) void ssd_sum_dt_kernel(const float* __restrict__ ddelta, T* __restrict__ ddt,
                                                          int64_t batch, int64_t heads, int64_t P, int64_t L) {
+  const int64_t per_row = L / E;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= batch * heads * L) return;
-  const int64_t t = i % L, bh = i / L;
+  if (i >= batch * heads * per_row) return;
+  const int64_t bh = i / per_row, t = (i - bh * per_row) * E;
   const float* src = ddelta + bh * P * L + t;  // rows b*dim + h*P + p = (b*heads + h)*P + p
-  float s = 0.0f;
-  for (int64_t p = 0; p < P; ++p) s += src[p * L];
-  ddt[i] = (T)s;
+  float s[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) s[e] = 0.0f;
+#pragma unroll 8
+  for (int64_t p = 0; p < P; ++p) {
+    if constexpr (E == 4) {
+      const float4 v = *(const float4*)(src + p * L);
+      s[0] += v.x; s[1] += v.y; s[2] += v.z; s[3] += v.w;
+    } else {
+      s[0] += src[p * L];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) ddt[bh * L + t + e] = (T)s[e];
 }
 
-// dA[h] = sum_{p, n} dA_full[h*P + p, n]; ddt_bias[h] = sum_p dbias_full[h*P + p]: one thread per
-// head, fixed order.
+// dA[h] = sum_{p, n} dA_full[h*P + p, n]; ddt_bias[h] = sum_p dbias_full[h*P + p].  One workgroup per
+// head: thread j sums terms j, j + 256, ... in order, then a fixed pairwise tree in LDS (results
+// reproducible bit for bit).
 __global__ __launch_bounds__(256) void ssd_sum_param_kernel(const float* dA_full, const float* dbias_full,
-                                                            float* dA, float* ddt_bias, int64_t heads, int64_t P,
-                                                            int64_t N) {
-  const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= heads) return;
-  float s = 0.0f;
-  for (int64_t k = 0; k < P * N; ++k) s += dA_full[h * P * N + k];
-  dA[h] = s;
-  if (ddt_bias) {
-    float sb = 0.0f;
-    for (int64_t p = 0; p < P; ++p) sb += dbias_full[h * P + p];
-    ddt_bias[h] = sb;
+                                                            float* dA, float* ddt_bias, int64_t P, int64_t N) {
+  __shared__ float red[2][256];
+  const int64_t h = blockIdx.x;
+  const int j = threadIdx.x;
+  float s = 0.0f, sb = 0.0f;
+  for (int64_t k = j; k < P * N; k += 256) s += dA_full[h * P * N + k];
+  if (dbias_full)
+    for (int64_t p = j; p < P; p += 256) sb += dbias_full[h * P + p];
+  red[0][j] = s;
+  red[1][j] = sb;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (j < w) {
+      red[0][j] += red[0][j + w];
+      red[1][j] += red[1][j + w];
+    }
+    __syncthreads();
+  }
+  if (j == 0) {
+    dA[h] = red[0][0];
+    if (ddt_bias) ddt_bias[h] = red[1][0];
   }
 }
 
@@ -135,13 +160,17 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
     err = launch_scan_bwd(b, stream);
   }
   if (err == hipSuccess && L > 0) {
-    hipLaunchKernelGGL((ssd_sum_dt_kernel<T>), dim3(blocks_for(f.batch * H * L)), dim3(256), 0, stream, ddelta,
-                       (T*)q.ddt, f.batch, H, P, L);
+    if (L % 4 == 0)
+      hipLaunchKernelGGL((ssd_sum_dt_kernel<T, 4>), dim3(blocks_for(f.batch * H * (L / 4))), dim3(256), 0, stream,
+                         ddelta, (T*)q.ddt, f.batch, H, P, L);
+    else
+      hipLaunchKernelGGL((ssd_sum_dt_kernel<T, 1>), dim3(blocks_for(f.batch * H * L)), dim3(256), 0, stream,
+                         ddelta, (T*)q.ddt, f.batch, H, P, L);
     err = hipGetLastError();
   }
-  if (err == hipSuccess) {
-    hipLaunchKernelGGL(ssd_sum_param_kernel, dim3(blocks_for(H)), dim3(256), 0, stream, dA_full,
-                       q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, H, P, N);
+  if (err == hipSuccess && H > 0) {
+    hipLaunchKernelGGL(ssd_sum_param_kernel, dim3((unsigned)H), dim3(256), 0, stream, dA_full,
+                       q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, P, N);
     err = hipGetLastError();
   }
   const hipError_t ferr = hipFreeAsync(scratch, stream);
