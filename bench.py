@@ -61,7 +61,7 @@ def algo_slots(N: int, gate: bool = True, skip: bool = True, softplus: bool = Tr
 # the same counters' reading for plain copies of known size (FETCH_SIZE x2, WRITE_SIZE x1); null until
 # measured for the current kernel.  2: the 2.8B-shaped layer's one scan kernel; 3: the 2^20-step
 # sequence's three kernels together (aggregate pass, segment carry, output pass).
-TRAFFIC = {2: 357.2e6, 3: 9055.4e6}
+TRAFFIC = {2: 359.8e6, 3: 9055.4e6}
 
 
 def algo_slots_bwd(N: int) -> int:
