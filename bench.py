@@ -25,6 +25,7 @@ under "decode" / "batch_sweep".
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -61,7 +62,7 @@ def algo_slots(N: int, gate: bool = True, skip: bool = True, softplus: bool = Tr
 # the same counters' reading for plain copies of known size (FETCH_SIZE x2, WRITE_SIZE x1); null until
 # measured for the current kernel.  2: the 2.8B-shaped layer's one scan kernel; 3: the 2^20-step
 # sequence's three kernels together (aggregate pass, segment carry, output pass).
-TRAFFIC = {2: 359.8e6, 3: 9055.4e6}
+TRAFFIC = {2: 359.8e6, 3: 8968.1e6}
 
 
 def algo_slots_bwd(N: int) -> int:
@@ -221,6 +222,8 @@ def main():
         out["conv1d"] = bench_conv(torch, np, ssm, max(10, args.steps // 2))
         if args.workload == 2:
             out["conv1d"]["fused_scan"] = bench_conv_scan(torch, gen, ssm, w, max(10, args.steps // 2))
+            out["conv1d"]["fused_scan_f32"] = bench_conv_scan(torch, gen, ssm, dataclasses.replace(w, dtype="f32"),
+                                                              max(10, args.steps // 2))
     if not args.no_bwd and args.workload == 2:
         out["backward"] = bench_bwd(torch, ssm, w, x, max(5, args.steps // 5), r["ms"])
     if not args.no_ssd and args.workload == 2:
@@ -511,10 +514,11 @@ def bench_conv(torch, np, ssm, steps, K=4):
 
 
 def bench_conv_scan(torch, gen, ssm, w, steps, K=4):
-    """The causal conv1d + SiLU and the scan of the 2.8B-shaped layer, two ways: fused
-    (selective_scan_fwd_conv: u computed inside the scan kernels, never stored) and separate
-    (causal_conv1d_fwd writing u, then selective_scan_fwd reading it).  Inputs rotated over
-    three copies."""
+    """The causal conv1d + SiLU and the scan of the 2.8B-shaped layer, two ways: the one call
+    (selective_scan_fwd_conv: for fp32 rows u is computed inside the scan kernels and never
+    stored; for bf16 rows the call runs the convolution kernel into scratch and then the scan,
+    the faster route there) and separate (causal_conv1d_fwd writing u, then selective_scan_fwd
+    reading it).  Inputs rotated over three copies."""
     import numpy as np
     x = gen.scan_inputs(w)
     g = np.random.default_rng(5)
@@ -554,9 +558,11 @@ def bench_conv_scan(torch, gen, ssm, w, steps, K=4):
     res.update({"workload": f"{w.name}, causal conv1d width {K} + SiLU ahead of the scan",
                 "steps": steps, "fused_elements_per_s": el / (res["fused_us_per_call"] * 1e-6),
                 "fused_vs_separate": res["separate_us_per_call"] / res["fused_us_per_call"],
-                "hbm_bytes_saved_per_call": 2 * el * 2,
-                "note": "fused: u = silu(conv(x)) inside the scan kernels; separate: u written by the conv "
-                        "kernel and read back by the scan"})
+                "hbm_bytes_saved_per_call": 2 * el * 4 if w.dtype == "f32" else 0,
+                "io_dtype": w.dtype,
+                "note": "fused: selective_scan_fwd_conv (fp32 rows: u = silu(conv(x)) inside the scan kernels; bf16 "
+                        "rows: the conv kernel into scratch, then the scan); separate: u written by the conv kernel "
+                        "and read back by the scan"})
     del ins, y, u
     return res
 

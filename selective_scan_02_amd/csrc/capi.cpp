@@ -3,11 +3,14 @@
 // before any HIP call, so a rejected call touches no output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 
 #include "../../include/ssm_scan.h"
 #include "ssm_launch.h"
@@ -88,17 +91,65 @@ hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream) {
   return hipMallocFromPoolAsync(p, bytes, pool, stream);
 }
 
+namespace {
+struct StreamWs {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::tuple<int, hipStream_t, int>, StreamWs> g_ws;
+}  // namespace
+
+bool stream_scratch(hipStream_t stream, int slot, size_t bytes, void** out) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return false;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  StreamWs& w = g_ws[{dev, stream, slot}];
+  if (w.cap < bytes) {
+    constexpr size_t kGrain = (size_t)2 << 20;
+    const size_t cap = (std::max(bytes, 2 * w.cap) + kGrain - 1) / kGrain * kGrain;
+    void* m = nullptr;
+    if (hipMalloc(&m, cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    w.p = m;  // the outgrown buffer is dropped, not freed: work queued before may still use it
+    w.cap = cap;
+    // Keep as much reserved in the pool: a call under stream capture takes its scratch from the
+    // pool (a graph cannot share this buffer with the stream's later calls), and capture does not
+    // allow the pool to make new memory.
+    void* t = nullptr;
+    if (scratch_alloc(&t, cap + kGrain, stream) == hipSuccess) (void)hipFreeAsync(t, stream);
+    (void)hipGetLastError();
+  }
+  *out = w.p;
+  return true;
+}
+
+bool is_stream_scratch(const void* ptr) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (const auto& kv : g_ws)
+    if (kv.second.p == ptr) return true;
+  return false;
+}
+
 hipError_t scratch_acquire(const ScanParams& p, void** ptr, size_t bytes, hipStream_t stream) {
   if (p.ws) {
     if (bytes > p.ws_bytes) return hipErrorInvalidValue;
     *ptr = p.ws;
     return hipSuccess;
   }
+  if (stream_scratch(stream, 0, bytes, ptr)) return hipSuccess;
   return scratch_alloc(ptr, bytes, stream);
 }
 
 hipError_t scratch_release(const ScanParams& p, void* ptr, hipStream_t stream) {
-  if (p.ws) return hipSuccess;
+  if (p.ws || is_stream_scratch(ptr)) return hipSuccess;
   return hipFreeAsync(ptr, stream);
 }
 

@@ -101,9 +101,9 @@ namespace chunked {
 #ifndef SSM_HELPERS
 // helper waves of the output kernels: 8 (two per SIMD next to its scanner) measured 5% faster
 // than 4 on the 2.8B-shaped layer (0.229-0.232 against 0.241-0.246 ms, same box) and about 2%
-// on the 2^20-step sequence; the kernels with the fused convolution keep 4: with 8 (each helper
-// then owns 2 steps, its window reaching into the previous chunk) the fused call measured 261-262
-// against 247-248 us, their registers at the 168 cap spilling 96 bytes
+// on the 2^20-step sequence.  The kernels with the fused convolution (fp32 rows only) also take
+// 8: with the channel's taps waited for ahead of the chunk loop they measured 260 against 270 us
+// with 4 on the 2.8B-shaped layer in fp32, and 629 against 651 us on 2^18 fp32 steps.
 #define SSM_HELPERS 8
 #endif
 
@@ -111,12 +111,11 @@ constexpr int kT = 16;  // time steps per chunk (= lanes of a DPP row)
 constexpr int kW = 64;  // channels per group = lanes per wave
 constexpr int kS = 4;   // scanner waves
 
-// Helper waves per workgroup: 4 in the aggregate pass, with the fused convolution and above
-// dstate 16 (twelve waves leave 168 registers per lane, and those scanners need more),
-// otherwise SSM_HELPERS.
+// Helper waves per workgroup: 4 in the aggregate pass and above dstate 16 (twelve waves leave 168
+// registers per lane, and those scanners need more), otherwise SSM_HELPERS.
 template <int MODE, bool CONV, int N>
 constexpr int helpers() {
-  return MODE == 2 || CONV || N > 16 ? 4 : SSM_HELPERS;
+  return MODE == 2 || N > 16 ? 4 : SSM_HELPERS;
 }
 template <int MODE, bool CONV, int N>
 constexpr int threads() {
@@ -420,6 +419,10 @@ void scan_chunked_kernel(const Args a) {
       for (int m = 0; m < 4; ++m) cwv[m] = m >= cskip ? a.cw[(int64_t)cc * a.ck + (m - cskip)] : 0.0f;
       cbias = a.cb ? a.cb[cc] : 0.0f;
     }
+    // the channel's parameters loaded above are waited for here, once: left pending into the
+    // chunk loop, their first use there would wait for every load and store in flight, in every
+    // iteration (vmcnt(0) only; the other counters are left at their maximum)
+    if constexpr (CONV) __builtin_amdgcn_s_waitcnt(0x0F70);
     // CONV: u of a chunk from its prep to its finalize, two iterations later (slot = chunk % 2:
     // an iteration finalizes chunk J-2 before it preps chunk J into the same slot)
     float ukeep[2][kTPH];
@@ -1066,12 +1069,18 @@ bool chunked_supported(const ScanParams& p) {
          p.batch < (1LL << 30) && al16(p.u) && al16(p.delta) && al16(p.z) && al16(p.y) && al16(p.B) && al16(p.C);
 }
 
-bool chunked_conv_supported(const ScanParams& p) { return p.dstate == 16 && chunked_supported(p); }
+// The fused convolution runs for fp32 rows.  For bf16 rows the convolution kernel followed by the
+// scan measured faster on every shape tried (2.8B-shaped layer 221 against 239 us; 8 x 1536 x 2048
+// even; 2 x 2048 x 4096 170 against 179 us; 1024 channels x 2^17 steps 1056 against 1067 us),
+// while for fp32 rows the fused kernels were (260 against 276 us; 2^18 steps 629 against 635 us).
+bool chunked_conv_supported(const ScanParams& p) {
+  return p.dstate == 16 && p.dtype != kBF16 && chunked_supported(p);
+}
 
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream) {
-  if (p.cw) {  // fused convolution: dstate 16 (the others take the convolution kernel, then the scan)
-    if (p.dstate != 16) return hipErrorInvalidValue;
-    return p.dtype == kBF16 ? chunked::run<16, __bf16, true>(p, stream) : chunked::run<16, float, true>(p, stream);
+  if (p.cw) {  // fused convolution: dstate 16, fp32 rows (the others take the convolution kernel, then the scan)
+    if (!chunked_conv_supported(p)) return hipErrorInvalidValue;
+    return chunked::run<16, float, true>(p, stream);
   }
   return p.dtype == kBF16 ? chunked::dispatch_n<__bf16>(p, stream) : chunked::dispatch_n<float>(p, stream);
 }

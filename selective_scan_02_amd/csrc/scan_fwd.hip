@@ -287,7 +287,8 @@ static hipError_t launch_scan_fwd_conv(const ScanParams& p, hipStream_t stream) 
   }
   const size_t bytes = (size_t)(p.batch * p.dim * p.seqlen) * (p.dtype == kBF16 ? 2 : 4);
   void* u = nullptr;
-  hipError_t e = scratch_alloc(&u, bytes, stream);
+  const bool kept = stream_scratch(stream, 1, bytes, &u);
+  hipError_t e = kept ? hipSuccess : scratch_alloc(&u, bytes, stream);
   if (e != hipSuccess) return e;
   c.out = u;
   e = launch_conv1d_fwd(c, stream);
@@ -295,7 +296,7 @@ static hipError_t launch_scan_fwd_conv(const ScanParams& p, hipStream_t stream) 
     q.u = u;
     e = launch_scan_fwd(q, stream);
   }
-  const hipError_t f = hipFreeAsync(u, stream);
+  const hipError_t f = kept ? hipSuccess : hipFreeAsync(u, stream);
   return e != hipSuccess ? e : f;
 }
 

@@ -131,9 +131,17 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t seqlen, int cus);
 // the carries and flags of one call reuse the memory of the previous one.
 hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream);
 
+// Scratch kept per (device, stream, slot) between calls, grow-only: the calls on one stream run in
+// order, so each reuses the buffer without allocating (a stream-ordered pool allocation and free
+// per call put a few microseconds between consecutive kernels).  False under graph capture, where
+// a pool allocation becomes part of the graph, or when the buffer cannot be made.  Slot 0 is the
+// forward scan's scratch, slot 1 the convolution output of the two-kernel convolution + scan.
+bool stream_scratch(hipStream_t stream, int slot, size_t bytes, void** out);
+bool is_stream_scratch(const void* ptr);
+
 // Scratch of one scan call: from the caller's workspace when the parameters carry one (which
-// must hold `bytes`, else hipErrorInvalidValue), otherwise from the pool.  scratch_release
-// returns pool memory on the stream and does nothing for a workspace.
+// must hold `bytes`, else hipErrorInvalidValue), otherwise the stream's slot-0 scratch, else the
+// pool.  scratch_release returns pool memory on the stream and does nothing for the others.
 hipError_t scratch_acquire(const ScanParams& p, void** ptr, size_t bytes, hipStream_t stream);
 hipError_t scratch_release(const ScanParams& p, void* ptr, hipStream_t stream);
 
@@ -170,7 +178,7 @@ bool dstate_supported(int64_t n);
 hipError_t launch_scan_fwd(const ScanParams& p, hipStream_t stream);      // dispatcher
 hipError_t launch_scan_generic(const ScanParams& p, hipStream_t stream);  // any shape / alignment
 bool chunked_supported(const ScanParams& p);
-bool chunked_conv_supported(const ScanParams& p);  // the fused convolution path (dstate 16)
+bool chunked_conv_supported(const ScanParams& p);  // the fused convolution path (dstate 16, fp32 rows)
 hipError_t launch_scan_chunked(const ScanParams& p, hipStream_t stream);  // fast path
 hipError_t launch_scan_bwd(const BwdParams& p, hipStream_t stream);
 bool ssd_supported(int64_t headdim, int64_t dstate);

@@ -4,15 +4,16 @@ Reference: the fp64 oracle's convolution (oracle.conv1d) followed by its scan (o
 the block's step before the scan, then the scan (Mamba summary, 方法 third step; mlqm.cn
 tutorial §7.1).  The oracle's scan reads its inputs as fp32 or bf16 bytes of one dtype, so the
 composed reference widens x's companions (delta, z, B, C) exactly to fp32 and rounds the fp64
-convolution output u to fp32 (relative error 2^-24, far below the tolerances).  The fused
-kernels keep u in fp32, so:
+convolution output u to fp32 (relative error 2^-24, far below the tolerances), and further to bf16
+for bf16 rows, as the convolution kernel of their route stores it.  The call runs the
+fused kernels for fp32 rows (u kept in fp32, never stored) and, for bf16 rows, the convolution
+kernel into scratch and then the scan (the faster route there; u rounded to bf16 in between), so:
   * y and last_state match that reference within 1e-4 (fp32 I/O) or 2e-2 (bf16 I/O);
   * the convolution state out is exact (it is a copy of inputs);
   * with fp32 I/O the fused call equals causal_conv1d_fwd followed by the scan bit for bit
-    (same fp32 arithmetic in the same order; the separate route stores u in fp32 too), and
-    with bf16 I/O the two differ only by the separate route's rounding of u to bf16.
-Every launch plan is covered: intervals, one pass and the two-pass split with the fused
-kernels (dstate 16), and the two-kernel route (other dstates, rows that are not whole
+    (same fp32 arithmetic in the same order; the separate route stores u in fp32 too).
+Every launch plan is covered: intervals, one pass and the two-pass split, with the fused kernels
+(fp32, dstate 16) and with the two-kernel route (bf16, other dstates, rows that are not whole
 16-byte pieces).
 """
 import sys
@@ -79,6 +80,9 @@ def reference(x, chans=None):
         u32[rows] = torch.from_numpy(u64.reshape(len(rows), L).astype(np.float32))
         u32 = u32.reshape(b, d, L)
         so = so.reshape(len(rows), -1)
+    if x["dtype"] == "bf16":
+        # bf16 rows take the convolution kernel, which writes u in the rows' dtype, then the scan
+        u32 = u32.to(torch.bfloat16).float()
     f = lambda t: None if t is None else t.float()
     h0 = x["h0"]
     if h0 is not None and chans is not None:
@@ -136,6 +140,7 @@ PLANS = [  # (name, plan, batch, dim, dstate, seqlen, dtype)
     ("intervals", "intervals", 2, 10240, 16, 512, "bf16"),
     ("intervals-f32", "intervals", 1, 20480, 16, 256, "f32"),
     ("single", "single", 1, 10240, 16, 256, "bf16"),
+    ("single-f32", "single", 1, 10240, 16, 256, "f32"),
     ("two-pass", "two-pass", 1, 256, 16, 40_000, "f32"),
     ("two-pass-bf16", "two-pass", 2, 64, 16, 65_536, "bf16"),
 ]
@@ -154,8 +159,8 @@ def test_fused_conv_scan_launch_plans(case):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_fused_equals_separate_kernels(dt):
-    """Against causal_conv1d_fwd followed by the scan on the GPU: bit for bit in fp32; in bf16 the
-    separate route rounds u to bf16 in between, so only the tolerance applies."""
+    """Against causal_conv1d_fwd followed by the scan on the GPU: bit for bit in fp32 (the fused
+    kernels); in bf16 (where the call takes the same two kernels) both within the tolerance."""
     b, d, n, L = 2, 10240, 16, 512   # the interval plan
     note(f"fused vs separate kernels {dt}")
     x = conv_inputs(b, d, n, L, dt, 4, seed=7, h0=True)
