@@ -131,6 +131,15 @@ bool stream_scratch(hipStream_t stream, int slot, size_t bytes, void** out) {
   return true;
 }
 
+hipError_t call_scratch(hipStream_t stream, int slot, size_t bytes, void** ptr, bool* kept) {
+  *kept = stream_scratch(stream, slot, bytes, ptr);
+  return *kept ? hipSuccess : scratch_alloc(ptr, bytes, stream);
+}
+
+hipError_t call_scratch_release(void* ptr, bool kept, hipStream_t stream) {
+  return kept ? hipSuccess : hipFreeAsync(ptr, stream);
+}
+
 bool is_stream_scratch(const void* ptr) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   for (const auto& kv : g_ws)

@@ -1859,7 +1859,8 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   size_t total = 0;
   for (size_t f : fl) total += (f + 63) / 64 * 64;  // 256-byte aligned pieces
   void* scratch = nullptr;
-  hipError_t err = scratch_alloc(&scratch, total * sizeof(float), stream);
+  bool kept = false;
+  hipError_t err = call_scratch(stream, 4, total * sizeof(float), &scratch, &kept);
   if (err != hipSuccess) return err;
   float* q = (float*)scratch;
   float* ctl = nullptr;
@@ -1924,7 +1925,7 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
                        a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)pslots);
     err = hipGetLastError();
   }
-  const hipError_t ferr = hipFreeAsync(scratch, stream);
+  const hipError_t ferr = call_scratch_release(scratch, kept, stream);
   return err != hipSuccess ? err : ferr;
 }
 

@@ -431,7 +431,8 @@ hipError_t run(const SsdParams& p, hipStream_t stream) {
   const int64_t bh = p.batch * p.heads;
   const size_t nS = (size_t)bh * a.chunks * N * kP;
   void* scratch = nullptr;
-  hipError_t err = scratch_alloc(&scratch, nS * sizeof(float), stream);
+  bool kept = false;
+  hipError_t err = call_scratch(stream, 2, nS * sizeof(float), &scratch, &kept);
   if (err != hipSuccess) return err;
   a.S = (float*)scratch;
   hipLaunchKernelGGL((ssd_state_kernel<N, kP>), dim3(kP / 16, (unsigned)bh), dim3(64), 0, stream, a);
@@ -441,7 +442,7 @@ hipError_t run(const SsdParams& p, hipStream_t stream) {
                        a);
     err = hipGetLastError();
   }
-  const hipError_t ferr = hipFreeAsync(scratch, stream);
+  const hipError_t ferr = call_scratch_release(scratch, kept, stream);
   return err != hipSuccess ? err : ferr;
 }
 

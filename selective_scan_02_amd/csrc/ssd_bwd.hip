@@ -122,7 +122,8 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
   size_t total = 0;
   for (size_t v : sz) total += v;
   void* scratch = nullptr;
-  hipError_t err = scratch_alloc(&scratch, total, stream);
+  bool kept = false;
+  hipError_t err = call_scratch(stream, 3, total, &scratch, &kept);
   if (err != hipSuccess) return err;
   char* c = (char*)scratch;
   T* delta = (T*)c;            c += sz[0];
@@ -173,7 +174,7 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
                        q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, P, N);
     err = hipGetLastError();
   }
-  const hipError_t ferr = hipFreeAsync(scratch, stream);
+  const hipError_t ferr = call_scratch_release(scratch, kept, stream);
   return err != hipSuccess ? err : ferr;
 }
 

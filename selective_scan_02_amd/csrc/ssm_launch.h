@@ -135,9 +135,14 @@ hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream);
 // order, so each reuses the buffer without allocating (a stream-ordered pool allocation and free
 // per call put a few microseconds between consecutive kernels).  False under graph capture, where
 // a pool allocation becomes part of the graph, or when the buffer cannot be made.  Slot 0 is the
-// forward scan's scratch, slot 1 the convolution output of the two-kernel convolution + scan.
+// forward scan's scratch, slot 1 the convolution output of the two-kernel convolution + scan, slot 2 the
+// SSD forward's chunk states, slot 3 the SSD backward's broadcast parameters and gradients, slot 4 the
+// backward scan's checkpoints, carries and partial sums.
 bool stream_scratch(hipStream_t stream, int slot, size_t bytes, void** out);
 bool is_stream_scratch(const void* ptr);
+// The stream's slot when it can be kept, else pool memory; call_scratch_release frees only the latter.
+hipError_t call_scratch(hipStream_t stream, int slot, size_t bytes, void** ptr, bool* kept);
+hipError_t call_scratch_release(void* ptr, bool kept, hipStream_t stream);
 
 // Scratch of one scan call: from the caller's workspace when the parameters carry one (which
 // must hold `bytes`, else hipErrorInvalidValue), otherwise the stream's slot-0 scratch, else the
