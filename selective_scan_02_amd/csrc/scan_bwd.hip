@@ -693,7 +693,9 @@ struct PreLds {
 };
 
 // 1'. Checkpoint pass, 16-byte rows: segment `seg` of this workgroup's channel group.
-template <int N, typename T>
+// UNI: every channel's A row holds one value (the SSD form), so a step's Abar is one exp for all states
+// (the same values as the general form computes).
+template <int N, typename T, bool UNI = false>
 __device__ __forceinline__ void fbwd_checkpoint(const BwdArgs& a, int seg, unsigned char* lds) {
   using TL = Tile<T>;
   float(*sB)[N] = reinterpret_cast<float(*)[N]>(lds);
@@ -756,13 +758,14 @@ __device__ __forceinline__ void fbwd_checkpoint(const BwdArgs& a, int seg, unsig
       const float dt = step_size(dv[i] + bias, a.softplus);
       const float du = dt * uv[i];
       const float4* br = (const float4*)sB[i];
+      const float e = UNI ? ex2(dt * A2[0]) : 0.0f;
 #pragma unroll
       for (int n = 0; n < N; n += 4) {
         const float4 bq = br[n / 4];
-        h[n] = __builtin_fmaf(ex2(dt * A2[n]), h[n], du * bq.x);
-        h[n + 1] = __builtin_fmaf(ex2(dt * A2[n + 1]), h[n + 1], du * bq.y);
-        h[n + 2] = __builtin_fmaf(ex2(dt * A2[n + 2]), h[n + 2], du * bq.z);
-        h[n + 3] = __builtin_fmaf(ex2(dt * A2[n + 3]), h[n + 3], du * bq.w);
+        h[n] = __builtin_fmaf(UNI ? e : ex2(dt * A2[n]), h[n], du * bq.x);
+        h[n + 1] = __builtin_fmaf(UNI ? e : ex2(dt * A2[n + 1]), h[n + 1], du * bq.y);
+        h[n + 2] = __builtin_fmaf(UNI ? e : ex2(dt * A2[n + 2]), h[n + 2], du * bq.z);
+        h[n + 3] = __builtin_fmaf(UNI ? e : ex2(dt * A2[n + 3]), h[n + 3], du * bq.w);
       }
       cum += dt;
     }
@@ -857,12 +860,12 @@ __device__ __forceinline__ void fbwd_adjoint_aggregate(const BwdArgs& a, int seg
 // 1' and 3a' in one launch: rows 0 .. nseg-1 of the grid are the checkpoint pass of each segment,
 // rows nseg .. 2 nseg-2 the adjoint aggregate of segments 1 .. nseg-1.  The two need nothing of each
 // other, and one grid of both keeps twice the waves resident to hide each other's latency.
-template <int N, typename T>
+template <int N, typename T, bool UNI = false>
 __global__ __launch_bounds__(kWave) void fbwd_pre_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char lds[PreLds<N, T>::kBytes];
   const int y = blockIdx.y;
   if (y < a.nseg)
-    fbwd_checkpoint<N, T>(a, y, lds);
+    fbwd_checkpoint<N, T, UNI>(a, y, lds);
   else
     fbwd_adjoint_aggregate<N, T>(a, y - a.nseg + 1, lds);
 }
@@ -1186,7 +1189,7 @@ __device__ __forceinline__ void lds_put_pair(__bf16* p, float x, float y) {
 }
 __device__ __forceinline__ void lds_put_pair(float* p, float x, float y) { *(float2*)p = make_float2(x, y); }
 
-template <int N, typename T>
+template <int N, typename T, bool UNI = false>
 __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kernel(BwdArgs a) {
   constexpr int kRS = roles_scanners<T, N>();
   constexpr int NPW = N / kRS;           // states per scanner
@@ -1406,9 +1409,10 @@ __global__ __launch_bounds__((roles_threads<T, N>())) void fbwd_main_roles_kerne
           lds_vec<NPW>(&sm.bcs[wv][0][i][0], Bv);
           lds_vec<NPW>(&sm.bcs[wv][1][i][0], Cv);
           float s = 0.0f;
+          const float e1 = UNI ? ex2(dt[i] * A2[0]) : 0.0f;  // the SSD form: one exp for the step
 #pragma unroll
           for (int j = 0; j < NPW; ++j) {
-            ab[i][j] = ex2(dt[i] * A2[j]);
+            ab[i][j] = UNI ? e1 : ex2(dt[i] * A2[j]);
             hp[i][j] = h[j];
             h[j] = __builtin_fmaf(ab[i][j], h[j], dut[i] * Bv[j]);
             s = __builtin_fmaf(Cv[j], h[j], s);
@@ -1784,6 +1788,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   a.u = p.u; a.delta = p.delta; a.A = p.A; a.B = p.B; a.C = p.C; a.D = p.D; a.z = p.z; a.dt_bias = p.dt_bias;
   a.h0 = p.h0; a.dy = p.dy; a.du = p.du; a.ddelta = p.ddelta; a.dz = p.dz; a.dh0 = p.dh0;
   a.ddelta_f32 = p.ddelta_f32 ? 1 : 0;
+  // the SSD form's A (one value per channel) takes the kernels that compute one exp per step; above
+  // dstate 16 their second copy would crowd the registers, so those take the general kernels
+  constexpr bool UNIF = FAST && N <= 16;
+  const bool uni = UNIF && p.a_uniform;
   a.batch = p.batch; a.dim = p.dim; a.seqlen = p.seqlen; a.softplus = p.softplus;
   a.chans = p.batch * p.dim;
   a.groups = (int)((p.dim + kWave - 1) / kWave);
@@ -1878,10 +1886,14 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     handover_wait(&a.max_polls, &a.publish);
   }
   const dim3 grid((unsigned)units, (unsigned)nseg);
-  if constexpr (FAST)  // checkpoints (and, on the segment plan, adjoint aggregates) in one grid
-    hipLaunchKernelGGL((fbwd_pre_kernel<N, T>), dim3((unsigned)units, (unsigned)(IV ? nseg : 2 * nseg - 1)),
-                       dim3(kWave), 0, stream, a);
-  else
+  if constexpr (FAST) {  // checkpoints (and, on the segment plan, adjoint aggregates) in one grid
+    if (uni)
+      hipLaunchKernelGGL((fbwd_pre_kernel<N, T, UNIF>), dim3((unsigned)units, (unsigned)(IV ? nseg : 2 * nseg - 1)),
+                         dim3(kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fbwd_pre_kernel<N, T>), dim3((unsigned)units, (unsigned)(IV ? nseg : 2 * nseg - 1)),
+                         dim3(kWave), 0, stream, a);
+  } else
     hipLaunchKernelGGL((bwd_checkpoint_kernel<N, T>), grid, dim3(kWave), 0, stream, a);
   err = hipGetLastError();
   if (err == hipSuccess && nseg > 1) {
@@ -1901,9 +1913,14 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   }
   if (err == hipSuccess && IV) err = zero(ctl, 64 + units * kRSc, stream);  // ticket and flags (0.0f is all zero bits)
   if (err == hipSuccess) {
-    if constexpr (ROLES)
-      hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T>), IV ? dim3((unsigned)a.iunits) : grid,
-                         dim3(roles_threads<T, N>()), 0, stream, a);
+    if constexpr (ROLES) {
+      if (uni)
+        hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T, UNIF>), IV ? dim3((unsigned)a.iunits) : grid,
+                           dim3(roles_threads<T, N>()), 0, stream, a);
+      else
+        hipLaunchKernelGGL((fbwd_main_roles_kernel<N, T>), IV ? dim3((unsigned)a.iunits) : grid,
+                           dim3(roles_threads<T, N>()), 0, stream, a);
+    }
     else if constexpr (FAST)
       hipLaunchKernelGGL((fbwd_main_kernel<N, T>), grid, dim3(kWave * W), 0, stream, a);
     else

@@ -158,6 +158,7 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
     b.ddt_bias = q.ddt_bias ? dbias_full : nullptr; b.dh0 = q.dh0;
     b.batch = f.batch; b.dim = dim; b.dstate = N; b.seqlen = L; b.dtype = q.dtype;
     b.ddelta_f32 = true;
+    b.a_uniform = true;
     err = launch_scan_bwd(b, stream);
   }
   if (err == hipSuccess && L > 0) {

@@ -96,6 +96,7 @@ struct BwdParams {
   float* ddt_bias;       // nullable
   float* dh0;            // nullable
   bool ddelta_f32 = false;  // ddelta in fp32 whatever dtype is (its row stride is still seqlen)
+  bool a_uniform = false;   // A[d, n] is the same for every n of each channel d (the SSD form)
   int64_t batch, dim, dstate, seqlen;
   int dtype;
 };

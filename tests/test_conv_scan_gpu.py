@@ -210,3 +210,14 @@ def test_fused_empty_sequence():
     y, last, cso = gpu_fused(x)
     assert y.shape == (b, d, 0)
     assert torch.equal(last.cpu(), x["h0"]) and torch.equal(cso.cpu(), x["cst"])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_conv_scan_full_layer_sampled(dt):
+    """The 2.8B-shaped layer (B=4, D=5120, N=16, L=2048) in the launch configuration the bench times:
+    fp32 rows on the fused kernels, bf16 rows on the convolution kernel then the scan; sampled channels
+    against the oracle, the whole convolution state exactly."""
+    b, d, n, L = 4, 5120, 16, 2048
+    note(f"conv+scan 2.8B-shaped layer {dt}")
+    x = conv_inputs(b, d, n, L, dt, 4, seed=21, h0=True)
+    check(x, chans=sampled(b * d, 48, 22))
