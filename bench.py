@@ -542,21 +542,29 @@ def bench_conv_scan(torch, gen, ssm, w, steps, K=4):
                      y=y, last_state=last)
 
     stream = torch.cuda.current_stream()
-    res = {}
-    for name, fn in (("fused", fused), ("separate", separate)):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res[name + "_us_per_call"] = e0.elapsed_time(e1) / steps * 1e3
+    # the two routes alternate in rounds (the order flipping each round), so that a drift of the
+    # clock over the run weighs on both alike
+    for i in range(3):
+        fused(i)
+        separate(i)
+    torch.cuda.synchronize()
+    rounds = 4
+    per = max(1, steps // rounds)
+    ms = {"fused": 0.0, "separate": 0.0}
+    for r in range(rounds):
+        order = (("fused", fused), ("separate", separate)) if r % 2 == 0 else (("separate", separate), ("fused", fused))
+        for name, fn in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(per):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms[name] += e0.elapsed_time(e1)
+    res = {name + "_us_per_call": v / (rounds * per) * 1e3 for name, v in ms.items()}
     el = w.batch * w.dim * w.seqlen
     res.update({"workload": f"{w.name}, causal conv1d width {K} + SiLU ahead of the scan",
-                "steps": steps, "fused_elements_per_s": el / (res["fused_us_per_call"] * 1e-6),
+                "steps": rounds * per, "fused_elements_per_s": el / (res["fused_us_per_call"] * 1e-6),
                 "fused_vs_separate": res["separate_us_per_call"] / res["fused_us_per_call"],
                 "hbm_bytes_saved_per_call": 2 * el * 4 if w.dtype == "f32" else 0,
                 "io_dtype": w.dtype,
