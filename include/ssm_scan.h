@@ -36,9 +36,13 @@
  *  - `dtype` (ssm_dtype_t) is the element type of u, delta, z, B, C and y.  A, D,
  *    dt_bias and the state are always fp32.  Arithmetic is fp32 throughout.
  *  - Ownership: the caller owns every buffer.  The library keeps no pointer to them
- *    after a call returns.  Scratch memory (scan segment carries and flags) is taken,
- *    stream-ordered on `stream`, from a memory pool the library creates per device and
- *    keeps until the process exits, and is returned to that pool on `stream`.
+ *    after a call returns.  Scratch memory (segment carries, checkpoints, chunk states) is
+ *    kept per (device, stream) between calls and held until the process exits: the calls on
+ *    one stream run in order and reuse it, calls on different streams never share it.  Under
+ *    graph capture it is taken instead, stream-ordered on `stream`, from a memory pool the
+ *    library creates per device, and returned to that pool on `stream`; a captured call needs
+ *    the pool to hold as much already (an earlier call of that size on any stream reserves it),
+ *    since capture does not let the pool make new memory.
  *  - Calls are asynchronous on `stream` (hipStream_t; NULL = the null stream) and
  *    never synchronise the device.
  *  - Errors: the return value is an ssm_status_t.  Arguments are validated before
@@ -112,14 +116,14 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, int dtype, void* stream);
 
 /*
- * The causal conv1d + SiLU of the Mamba block fused ahead of the scan: the scan's input u is
- * computed from x inside the scan kernels instead of being read from memory,
+ * The causal conv1d + SiLU of the Mamba block and the scan after it, in one call:
  *   u_t = silu(conv_bias[d] + sum_{k<width} conv_weight[d,k] * x[t-(width-1)+k])
  * (Mamba summary (junchaoiu.github.io), 方法 third step: 1-D convolution for local features, then
  * SiLU, then the selective SSM; mlqm.cn tutorial §7.1), and then exactly the scan of
- * selective_scan_fwd_resume on that u.  u never reaches memory: against causal_conv1d_fwd
- * followed by the scan, this saves writing u and reading it back.  (A model that also feeds u
- * to other layers needs causal_conv1d_fwd for it.)
+ * selective_scan_fwd_resume on that u.  The call takes whichever route measured faster: for fp32
+ * rows (dstate 16) the convolution runs inside the scan kernels and u never reaches memory; for
+ * bf16 rows the convolution kernel writes u to scratch kept for the stream and the scan reads it.
+ * (A model that also feeds u to other layers needs causal_conv1d_fwd for it.)
  *
  *   x               : [batch, dim, seqlen] (dtype), the convolution's input
  *   conv_weight     : [dim, width] fp32, width in 1..4 (required); conv_bias : [dim] fp32, NULL = 0
@@ -129,10 +133,11 @@ int selective_scan_fwd_resume(const void* u, const void* delta, const float* A, 
  *                     overlap any other argument.
  *   delta, A, B, C, D, z, dt_bias, softplus, initial_state, y, last_state, sizes, dtype, stream:
  *                     as for selective_scan_fwd_resume.
- * u is kept in fp32 between the convolution and the scan (causal_conv1d_fwd followed by the scan
- * rounds it to dtype in between), so the two routes agree within the dtype's rounding of u.
- * Calls the fast scan kernels cannot take (dstate < 4, rows that are not whole 16-byte pieces,
- * unaligned tensors) run the convolution into pool scratch and the scan on it.  Errors as for
+ * On the fused route u is kept in fp32 between the convolution and the scan, as
+ * causal_conv1d_fwd followed by the scan does with fp32 rows, so the two agree bit for bit there;
+ * on the other route u is rounded to the rows' dtype, as causal_conv1d_fwd stores it.  Other
+ * dstates, rows that are not whole 16-byte pieces and unaligned tensors take the second route
+ * too.  Errors as for
  * selective_scan_fwd; width outside 1..4 is SSM_ERR_UNSUPPORTED, a NULL conv_weight
  * SSM_ERR_NULL_ARG.
  */
@@ -194,7 +199,7 @@ int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
  * deterministic.  Every output must not overlap an input or another output.  seqlen == 0
  * writes zeros to dA, dD, ddt_bias and dinitial_state.  Required: u, delta, A, B, C, dy,
  * du, ddelta, dA, dB, dC (all but A and dA may be NULL when seqlen == 0).  Scratch memory
- * from the library's pool: about (4 * dstate / T + 1) * 4 bytes per (batch, dim, step),
+ * (kept for the stream, as above): about (4 * dstate / T + 1) * 4 bytes per (batch, dim, step),
  * T = 16, 8, 2, 1 steps per chunk for dstate <= 8, 16, 32, 64, plus the per-channel-group
  * partials of dB and dC.  Errors as for selective_scan_fwd.
  */
