@@ -373,10 +373,21 @@ int ssm_test_handover_wait(int max_polls, int publish);
 /* Text describing the calling thread's most recent non-OK status ("" if none). */
 const char* ssm_last_error(void);
 
+/*
+ * Frees the memory the library keeps for `stream` on the current device: the scratch of the
+ * scans on that stream (carries, checkpoints, chunk states, the convolution's output) and the
+ * interval schedule's control block.  For callers that retire a stream, or a serving loop that
+ * wants the memory back between phases.  It first waits for the work queued on the stream;
+ * the caller must not queue new work on that stream from another thread while it runs.  The
+ * next call on the stream makes what it needs again.  A capturing stream is refused with
+ * SSM_ERR_UNSUPPORTED.  Memory the library's pool holds in reserve for captured calls is kept.
+ */
+int ssm_release_stream(void* stream);
+
 /* ABI version of this header (incremented whenever an entry point is added or changed). */
 int ssm_abi_version(void);
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ EXPORTS = ("selective_scan_fwd", "selective_scan_fwd_resume", "selective_scan_fw
            "ssd_scan_fwd", "ssd_scan_bwd",
            "selective_state_update", "causal_conv1d_fwd",
            "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
-           "ssm_last_error", "ssm_abi_version")
+           "ssm_release_stream", "ssm_last_error", "ssm_abi_version")
 
 
 class SsmError(RuntimeError):
@@ -90,6 +90,8 @@ def load():
         lib.ssm_handover_failures.restype = I
         lib.ssm_test_handover_wait.argtypes = [I, I]
         lib.ssm_test_handover_wait.restype = I
+        lib.ssm_release_stream.argtypes = [P]
+        lib.ssm_release_stream.restype = I
         _lib = lib
     return _lib
 
@@ -103,6 +105,13 @@ def scan_plan(batch: int, dim: int, dstate: int, seqlen: int, dtype=torch.bfloat
     code = BF16 if dtype in (torch.bfloat16, "bf16", BF16) else F32
     _check(load().ssm_scan_plan(batch, dim, dstate, seqlen, code, num_cus, out))
     return {"mode": PLAN_MODES[out[0]], "groups": out[1], "segments": out[2], "seg_len": out[3], "units": out[4]}
+
+
+def release_stream(stream=None) -> None:
+    """Free the scratch and control block the library keeps for `stream` (a torch stream, or None
+    for torch's current stream) on the current device, after the work queued on it."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    _check(load().ssm_release_stream(ctypes.c_void_p(s.cuda_stream)))
 
 
 def handover_failures(reset: bool = False) -> int:

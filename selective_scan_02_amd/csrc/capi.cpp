@@ -140,6 +140,20 @@ hipError_t call_scratch_release(void* ptr, bool kept, hipStream_t stream) {
   return kept ? hipSuccess : hipFreeAsync(ptr, stream);
 }
 
+void stream_scratch_release(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (std::get<0>(it->first) == dev && std::get<1>(it->first) == stream) {
+      if (it->second.p) (void)hipFree(it->second.p);
+      it = g_ws.erase(it);
+    } else {
+      ++it;
+    }
+  }
+}
+
 bool is_stream_scratch(const void* ptr) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   for (const auto& kv : g_ws)
@@ -169,6 +183,17 @@ extern "C" {
 const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+int ssm_release_stream(void* stream) {
+  const hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (int rc = hip_status(hipStreamIsCapturing(s, &st), "ssm_release_stream")) return rc;
+  if (st != hipStreamCaptureStatusNone) return fail(SSM_ERR_UNSUPPORTED, "ssm_release_stream: the stream is capturing");
+  if (int rc = hip_status(hipStreamSynchronize(s), "ssm_release_stream")) return rc;
+  ssm::stream_scratch_release(s);
+  ssm::interval_ctl_release(s);
+  return hip_status(hipGetLastError(), "ssm_release_stream");
+}
 
 int ssm_handover_failures(int64_t* count, int reset) {
   g_last_error.clear();

@@ -1033,6 +1033,16 @@ bool interval_ctl(hipStream_t s, int64_t nflags, int64_t units, unsigned long lo
   return true;
 }
 
+void interval_ctl_release(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_ctl_mutex);
+  auto it = g_ctl.find({dev, s});
+  if (it == g_ctl.end()) return;
+  if (it->second.mem) (void)hipFree(it->second.mem);  // the stream has drained (the caller synchronised it)
+  g_ctl.erase(it);
+}
+
 void interval_ctl_invalidate(hipStream_t s) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;

@@ -141,6 +141,8 @@ hipError_t scratch_alloc(void** p, size_t bytes, hipStream_t stream);
 // backward scan's checkpoints, carries and partial sums.
 bool stream_scratch(hipStream_t stream, int slot, size_t bytes, void** out);
 bool is_stream_scratch(const void* ptr);
+// Frees every slot kept for the stream on the current device (the stream must have drained).
+void stream_scratch_release(hipStream_t stream);
 // The stream's slot when it can be kept, else pool memory; call_scratch_release frees only the latter.
 hipError_t call_scratch(hipStream_t stream, int slot, size_t bytes, void** ptr, bool* kept);
 hipError_t call_scratch_release(void* ptr, bool kept, hipStream_t stream);
@@ -176,6 +178,8 @@ hipError_t handover_failures(uint64_t* count, bool reset);
 bool interval_ctl(hipStream_t s, int64_t nflags, int64_t units, unsigned long long** ticket,
                   unsigned long long** flags, unsigned long long* base, unsigned long long* gen);
 void interval_ctl_invalidate(hipStream_t s);  // after a failed launch: the next call makes a new block
+// Frees the stream's control block (the stream must have drained); the next call makes a new one.
+void interval_ctl_release(hipStream_t s);
 hipError_t bwd_handover_failures(uint64_t* count, bool reset);  // the backward main pass's
 void set_handover_wait(int max_polls, int publish);
 void handover_wait(int* max_polls, int* publish);  // the current settings

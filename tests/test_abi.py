@@ -46,7 +46,7 @@ def test_header_declares_the_entry_points():
                  "selective_state_update",
                  "causal_conv1d_fwd",
                  "causal_conv1d_update", "ssm_scan_plan", "ssm_handover_failures", "ssm_test_handover_wait",
-                 "ssm_last_error", "ssm_abi_version"):
+                 "ssm_release_stream", "ssm_last_error", "ssm_abi_version"):
         assert name in fns
     assert set(fns) == set(ssm.EXPORTS)
 
@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.ssm_abi_version() == 9
+    assert lib.ssm_abi_version() == 10
 
 
 def scan_args(**over):

@@ -79,3 +79,23 @@ def test_interval_control_block_across_calls_and_streams():
         assert same(o, ref)
     torch.cuda.synchronize()
     assert ssm.handover_failures(reset=True) == 0
+
+
+def test_release_stream_then_calls_remake_what_they_need():
+    """ssm_release_stream frees the stream's scratch and control block after its queued work; the
+    calls after it make them again and give the same bits (the interval plan and the two-pass plan,
+    on a side stream and on the current one)."""
+    note("release the per-stream scratch and control block")
+    g = dev(gen.random_scan_inputs(4, 5120, 16, 256, "bf16", seed=31))     # interval plan
+    g2 = dev(gen.random_scan_inputs(1, 64, 16, 65536, "f32", seed=32))     # two-pass plan
+    s = torch.cuda.Stream()
+    for stream in (s, torch.cuda.current_stream()):
+        with torch.cuda.stream(stream):
+            r1, q1 = scan(g), scan(g2)
+            ssm.release_stream(stream)
+            r2, q2 = scan(g), scan(g2)
+            ssm.release_stream(stream)
+            r3 = scan(g)
+        torch.cuda.synchronize()
+        assert same(r1, r2) and same(r1, r3)
+        assert torch.equal(q1[0], q2[0]) and torch.equal(q1[1], q2[1])
