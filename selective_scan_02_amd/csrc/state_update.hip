@@ -8,9 +8,9 @@
 // h = dA*h + dB*x, y = sum(C*h) + D*x).
 //
 // The step is bound by HBM: 2*dstate*4 bytes of state traffic per (b, d)
-// against a few bytes of inputs.  Layout: each lane owns 8 consecutive states
-// of one (b, d) row (two 16-byte loads and stores), so a wave reads contiguous
-// state with every instruction; the dstate/8 lanes of a row combine their
+// against a few bytes of inputs.  Layout: each lane owns 4 consecutive states
+// of one (b, d) row (one 16-byte load and store), so a wave reads contiguous
+// state with every instruction; the dstate/4 lanes of a row combine their
 // partial readouts with cross-lane adds.
 #include <hip/hip_runtime.h>
 
@@ -37,17 +37,22 @@ struct StepArgs {
 };
 
 // A block covers 256 / LPR consecutive channels d (LPR lanes per (b, d) row) of kRPT consecutive
-// batch rows: the channel's parameters (its row of A, dt_bias, D) are loaded once for the kRPT
-// rows, every state load or store instruction of a wave moves one contiguous kilobyte, and each
-// lane keeps all its rows' state loads in flight.  (b, d) come from the block's coordinates, with
-// no division.  Grids taller than the launch limit walk the batch groups with a stride.  Two rows
-// per thread measured best on the 2.8B-shaped serving batch (256 x 5120, dstate 16): 29.7 / 38.0 us
-// back to back / cache flushed, against 30.2 / 39.8 for one row and 29.3 / 39.6 for four.
-constexpr int kRPT = 2;
-// States per lane (all of them when dstate is smaller): a lane moves two 16-byte pieces of its row.
-// On the same batch, 8 states per lane with 2 rows measured 28.0 / 37.2 us, 4 per lane 29.6 / 37.6,
-// 16 per lane 35.9 / 47.1.
-constexpr int kSPL = 8;
+// batch rows, and every lane moves SPL = 4 consecutive states of a row with one 16-byte load and
+// store, so each state load or store instruction of a wave moves one contiguous kilobyte.  All of a
+// lane's loads -- its rows' states first, then their inputs, then the channel's parameters -- are
+// issued before any arithmetic, so a wave waits for memory once.  (b, d) come from the block's
+// coordinates, with no division.  Grids taller than the launch limit walk the batch groups with a
+// stride.  On the 2.8B-shaped serving batch (256 x 5120, dstate 16; HIP events around each step,
+// cache flushed before it / back to back): 4 states per lane with 2 rows per thread measured
+// 32.4 / 27.3 us, against 36.2 / 28.5 with 8 states per lane and 37.3 / 27.6 for the layout before
+// it (8 states per lane, the channel's parameters waited for before the state loads were issued);
+// persistent blocks walking several units, with or without the next unit's loads issued ahead,
+// measured 36.6-50 us.
+#ifndef SSM_DECODE_RPT
+#define SSM_DECODE_RPT 2
+#endif
+constexpr int kRPT = SSM_DECODE_RPT;
+constexpr int kSPL = 4;
 
 template <int N, typename T>
 __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
@@ -60,37 +65,26 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
   const bool dok = dr < a.dim;
   const int64_t d = dok ? dr : a.dim - 1;
 
-  // this lane's SPL consecutive entries of A[d], premultiplied by log2(e); dt_bias and D of d
-  float a2[SPL];
-  if constexpr (kVec) {
-#pragma unroll
-    for (int k = 0; k < SPL; k += 4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(a.A + d * N + q * SPL + k);
-      a2[k] = a4.x * kLog2e; a2[k + 1] = a4.y * kLog2e; a2[k + 2] = a4.z * kLog2e; a2[k + 3] = a4.w * kLog2e;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) a2[j] = a.A[d * N + q * SPL + j] * kLog2e;
-  }
-  const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
-  const float Dd = a.D ? a.D[d] : 0.0f;
-
+  // optional inputs are loaded from a valid stand-in address and selected away afterwards: a load
+  // issued on only some paths makes the compiler wait for every load in flight before going on
+  const bool gated = a.z != nullptr, biased = a.dt_bias != nullptr, skip = a.D != nullptr;
+  const T* zp = gated ? (const T*)a.z : (const T*)a.u;
+  const float* biasp = biased ? a.dt_bias : a.A;
+  const float* Dp = skip ? a.D : a.A;
   const int64_t groups = (a.batch + kRPT - 1) / kRPT;
   for (int64_t g = blockIdx.y; g < groups; g += gridDim.y) {
     const int64_t b0 = g * kRPT;
-    float h[kRPT][SPL];
+    float h[kRPT][SPL], bv[kRPT][SPL], cv[kRPT][SPL], dl[kRPT], ut[kRPT], zt[kRPT];
     int64_t rr[kRPT], bb[kRPT];
+    // loads: the rows' states, then their inputs, then the channel's parameters
 #pragma unroll
     for (int i = 0; i < kRPT; ++i) {
       bb[i] = b0 + i < a.batch ? b0 + i : a.batch - 1;
       rr[i] = bb[i] * a.dim + d;
       const float* sp = a.state + rr[i] * N + q * SPL;
       if constexpr (kVec) {
-#pragma unroll
-        for (int k = 0; k < SPL; k += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(sp + k);
-          h[i][k] = v.x; h[i][k + 1] = v.y; h[i][k + 2] = v.z; h[i][k + 3] = v.w;
-        }
+        const float4 v = *reinterpret_cast<const float4*>(sp);
+        h[i][0] = v.x; h[i][1] = v.y; h[i][2] = v.z; h[i][3] = v.w;
       } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) h[i][j] = sp[j];
@@ -99,59 +93,69 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
 #pragma unroll
     for (int i = 0; i < kRPT; ++i) {
       const int64_t r = rr[i], b = bb[i];
-      const bool active = dok && b0 + i < a.batch;
-      const float dt = softplus(ld((const T*)a.delta, r) + bias);
-      const float ut = ld((const T*)a.u, r);
-      const float du = dt * ut;
-      // this lane's SPL consecutive entries of B[b] and C[b], 4 per vector load
-      float bv[SPL], cv[SPL];
+      dl[i] = ld((const T*)a.delta, r);
+      ut[i] = ld((const T*)a.u, r);
+      zt[i] = ld(zp, r);
+      // this lane's SPL consecutive entries of B[b] and C[b]
       if constexpr (kVec && sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < SPL; k += 4) {
-          const uint2 b2 = *reinterpret_cast<const uint2*>((const T*)a.B + b * N + q * SPL + k);
-          const uint2 c2 = *reinterpret_cast<const uint2*>((const T*)a.C + b * N + q * SPL + k);
-          bv[k] = __builtin_bit_cast(float, b2.x << 16); bv[k + 1] = __builtin_bit_cast(float, b2.x & 0xffff0000u);
-          bv[k + 2] = __builtin_bit_cast(float, b2.y << 16); bv[k + 3] = __builtin_bit_cast(float, b2.y & 0xffff0000u);
-          cv[k] = __builtin_bit_cast(float, c2.x << 16); cv[k + 1] = __builtin_bit_cast(float, c2.x & 0xffff0000u);
-          cv[k + 2] = __builtin_bit_cast(float, c2.y << 16); cv[k + 3] = __builtin_bit_cast(float, c2.y & 0xffff0000u);
-        }
+        const uint2 b2 = *reinterpret_cast<const uint2*>((const T*)a.B + b * N + q * SPL);
+        const uint2 c2 = *reinterpret_cast<const uint2*>((const T*)a.C + b * N + q * SPL);
+        bv[i][0] = __builtin_bit_cast(float, b2.x << 16); bv[i][1] = __builtin_bit_cast(float, b2.x & 0xffff0000u);
+        bv[i][2] = __builtin_bit_cast(float, b2.y << 16); bv[i][3] = __builtin_bit_cast(float, b2.y & 0xffff0000u);
+        cv[i][0] = __builtin_bit_cast(float, c2.x << 16); cv[i][1] = __builtin_bit_cast(float, c2.x & 0xffff0000u);
+        cv[i][2] = __builtin_bit_cast(float, c2.y << 16); cv[i][3] = __builtin_bit_cast(float, c2.y & 0xffff0000u);
       } else if constexpr (kVec) {
-#pragma unroll
-        for (int k = 0; k < SPL; k += 4) {
-          const float4 b4 = *reinterpret_cast<const float4*>((const T*)a.B + b * N + q * SPL + k);
-          const float4 c4 = *reinterpret_cast<const float4*>((const T*)a.C + b * N + q * SPL + k);
-          bv[k] = b4.x; bv[k + 1] = b4.y; bv[k + 2] = b4.z; bv[k + 3] = b4.w;
-          cv[k] = c4.x; cv[k + 1] = c4.y; cv[k + 2] = c4.z; cv[k + 3] = c4.w;
-        }
+        const float4 b4 = *reinterpret_cast<const float4*>((const T*)a.B + b * N + q * SPL);
+        const float4 c4 = *reinterpret_cast<const float4*>((const T*)a.C + b * N + q * SPL);
+        bv[i][0] = b4.x; bv[i][1] = b4.y; bv[i][2] = b4.z; bv[i][3] = b4.w;
+        cv[i][0] = c4.x; cv[i][1] = c4.y; cv[i][2] = c4.z; cv[i][3] = c4.w;
       } else {
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
-          bv[j] = ld((const T*)a.B, b * N + q * SPL + j);
-          cv[j] = ld((const T*)a.C, b * N + q * SPL + j);
+          bv[i][j] = ld((const T*)a.B, b * N + q * SPL + j);
+          cv[i][j] = ld((const T*)a.C, b * N + q * SPL + j);
         }
       }
+    }
+    // this lane's SPL consecutive entries of A[d], premultiplied by log2(e); dt_bias and D of d
+    float a2[SPL];
+    if constexpr (kVec) {
+      const float4 a4 = *reinterpret_cast<const float4*>(a.A + d * N + q * SPL);
+      a2[0] = a4.x * kLog2e; a2[1] = a4.y * kLog2e; a2[2] = a4.z * kLog2e; a2[3] = a4.w * kLog2e;
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) a2[j] = a.A[d * N + q * SPL + j] * kLog2e;
+    }
+    float bias = biasp[d], Dd = Dp[d];
+    asm volatile("" : "+v"(bias), "+v"(Dd));  // keeps both loads unconditional
+    bias = biased ? bias : 0.0f;
+    Dd = skip ? Dd : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRPT; ++i) {
+      const int64_t r = rr[i];
+      const bool active = dok && b0 + i < a.batch;
+      const float dt = softplus(dl[i] + bias);
+      const float du = dt * ut[i];
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < SPL; ++j) {
         const float abar = ex2(dt * a2[j]);
-        h[i][j] = __builtin_fmaf(abar, h[i][j], du * bv[j]);
-        acc = __builtin_fmaf(cv[j], h[i][j], acc);
+        h[i][j] = __builtin_fmaf(abar, h[i][j], du * bv[i][j]);
+        acc = __builtin_fmaf(cv[i][j], h[i][j], acc);
       }
 #pragma unroll
       for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
       if (active) {
         float* sp = a.state + r * N + q * SPL;
         if constexpr (kVec) {
-#pragma unroll
-          for (int k = 0; k < SPL; k += 4)
-            *reinterpret_cast<float4*>(sp + k) = make_float4(h[i][k], h[i][k + 1], h[i][k + 2], h[i][k + 3]);
+          *reinterpret_cast<float4*>(sp) = make_float4(h[i][0], h[i][1], h[i][2], h[i][3]);
         } else {
 #pragma unroll
           for (int j = 0; j < SPL; ++j) sp[j] = h[i][j];
         }
         if (q == 0) {
-          float yt = __builtin_fmaf(Dd, ut, acc);
-          if (a.z) yt *= silu(ld((const T*)a.z, r));
+          float yt = __builtin_fmaf(Dd, ut[i], acc);
+          if (gated) yt *= silu(zt[i]);
           st((T*)a.y, r, yt);
         }
       }
