@@ -250,6 +250,26 @@ def test_decode_small_shapes():
             assert oracle.rel_err(f64(state), ref_state) <= 1e-5
 
 
+@pytest.mark.parametrize("n", [2, 16, 64])
+def test_decode_optional_terms_absent(n):
+    # no z, D or dt_bias: the kernel loads stand-ins for them and selects the terms away
+    b, d = 3, 70
+    note(f"decode B={b} D={d} N={n} f32 without z, D, dt_bias")
+    x = gen.random_scan_inputs(b, d, n, 2, "f32", seed=31 + n)
+    state0 = torch.randn(b, d, n, generator=torch.Generator().manual_seed(n))
+    ref_state = state0.double().numpy()
+    state = state0.cuda()
+    g = dev(x)
+    for t in range(2):
+        st = {k: g[k][..., t].contiguous() for k in ("u", "delta", "B", "C")}
+        y = ssm.state_update(state, st["u"], st["delta"], g["A"], st["B"], st["C"], None, None, None)
+        torch.cuda.synchronize()
+        yr, ref_state = oracle.step(ref_state, *(x[k][..., t].contiguous() for k in ("u", "delta")), x["A"],
+                                    x["B"][..., t].contiguous(), x["C"][..., t].contiguous(), None, None, None)
+        assert oracle.rel_err(f64(y), yr) <= TOL["f32"]
+        assert oracle.rel_err(f64(state), ref_state) <= 1e-5
+
+
 def test_decode_batch_beyond_one_grid_column():
     # 131075 batch rows: more row pairs than one launch column holds (65535), so the blocks walk the
     # batch with a stride; an odd count leaves the last pair half empty
