@@ -191,8 +191,8 @@ def main():
         "roofline": {"bound": "alu", "achieved": r["tops"], "peak": PEAK_VALU_TOPS, "unit": "Tops/s",
                      "frac": r["tops"] / PEAK_VALU_TOPS, "traffic": TRAFFIC.get(args.workload),
                      "ops_per_element": r["slots"], "op": "fp32 VALU issue slot per lane (exp/log/rcp = 2)",
-                     "kernel": "scan_chunked_kernel (the call's one scan kernel, plus a one-block flag clear "
-                               "when segments are chained)"},
+                     "kernel": "scan_chunked_kernel (the call's one launch: the interval plan keeps its ticket and hand-over "
+                               "flags in the stream's control block, so nothing is cleared per call)"},
         "hbm": {"achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": r["gbs"] / PEAK_HBM_GBS,
                 "bytes_per_step": r["bytes_step"]},
         "wall_s_timed": r["wall"],
