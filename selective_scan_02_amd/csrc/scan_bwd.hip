@@ -92,6 +92,8 @@ struct BwdArgs {
   int iunits;     // intervals (workgroups); 0: the segment plan
   int max_polls;  // bound of a hand-over wait
   int publish;    // 0 only under the test hook: split points never publish
+  float* clear;        // the checkpoint pass zeroes [clear, clear + clear_n) (the main pass's ticket and
+  int64_t clear_n;     // flags) on its way, so no launch of its own clears them before the main pass
 };
 
 // Hand-over waits of the main pass that gave up (bwd_handover_failures).
@@ -863,6 +865,11 @@ __device__ __forceinline__ void fbwd_adjoint_aggregate(const BwdArgs& a, int seg
 template <int N, typename T, bool UNI = false>
 __global__ __launch_bounds__(kWave) void fbwd_pre_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char lds[PreLds<N, T>::kBytes];
+  if (a.clear) {
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * kWave;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kWave + threadIdx.x; i < a.clear_n; i += stride)
+      a.clear[i] = 0.0f;
+  }
   const int y = blockIdx.y;
   if (y < a.nseg)
     fbwd_checkpoint<N, T, UNI>(a, y, lds);
@@ -1886,6 +1893,10 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
     handover_wait(&a.max_polls, &a.publish);
   }
   const dim3 grid((unsigned)units, (unsigned)nseg);
+  if (FAST && IV) {  // the main pass's ticket and flags (0.0f is all zero bits), cleared by the checkpoint pass
+    a.clear = ctl;
+    a.clear_n = 64 + units * kRSc;
+  }
   if constexpr (FAST) {  // checkpoints (and, on the segment plan, adjoint aggregates) in one grid
     if (uni)
       hipLaunchKernelGGL((fbwd_pre_kernel<N, T, UNIF>), dim3((unsigned)units, (unsigned)(IV ? nseg : 2 * nseg - 1)),
@@ -1911,7 +1922,7 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
       err = hipGetLastError();
     }
   }
-  if (err == hipSuccess && IV) err = zero(ctl, 64 + units * kRSc, stream);  // ticket and flags (0.0f is all zero bits)
+  if (err == hipSuccess && IV && !FAST) err = zero(ctl, 64 + units * kRSc, stream);  // ticket and flags
   if (err == hipSuccess) {
     if constexpr (ROLES) {
       if (uni)
