@@ -433,11 +433,11 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(const float* pB, con
 // outputs over a quarter of the groups (g = quarter, quarter + 4, ...), and the quarters' sums meet
 // in LDS in a fixed order, so the result is still reproducible bit for bit.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_bc_reduce4_kernel(const float* pB, const float* pC, T* dB, T* dC,
-                                                             int64_t count, int groups) {
+__device__ __forceinline__ void bc_reduce4(const float* pB, const float* pC, T* dB, T* dC, int64_t count, int groups,
+                                           int64_t blk) {
   __shared__ float4 sb[4][64], sc[4][64];
   const int qd = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int64_t i4 = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  const int64_t i4 = (blk * 64 + lane) * 4;
   float4 b = make_float4(0.f, 0.f, 0.f, 0.f), c = b;
   if (i4 < count) {
     for (int g = qd; g < groups; g += 4) {
@@ -466,10 +466,10 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce4_kernel(const float* pB, co
 }
 
 // 5b. dA, dD, ddt_bias: sum over segments and batch rows, one thread per (d, n).
-__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(const float* pA, const float* pD, const float* pbias,
-                                                               float* dA, float* dD, float* dbias, int64_t batch,
-                                                               int64_t dim, int N, int nseg) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+__device__ __forceinline__ void param_reduce(const float* pA, const float* pD, const float* pbias, float* dA,
+                                             float* dD, float* dbias, int64_t batch, int64_t dim, int N, int nseg,
+                                             int64_t blk) {
+  const int64_t i = blk * 256 + threadIdx.x;
   if (i >= dim * N) return;
   const int64_t d = i / N;
   const int n = (int)(i % N);
@@ -489,6 +489,25 @@ __global__ __launch_bounds__(256) void bwd_param_reduce_kernel(const float* pA, 
     if (dD) dD[d] = sd;
     if (dbias) dbias[d] = sb;
   }
+}
+
+__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(const float* pA, const float* pD, const float* pbias,
+                                                               float* dA, float* dD, float* dbias, int64_t batch,
+                                                               int64_t dim, int N, int nseg) {
+  param_reduce(pA, pD, pbias, dA, dD, dbias, batch, dim, N, nseg, blockIdx.x);
+}
+
+// 5a' and 5b in one grid: blocks 0 .. nbc-1 sum dB and dC, the rest dA, dD and ddt_bias (the two need
+// nothing of each other; one launch fewer after the main pass).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* pB, const float* pC, T* dB, T* dC, int64_t count,
+                                                         int groups, int64_t nbc, const float* pA, const float* pD,
+                                                         const float* pbias, float* dA, float* dD, float* dbias,
+                                                         int64_t batch, int64_t dim, int N, int nseg) {
+  if ((int64_t)blockIdx.x < nbc)
+    bc_reduce4(pB, pC, dB, dC, count, groups, blockIdx.x);
+  else
+    param_reduce(pA, pD, pbias, dA, dD, dbias, batch, dim, N, nseg, (int64_t)blockIdx.x - nbc);
 }
 
 // Zero-length sequence: every gradient is zero.  A fill kernel rather than a memset node.
@@ -1940,18 +1959,22 @@ hipError_t run(const BwdParams& p, hipStream_t stream) {
   }
   if (err == hipSuccess) {
     const int64_t count = p.batch * N * L;
-    if (count % 4 == 0)
-      hipLaunchKernelGGL((bwd_bc_reduce4_kernel<T>), dim3((unsigned)((count / 4 + 63) / 64)), dim3(256), 0, stream,
-                         a.pB, a.pC, (T*)p.dB, (T*)p.dC, count, a.groups);
-    else
+    if (count % 4 == 0) {
+      const int64_t nbc = (count / 4 + 63) / 64;
+      hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3((unsigned)(nbc + blocks_of(p.dim * N))), dim3(256), 0, stream,
+                         a.pB, a.pC, (T*)p.dB, (T*)p.dC, count, a.groups, nbc, a.pA, a.pD, a.pbias, p.dA, p.dD,
+                         p.ddt_bias, p.batch, p.dim, N, (int)pslots);
+      err = hipGetLastError();
+    } else {
       hipLaunchKernelGGL((bwd_bc_reduce_kernel<T>), dim3(blocks_of(count)), dim3(256), 0, stream, a.pB, a.pC,
                          (T*)p.dB, (T*)p.dC, count, a.groups);
-    err = hipGetLastError();
-  }
-  if (err == hipSuccess) {
-    hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(blocks_of(p.dim * N)), dim3(256), 0, stream, a.pA, a.pD,
-                       a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)pslots);
-    err = hipGetLastError();
+      err = hipGetLastError();
+      if (err == hipSuccess) {
+        hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(blocks_of(p.dim * N)), dim3(256), 0, stream, a.pA, a.pD,
+                           a.pbias, p.dA, p.dD, p.ddt_bias, p.batch, p.dim, N, (int)pslots);
+        err = hipGetLastError();
+      }
+    }
   }
   const hipError_t ferr = call_scratch_release(scratch, kept, stream);
   return err != hipSuccess ? err : ferr;
