@@ -11,7 +11,7 @@
 //   ddt_bias[h]   = sum over the head's channels of ddt_bias[h*P + p]
 // and every other gradient (dx, dz, dB, dC, dD, dh0) is the scan's own.  So this runs: one kernel
 // that broadcasts dt (and A, dt_bias) to the channels, the backward scan's kernels
-// (scan_bwd.hip) on the broadcast problem, and two kernels that sum the head gradients in a fixed
+// (scan_bwd.hip) on the broadcast problem, and one kernel that sums the head gradients in a fixed
 // order (results reproducible bit for bit).  The per-channel step-size gradients are kept in fp32
 // (the backward scan writes them so on request): summed from the I/O dtype, 64 rounded terms per
 // head put the head gradient 3% off on the 2.8B-shaped layer.  The broadcast step sizes (dtype of
@@ -25,11 +25,10 @@ namespace {
 
 // delta[b, d, t] = dt[b, d / P, t], E elements per thread (16 bytes when rows allow).
 template <typename T, int E>
-__global__ __launch_bounds__(256) void ssd_bcast_dt_kernel(const T* __restrict__ dt, T* __restrict__ delta,
-                                                           int64_t rows, int64_t dim, int64_t heads, int64_t P,
-                                                           int64_t L) {
+__device__ __forceinline__ void bcast_dt(const T* __restrict__ dt, T* __restrict__ delta, int64_t rows, int64_t dim,
+                                         int64_t heads, int64_t P, int64_t L, int64_t blk) {
   const int64_t per_row = L / E;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = blk * 256 + threadIdx.x;
   if (i >= rows * per_row) return;
   const int64_t r = i / per_row, q = i - r * per_row;
   const int64_t b = r / dim, d = r - b * dim;
@@ -44,9 +43,9 @@ __global__ __launch_bounds__(256) void ssd_bcast_dt_kernel(const T* __restrict__
 }
 
 // A_full[d, n] = A[d / P]; bias_full[d] = dt_bias[d / P].
-__global__ __launch_bounds__(256) void ssd_bcast_param_kernel(const float* A, const float* dt_bias, float* A_full,
-                                                              float* bias_full, int64_t dim, int64_t P, int64_t N) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void bcast_param(const float* A, const float* dt_bias, float* A_full, float* bias_full,
+                                            int64_t dim, int64_t P, int64_t N, int64_t blk) {
+  const int64_t i = blk * 256 + threadIdx.x;
   if (i >= dim * N) return;
   const int64_t d = i / N;
   A_full[i] = A[d / P];
@@ -57,10 +56,10 @@ __global__ __launch_bounds__(256) void ssd_bcast_param_kernel(const float* A, co
 // takes E consecutive steps (16-byte loads when rows allow), and the p loop is unrolled so that
 // several rows' loads are in flight at once; each step's sum keeps the same order either way.
 template <typename T, int E>
-__global__ __launch_bounds__(256) void ssd_sum_dt_kernel(const float* __restrict__ ddelta, T* __restrict__ ddt,
-                                                         int64_t batch, int64_t heads, int64_t P, int64_t L) {
+__device__ __forceinline__ void sum_dt(const float* __restrict__ ddelta, T* __restrict__ ddt, int64_t batch,
+                                       int64_t heads, int64_t P, int64_t L, int64_t blk) {
   const int64_t per_row = L / E;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = blk * 256 + threadIdx.x;
   if (i >= batch * heads * per_row) return;
   const int64_t bh = i / per_row, t = (i - bh * per_row) * E;
   const float* src = ddelta + bh * P * L + t;  // rows b*dim + h*P + p = (b*heads + h)*P + p
@@ -83,10 +82,9 @@ __global__ __launch_bounds__(256) void ssd_sum_dt_kernel(const float* __restrict
 // dA[h] = sum_{p, n} dA_full[h*P + p, n]; ddt_bias[h] = sum_p dbias_full[h*P + p].  One workgroup per
 // head: thread j sums terms j, j + 256, ... in order, then a fixed pairwise tree in LDS (results
 // reproducible bit for bit).
-__global__ __launch_bounds__(256) void ssd_sum_param_kernel(const float* dA_full, const float* dbias_full,
-                                                            float* dA, float* ddt_bias, int64_t P, int64_t N) {
+__device__ __forceinline__ void sum_param(const float* dA_full, const float* dbias_full, float* dA, float* ddt_bias,
+                                          int64_t P, int64_t N, int64_t h) {
   __shared__ float red[2][256];
-  const int64_t h = blockIdx.x;
   const int j = threadIdx.x;
   float s = 0.0f, sb = 0.0f;
   for (int64_t k = j; k < P * N; k += 256) s += dA_full[h * P * N + k];
@@ -106,6 +104,31 @@ __global__ __launch_bounds__(256) void ssd_sum_param_kernel(const float* dA_full
     dA[h] = red[0][0];
     if (ddt_bias) ddt_bias[h] = red[1][0];
   }
+}
+
+// The per-head parameters broadcast to every channel (step sizes: blocks 0 .. nb-1; A and the step
+// bias: the rest), in one grid ahead of the backward scan.
+template <typename T, int E>
+__global__ __launch_bounds__(256) void ssd_bcast_kernel(const T* dt, T* delta, int64_t rows, int64_t dim, int64_t heads,
+                                                        int64_t P, int64_t L, int64_t nb, const float* A,
+                                                        const float* dt_bias, float* A_full, float* bias_full,
+                                                        int64_t N) {
+  if ((int64_t)blockIdx.x < nb)
+    bcast_dt<T, E>(dt, delta, rows, dim, heads, P, L, blockIdx.x);
+  else
+    bcast_param(A, dt_bias, A_full, bias_full, dim, P, N, (int64_t)blockIdx.x - nb);
+}
+
+// The per-head sums after it (step-size gradients: blocks 0 .. nb-1; dA and the step-bias gradient: one
+// block per head after them), in one grid.
+template <typename T, int E>
+__global__ __launch_bounds__(256) void ssd_sum_kernel(const float* ddelta, T* ddt, int64_t batch, int64_t heads,
+                                                      int64_t P, int64_t L, int64_t nb, const float* dA_full,
+                                                      const float* dbias_full, float* dA, float* ddt_bias, int64_t N) {
+  if ((int64_t)blockIdx.x < nb)
+    sum_dt<T, E>(ddelta, ddt, batch, heads, P, L, blockIdx.x);
+  else
+    sum_param(dA_full, dbias_full, dA, ddt_bias, P, N, (int64_t)blockIdx.x - nb);
 }
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -134,20 +157,17 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
   float* dbias_full = (float*)c;
   const bool with_bias = f.dt_bias != nullptr;
 
-  if (L > 0) {
+  {
     constexpr int E = 16 / (int)sizeof(T);
     const bool vec = L % E == 0 && ((uintptr_t)f.dt & 15) == 0;
+    const int64_t nb = L > 0 ? (int64_t)blocks_for(rows * (vec ? L / E : L)) : 0;
+    const dim3 g((unsigned)(nb + blocks_for(dim * N)));
     if (vec)
-      hipLaunchKernelGGL((ssd_bcast_dt_kernel<T, E>), dim3(blocks_for(rows * (L / E))), dim3(256), 0, stream,
-                         (const T*)f.dt, delta, rows, dim, H, P, L);
+      hipLaunchKernelGGL((ssd_bcast_kernel<T, E>), g, dim3(256), 0, stream, (const T*)f.dt, delta, rows, dim, H, P, L,
+                         nb, f.A, f.dt_bias, A_full, with_bias ? bias_full : nullptr, N);
     else
-      hipLaunchKernelGGL((ssd_bcast_dt_kernel<T, 1>), dim3(blocks_for(rows * L)), dim3(256), 0, stream,
-                         (const T*)f.dt, delta, rows, dim, H, P, L);
-    err = hipGetLastError();
-  }
-  if (err == hipSuccess) {
-    hipLaunchKernelGGL(ssd_bcast_param_kernel, dim3(blocks_for(dim * N)), dim3(256), 0, stream, f.A, f.dt_bias,
-                       A_full, with_bias ? bias_full : nullptr, dim, P, N);
+      hipLaunchKernelGGL((ssd_bcast_kernel<T, 1>), g, dim3(256), 0, stream, (const T*)f.dt, delta, rows, dim, H, P, L,
+                         nb, f.A, f.dt_bias, A_full, with_bias ? bias_full : nullptr, N);
     err = hipGetLastError();
   }
   if (err == hipSuccess) {
@@ -161,18 +181,16 @@ hipError_t run(const SsdBwdParams& q, hipStream_t stream) {
     b.a_uniform = true;
     err = launch_scan_bwd(b, stream);
   }
-  if (err == hipSuccess && L > 0) {
-    if (L % 4 == 0)
-      hipLaunchKernelGGL((ssd_sum_dt_kernel<T, 4>), dim3(blocks_for(f.batch * H * (L / 4))), dim3(256), 0, stream,
-                         ddelta, (T*)q.ddt, f.batch, H, P, L);
+  if (err == hipSuccess) {
+    const bool v4 = L % 4 == 0;
+    const int64_t nb = L > 0 ? (int64_t)blocks_for(f.batch * H * (v4 ? L / 4 : L)) : 0;
+    const dim3 g((unsigned)(nb + H));
+    if (v4)
+      hipLaunchKernelGGL((ssd_sum_kernel<T, 4>), g, dim3(256), 0, stream, ddelta, (T*)q.ddt, f.batch, H, P, L, nb,
+                         dA_full, q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, N);
     else
-      hipLaunchKernelGGL((ssd_sum_dt_kernel<T, 1>), dim3(blocks_for(f.batch * H * L)), dim3(256), 0, stream,
-                         ddelta, (T*)q.ddt, f.batch, H, P, L);
-    err = hipGetLastError();
-  }
-  if (err == hipSuccess && H > 0) {
-    hipLaunchKernelGGL(ssd_sum_param_kernel, dim3((unsigned)H), dim3(256), 0, stream, dA_full,
-                       q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, P, N);
+      hipLaunchKernelGGL((ssd_sum_kernel<T, 1>), g, dim3(256), 0, stream, ddelta, (T*)q.ddt, f.batch, H, P, L, nb,
+                         dA_full, q.ddt_bias ? dbias_full : nullptr, q.dA, q.ddt_bias, N);
     err = hipGetLastError();
   }
   const hipError_t ferr = call_scratch_release(scratch, kept, stream);
